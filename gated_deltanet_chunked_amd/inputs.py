@@ -1,0 +1,160 @@
+"""Seeded synthetic inputs for the gated delta rule.
+
+This module only draws random numbers and rounds them to the storage dtype.
+It holds none of the rule's arithmetic, so both the CPU oracle and the HIP
+path can be fed from it.
+
+Recipe (shared by every test and the benchmark):
+
+* draws come from ``numpy.random.default_rng(seed)`` (PCG64) in a fixed order:
+  sequence lengths (varlen only), q, k, v (standard normal), a, b (standard
+  normal, one per token and value head), A (uniform, one per value head),
+  then the initial state (``state_std`` * standard normal) when requested;
+* the gates follow the module initialisation of the Qwen3-Next blog post
+  ("Code-Qwen3-Next", section 1 and the gate lines of section 4):
+  dt_bias = 1, A ~ U(A_lo, A_hi), g = -A * softplus(a + dt_bias),
+  beta = sigmoid(b); both are computed in float64 and stored as float32;
+* for bf16 inputs, q, k and v are rounded to bfloat16 (round to nearest even)
+  and those rounded values are what both sides receive.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional, Sequence
+
+import numpy as np
+
+D = 128
+
+
+def round_to_bf16(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest bfloat16 (ties to even); returns float32."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    r = ((u + 0x7FFF + lsb) >> 16) << 16
+    out = r.astype(np.uint32).view(np.float32)
+    nan = np.isnan(x)
+    if nan.any():
+        out = out.copy()
+        out[nan] = np.nan
+    return out
+
+
+def _softplus(x: np.ndarray) -> np.ndarray:
+    return np.maximum(x, 0.0) + np.log1p(np.exp(-np.abs(x)))
+
+
+@dataclasses.dataclass
+class GdrInputs:
+    """One workload: packed tokens delimited by ``cu_seqlens``."""
+
+    q: np.ndarray            # [T, Nqk, D] float32 (bf16-representable when dtype == "bf16")
+    k: np.ndarray            # [T, Nqk, D]
+    v: np.ndarray            # [T, Nv, D]
+    g: np.ndarray            # [T, Nv] float32, natural-log decay (<= 0)
+    beta: np.ndarray         # [T, Nv] float32 in (0, 1)
+    state_in: Optional[np.ndarray]  # [N, Nv, D, D] float32 (row = value index) or None
+    cu_seqlens: np.ndarray   # [N + 1] int32
+    dtype: str               # "f32" or "bf16": storage type of q, k, v and out
+    seed: int
+    name: str = ""
+
+    @property
+    def T(self) -> int:
+        return int(self.q.shape[0])
+
+    @property
+    def N(self) -> int:
+        return int(self.cu_seqlens.shape[0] - 1)
+
+    @property
+    def Nqk(self) -> int:
+        return int(self.q.shape[1])
+
+    @property
+    def Nv(self) -> int:
+        return int(self.v.shape[1])
+
+
+def make_inputs(lengths: Sequence[int], Nqk: int, Nv: int, *, dtype: str = "bf16",
+                seed: int = 0, state_std: Optional[float] = 0.01,
+                A_range=(0.0, 16.0), dk: int = D, dv: int = D,
+                name: str = "") -> GdrInputs:
+    """Draw one workload with the given per-sequence lengths."""
+    lengths = [int(x) for x in lengths]
+    rng = np.random.default_rng(seed)
+    return _draw(rng, lengths, Nqk, Nv, dtype, seed, state_std, A_range, dk, dv, name)
+
+
+def _draw(rng, lengths, Nqk, Nv, dtype, seed, state_std, A_range, dk, dv, name):
+    if dtype not in ("f32", "bf16"):
+        raise ValueError(f"unknown dtype {dtype!r}")
+    T = int(sum(lengths))
+    N = len(lengths)
+    cu = np.zeros(N + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(np.asarray(lengths, dtype=np.int64)).astype(np.int32)
+    q = rng.standard_normal((T, Nqk, dk)).astype(np.float32)
+    k = rng.standard_normal((T, Nqk, dk)).astype(np.float32)
+    v = rng.standard_normal((T, Nv, dv)).astype(np.float32)
+    a = rng.standard_normal((T, Nv))
+    b = rng.standard_normal((T, Nv))
+    A = rng.uniform(A_range[0], A_range[1], size=Nv)
+    state = None
+    if state_std is not None:
+        state = (state_std * rng.standard_normal((N, Nv, dv, dk))).astype(np.float32)
+    dt_bias = 1.0
+    g = (-A[None, :] * _softplus(a + dt_bias)).astype(np.float32)
+    beta = (1.0 / (1.0 + np.exp(-b))).astype(np.float32)
+    if dtype == "bf16":
+        q, k, v = round_to_bf16(q), round_to_bf16(k), round_to_bf16(v)
+    return GdrInputs(q=q, k=k, v=v, g=g, beta=beta, state_in=state, cu_seqlens=cu,
+                     dtype=dtype, seed=seed, name=name)
+
+
+# The five workloads the throughput and parity targets are quoted on.
+CONFIG_NAMES = {
+    0: "tiny chunk fwd: B=1 T=512 Nqk=2 Nv=4 D=128 fp32, zero initial state",
+    1: "prefill: B=1 T=4096 Nqk=16 Nv=32 D=128 bf16",
+    2: "varlen packed prefill: 8 sequences, lengths U[1,8192], Nqk=16 Nv=32 bf16",
+    3: "long-context prefill: B=1 T=32768 Nqk=16 Nv=32 bf16",
+    4: "decode step: N=256 sequences x 1 token, Nqk=16 Nv=32 bf16, fp32 states",
+}
+
+
+def config_inputs(c: int) -> GdrInputs:
+    """The seeded inputs of workload ``c`` (seed = c)."""
+    rng = np.random.default_rng(c)
+    if c == 0:
+        return _draw(rng, [512], 2, 4, "f32", c, None, (0.0, 16.0), D, D, CONFIG_NAMES[c])
+    if c == 1:
+        return _draw(rng, [4096], 16, 32, "bf16", c, 0.01, (0.0, 16.0), D, D, CONFIG_NAMES[c])
+    if c == 2:
+        lengths = rng.integers(1, 8192, size=8, endpoint=True).tolist()
+        return _draw(rng, lengths, 16, 32, "bf16", c, 0.01, (0.0, 16.0), D, D, CONFIG_NAMES[c])
+    if c == 3:
+        return _draw(rng, [32768], 16, 32, "bf16", c, 0.01, (0.0, 16.0), D, D, CONFIG_NAMES[c])
+    if c == 4:
+        return _draw(rng, [1] * 256, 16, 32, "bf16", c, 0.01, (0.0, 16.0), D, D, CONFIG_NAMES[c])
+    raise ValueError(f"no workload {c}")
+
+
+def config_shape(c: int) -> dict:
+    """Sizes of workload ``c`` without drawing it (lengths of config 2 are drawn)."""
+    if c == 2:
+        rng = np.random.default_rng(c)
+        lengths = rng.integers(1, 8192, size=8, endpoint=True).tolist()
+        return dict(lengths=lengths, Nqk=16, Nv=32, dtype="bf16")
+    table = {0: ([512], 2, 4, "f32"), 1: ([4096], 16, 32, "bf16"), 3: ([32768], 16, 32, "bf16"),
+             4: ([1] * 256, 16, 32, "bf16")}
+    lengths, Nqk, Nv, dt = table[c]
+    return dict(lengths=lengths, Nqk=Nqk, Nv=Nv, dtype=dt)
+
+
+def orthonormal_keys(n: int, dk: int, seed: int) -> np.ndarray:
+    """n <= dk orthonormal rows (QR of a Gaussian), float64."""
+    rng = np.random.default_rng(seed)
+    m = rng.standard_normal((dk, dk))
+    qm, r = np.linalg.qr(m)
+    qm = qm * np.sign(np.diag(r))[None, :]
+    return np.ascontiguousarray(qm.T[:n])

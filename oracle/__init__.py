@@ -1,0 +1,107 @@
+"""CPU fp64 oracle of the gated delta rule -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg import
+this package.  The HIP library and its Python binding never do.
+
+``recurrent`` runs the per-token recurrence in C (``gdr_oracle.c``), the
+plain definition the chunkwise form must reproduce (Qwen3-Next blog post,
+section 5(2)).  ``oracle.alt`` holds two independently written codings of the
+same rule (the DeltaNet matrix form and the chunkwise form of section 5(1)),
+used only to pin ``recurrent`` in the oracle's own tests.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(HERE, "liboracle.so")
+_lib = None
+
+EPS = 1e-6
+
+
+def load_library(path: str):
+    """Open an oracle shared library and declare its C signatures."""
+    lib = ctypes.CDLL(path)
+    dp = ctypes.POINTER(ctypes.c_double)
+    lib.gdr_oracle_run.argtypes = [dp, dp, dp, dp, dp, dp, ctypes.POINTER(ctypes.c_int32),
+                                   ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                   ctypes.c_int32, ctypes.c_int32,
+                                   ctypes.c_double, ctypes.c_double, dp, dp, ctypes.c_int32]
+    lib.gdr_oracle_run.restype = ctypes.c_int
+    lib.gdr_oracle_threads.argtypes = [ctypes.c_int32]
+    lib.gdr_oracle_threads.restype = ctypes.c_int
+    return lib
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        from . import build as _b
+        _b.build()
+    _lib = load_library(_LIB_PATH)
+    return _lib
+
+
+def _f64(x):
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(a):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def threads(n: int = 0) -> int:
+    return int(_load().gdr_oracle_threads(int(n)))
+
+
+def recurrent(q, k, v, g, beta, state_in: Optional[np.ndarray], cu_seqlens,
+              scale: float, eps: float = EPS, nthreads: int = 0,
+              want_state: bool = True, lib=None) -> Tuple[np.ndarray, Optional[np.ndarray]]:
+    """Per-token gated delta rule in fp64.
+
+    Shapes: q, k [T, Nqk, Dk]; v [T, Nv, Dv]; g, beta [T, Nv];
+    state_in [N, Nv, Dv, Dk] or None (zeros); cu_seqlens [N + 1].
+    Returns (out [T, Nv, Dv], state_out [N, Nv, Dv, Dk] or None), float64.
+    ``lib`` selects another build of the oracle (used by the mutation tests).
+    """
+    lib = _load() if lib is None else lib
+    q, k, v, g, beta = (_f64(x) for x in (q, k, v, g, beta))
+    cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
+    T, Nqk, Dk = q.shape
+    Nv, Dv = v.shape[1], v.shape[2]
+    N = cu.shape[0] - 1
+    if k.shape != q.shape or v.shape[0] != T or g.shape != (T, Nv) or beta.shape != (T, Nv):
+        raise ValueError("shape mismatch")
+    if int(cu[-1]) != T:
+        raise ValueError("cu_seqlens[-1] must equal T")
+    sin = None if state_in is None else _f64(state_in)
+    if sin is not None and sin.shape != (N, Nv, Dv, Dk):
+        raise ValueError("state_in shape mismatch")
+    out = np.zeros((T, Nv, Dv), dtype=np.float64)
+    sout = np.zeros((N, Nv, Dv, Dk), dtype=np.float64) if want_state else None
+    rc = lib.gdr_oracle_run(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                            _ptr(sin) if sin is not None else None,
+                            cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                            N, Nqk, Nv, Dk, Dv, float(scale), float(eps),
+                            _ptr(out), _ptr(sout) if sout is not None else None, int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle rejected its arguments (code {rc})")
+    return out, sout
+
+
+def rel_l2(x, ref) -> float:
+    """||x - ref||_2 / ||ref||_2 over the whole array, in fp64."""
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    den = float(np.linalg.norm(ref.ravel()))
+    num = float(np.linalg.norm((x - ref).ravel()))
+    if den == 0.0:
+        return num
+    return num / den
