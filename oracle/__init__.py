@@ -31,7 +31,8 @@ def load_library(path: str):
     lib.gdr_oracle_run.argtypes = [dp, dp, dp, dp, dp, dp, ctypes.POINTER(ctypes.c_int32),
                                    ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                    ctypes.c_int32, ctypes.c_int32,
-                                   ctypes.c_double, ctypes.c_double, dp, dp, ctypes.c_int32]
+                                   ctypes.c_double, ctypes.c_double, ctypes.c_int32,
+                                   dp, dp, ctypes.c_int32]
     lib.gdr_oracle_run.restype = ctypes.c_int
     lib.gdr_oracle_threads.argtypes = [ctypes.c_int32]
     lib.gdr_oracle_threads.restype = ctypes.c_int
@@ -63,12 +64,13 @@ def threads(n: int = 0) -> int:
 
 def recurrent(q, k, v, g, beta, state_in: Optional[np.ndarray], cu_seqlens,
               scale: float, eps: float = EPS, nthreads: int = 0,
-              want_state: bool = True, lib=None) -> Tuple[np.ndarray, Optional[np.ndarray]]:
+              want_state: bool = True, lib=None, l2norm: bool = True) -> Tuple[np.ndarray, Optional[np.ndarray]]:
     """Per-token gated delta rule in fp64.
 
     Shapes: q, k [T, Nqk, Dk]; v [T, Nv, Dv]; g, beta [T, Nv];
     state_in [N, Nv, Dv, Dk] or None (zeros); cu_seqlens [N + 1].
     Returns (out [T, Nv, Dv], state_out [N, Nv, Dv, Dk] or None), float64.
+    ``l2norm=False`` skips the query/key normalisation.
     ``lib`` selects another build of the oracle (used by the mutation tests).
     """
     lib = _load() if lib is None else lib
@@ -89,7 +91,7 @@ def recurrent(q, k, v, g, beta, state_in: Optional[np.ndarray], cu_seqlens,
     rc = lib.gdr_oracle_run(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                             _ptr(sin) if sin is not None else None,
                             cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
-                            N, Nqk, Nv, Dk, Dv, float(scale), float(eps),
+                            N, Nqk, Nv, Dk, Dv, float(scale), float(eps), int(bool(l2norm)),
                             _ptr(out), _ptr(sout) if sout is not None else None, int(nthreads))
     if rc != 0:
         raise ValueError(f"oracle rejected its arguments (code {rc})")

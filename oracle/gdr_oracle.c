@@ -23,7 +23,9 @@
  *     state_out[b][h] = S
  *
  * The L2 normalisation x / sqrt(sum x^2 + eps) is the Ascend operator page's
- * formula (section "math formulas"); eps = 1e-6 in every caller.  Rows of S
+ * formula (section "math formulas"); eps = 1e-6 in every caller.  With
+ * l2norm = 0 the normalisation is skipped (kh = k, qh = scale * q), the
+ * blog's use_qk_l2norm_in_kernel = False.  Rows of S
  * evolve independently of each other (every step acts on each row alone), so
  * the work is split over (sequence, head, block of rows) with OpenMP.
  */
@@ -44,7 +46,7 @@ int gdr_oracle_run(const double* q, const double* k, const double* v,
                    const double* state_in,      /* [N][Nv][Dv][Dk] or NULL */
                    const int32_t* cu_seqlens,   /* [N+1] */
                    int32_t N, int32_t Nqk, int32_t Nv, int32_t Dk, int32_t Dv,
-                   double scale, double eps,
+                   double scale, double eps, int32_t l2norm,
                    double* out,                 /* [T][Nv][Dv] */
                    double* state_out,           /* [N][Nv][Dv][Dk] or NULL */
                    int32_t nthreads)
@@ -92,8 +94,8 @@ int gdr_oracle_run(const double* q, const double* k, const double* v,
                 const double* qt = q + ((size_t)t * Nqk + j) * Dk;
                 double ssk = 0.0, ssq = 0.0;
                 for (int32_t c = 0; c < Dk; ++c) { ssk += kt[c] * kt[c]; ssq += qt[c] * qt[c]; }
-                const double rk = 1.0 / sqrt(ssk + eps);
-                const double rq = scale / sqrt(ssq + eps);
+                const double rk = l2norm ? 1.0 / sqrt(ssk + eps) : 1.0;
+                const double rq = l2norm ? scale / sqrt(ssq + eps) : scale;
                 for (int32_t c = 0; c < Dk; ++c) { kh[c] = kt[c] * rk; qh[c] = qt[c] * rq; }
                 const double alpha = exp(g[(size_t)t * Nv + h]);
                 const double bt = beta[(size_t)t * Nv + h];

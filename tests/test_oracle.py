@@ -128,3 +128,15 @@ def test_similarity_identity():
 
 def test_oracle_threads_reported():
     assert oracle.threads(2) == 2
+
+
+def test_without_normalisation_matches_prenormalised():
+    """l2norm=False on pre-normalised q, k equals l2norm=True with eps = 0."""
+    q, k, v, g, beta, s0, cu = _case(13, [9], 1, 2)
+    qn = q / np.linalg.norm(q, axis=-1, keepdims=True)
+    kn = k / np.linalg.norm(k, axis=-1, keepdims=True)
+    o1, s1 = oracle.recurrent(qn, kn, v, g, beta, s0, cu, 0.4, l2norm=False)
+    o2, s2 = oracle.recurrent(q, k, v, g, beta, s0, cu, 0.4, eps=0.0)
+    assert pins._rel(o1, o2) < 1e-14 and pins._rel(s1, s2) < 1e-14
+    o3, _ = oracle.recurrent(q, k, v, g, beta, s0, cu, 0.4, l2norm=False)
+    assert pins._rel(o3, o1) > 1e-2

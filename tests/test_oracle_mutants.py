@@ -27,10 +27,10 @@ MUTANTS = {
     "state_transposed": ("state_in[state_off + (size_t)(r0 + r) * Dk + c]",
                          "state_in[state_off + (size_t)c * Dv + (r0 + r)]"),
     "gqa_interleaved": ("const int32_t j = h / group;", "const int32_t j = h % Nqk;"),
-    "eps_outside_sqrt": ("const double rk = 1.0 / sqrt(ssk + eps);",
-                         "const double rk = 1.0 / (sqrt(ssk) + eps);"),
-    "scale_dropped": ("const double rq = scale / sqrt(ssq + eps);",
-                      "const double rq = 1.0 / sqrt(ssq + eps);"),
+    "eps_outside_sqrt": ("const double rk = l2norm ? 1.0 / sqrt(ssk + eps) : 1.0;",
+                         "const double rk = l2norm ? 1.0 / (sqrt(ssk) + eps) : 1.0;"),
+    "scale_dropped": ("const double rq = l2norm ? scale / sqrt(ssq + eps) : scale;",
+                      "const double rq = l2norm ? 1.0 / sqrt(ssq + eps) : scale;"),
     "gate_wrong_head": ("const double alpha = exp(g[(size_t)t * Nv + h]);",
                         "const double alpha = exp(g[(size_t)t * Nv + j]);"),
     "query_unnormalised": ("ssq += qt[c] * qt[c];", "ssq += 1.0;"),
