@@ -1,0 +1,240 @@
+"""Throughput of libgdr on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill|long|varlen]
+                    [--no-cpu-baseline]
+
+One step is one pass of the whole hot path on synthetic, seeded inputs that
+are resident in HBM before the timed region starts:
+  * gdr_chunk_fwd on the prefill workload (default: B=1, T=4096, Nqk=16,
+    Nv=32, D=128, bf16 q/k/v, fp32 gates and states), and
+  * gdr_recurrent_step on the decode workload (256 sequences x 1 token, same
+    heads, fp32 states updated in place).
+``value`` is the chunkwise forward's tokens/s from the GPU time of its kernels
+(HIP events recorded around every launch inside the timed region); the decode
+step's GB/s and both rooflines are reported beside it.  ``ms_per_step`` is
+the host wall clock of a whole step.  rank 0 prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBPS = 8000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}
+D = 128
+L = 128
+
+
+def alg_flops_chunk(lengths, Nqk, Nv):
+    """Algorithmic FLOPs of the chunkwise forward, split by the kernel that
+    performs each term: intra (Grams once per query/key head, the triangular
+    inverse, the U/W/P products on triangles) and inter (the three products
+    with the state: W S^T, Q S^T, V_new^T K)."""
+    intra = inter = 0.0
+    for n in lengths:
+        full, tail = divmod(int(n), L)
+        for ell, cnt in ((L, full), (tail, 1 if tail else 0)):
+            if cnt == 0:
+                continue
+            intra += cnt * (Nqk * 2 * D * ell * ell + Nv * (ell ** 3 / 3 + 3 * D * ell * (ell + 1)))
+            inter += cnt * Nv * 6 * ell * D * D
+    return intra, inter
+
+
+def alg_bytes_decode(N, Nqk, Nv, es=2):
+    state = N * Nv * D * D * 4 * 2
+    qkv = N * (2 * Nqk + Nv) * D * es
+    gb = N * Nv * 4 * 2
+    out = N * Nv * D * es
+    return state + qkv + gb + out
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", choices=["prefill", "long", "varlen"], default="prefill")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the gated delta rule shards over sequences and "
+              "value heads with no exchange, and this build runs on a single MI355X; "
+              "use --gpus 1", file=sys.stderr)
+        return 2
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    import gated_deltanet_chunked_amd as gdr
+    from gated_deltanet_chunked_amd.inputs import config_inputs, CONFIG_NAMES
+    gdr.load()   # raises if libgdr.so is missing: there is no fallback
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    scale = D ** -0.5
+
+    cfg = {"prefill": 1, "varlen": 2, "long": 3}[args.workload]
+    pre = config_inputs(cfg)
+    dec = config_inputs(4)
+
+    def to_dev(inp):
+        dt = torch.bfloat16 if inp.dtype == "bf16" else torch.float32
+        return dict(q=torch.from_numpy(inp.q).to(dev, dt), k=torch.from_numpy(inp.k).to(dev, dt),
+                    v=torch.from_numpy(inp.v).to(dev, dt), g=torch.from_numpy(inp.g).to(dev),
+                    beta=torch.from_numpy(inp.beta).to(dev),
+                    cu=torch.from_numpy(inp.cu_seqlens).to(dev),
+                    s0=torch.from_numpy(inp.state_in).to(dev))
+
+    P, Dd = to_dev(pre), to_dev(dec)
+    T, N, Nqk, Nv = pre.T, pre.N, pre.Nqk, pre.Nv
+    out = torch.empty((T, Nv, D), dtype=P["q"].dtype, device=dev)
+    sout = torch.empty_like(P["s0"])
+    ws = torch.empty(gdr.workspace_size(T, N, Nqk, Nv, gdr.GDR_BF16), dtype=torch.uint8, device=dev)
+    dstate = Dd["s0"].clone()
+    dout = torch.empty((dec.N, dec.Nv, D), dtype=Dd["q"].dtype, device=dev)
+
+    def step(timings):
+        gdr.chunk_fwd(P["q"], P["k"], P["v"], P["g"], P["beta"], P["cu"], P["s0"], scale=scale,
+                      out=out, state_out=sout, workspace=ws, timings=timings)
+        e0.record()
+        gdr.recurrent_step(Dd["q"], Dd["k"], Dd["v"], Dd["g"], Dd["beta"], dstate,
+                           state_out=dstate, out=dout, scale=scale)
+        e1.record()
+
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    for _ in range(args.warmup):
+        step([])
+    torch.cuda.synchronize()
+
+    chunk_ms, dec_ms = [], []
+    per_kernel = {}
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        tim = []
+        step(tim)
+        e1.synchronize()
+        dec_ms.append(e0.elapsed_time(e1))
+        chunk_ms.append(sum(ms for _, ms in tim))
+        for name, ms in tim:
+            per_kernel.setdefault(name, []).append(ms)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    # ---- prefill figures
+    lengths = np.diff(pre.cu_seqlens).tolist()
+    f_intra, f_inter = alg_flops_chunk(lengths, Nqk, Nv)
+    f_total = f_intra + f_inter
+    chunk_s = float(np.mean(chunk_ms)) * 1e-3
+    tok_s = T / chunk_s
+    # average duration of one launch of each kernel, and launches per call
+    kstats = {}
+    for name, lst in per_kernel.items():
+        kstats[name] = dict(avg_ms=float(np.mean(lst)), launches_per_call=len(lst) / args.steps)
+    # ---- decode figures
+    dec_s = float(np.mean(dec_ms)) * 1e-3
+    dec_bytes = alg_bytes_decode(dec.N, dec.Nqk, dec.Nv)
+    dec_gbps = dec_bytes / dec_s / 1e9
+
+    # the dominant kernel: the one with the most GPU time per step
+    per_step = {name: s["avg_ms"] * s["launches_per_call"] for name, s in kstats.items()}
+    per_step["decode"] = dec_s * 1e3
+    dom = max(per_step, key=per_step.get)
+    if dom == "decode":
+        roof = dict(kernel="decode", bound="hbm", achieved=round(dec_gbps, 1), peak=HBM_PEAK_GBPS,
+                    unit="GB/s", frac=round(dec_gbps / HBM_PEAK_GBPS, 4), traffic=None,
+                    per_launch=f"{dec_bytes} algorithmic bytes")
+    else:
+        f_dom = {"intra": f_intra, "inter": f_inter}.get(dom, 0.0)
+        launches = per_kernel[dom]
+        per_launch_flops = f_dom / kstats[dom]["launches_per_call"]
+        ach = per_launch_flops / (kstats[dom]["avg_ms"] * 1e-3) / 1e12
+        roof = dict(kernel=dom, bound="mfma", achieved=round(ach, 2), peak=MFMA_PEAK_TFLOPS["bf16"],
+                    unit="TFLOP/s", frac=round(ach / MFMA_PEAK_TFLOPS["bf16"], 4), traffic=None,
+                    per_launch=f"{per_launch_flops:.4g} algorithmic FLOP")
+        del launches
+
+    res = {
+        "metric": "chunk GDR fwd tokens/s + % MFMA peak; decode-step GB/s (% HBM peak)",
+        "value": round(tok_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; distributions of the Qwen3-Next gate initialisation)",
+        "config": {"workload": CONFIG_NAMES[cfg] + " + " + CONFIG_NAMES[4],
+                   "tokens": T, "sequences": N, "Nqk": Nqk, "Nv": Nv, "D": D, "chunk": L,
+                   "decode_sequences": dec.N},
+        "chunk_fwd": {"gpu_ms": round(chunk_s * 1e3, 4), "tokens_per_s": round(tok_s, 1),
+                      "alg_tflops": round(f_total / chunk_s / 1e12, 2),
+                      "frac_bf16_mfma_peak": round(f_total / chunk_s / 1e12 / MFMA_PEAK_TFLOPS["bf16"], 4),
+                      "alg_gflop": round(f_total / 1e9, 3),
+                      "kernels": {k: {"avg_ms": round(v["avg_ms"], 4),
+                                      "launches_per_call": v["launches_per_call"]}
+                                  for k, v in kstats.items()}},
+        "decode": {"gpu_ms": round(dec_s * 1e3, 4), "gbps": round(dec_gbps, 1),
+                   "frac_hbm_peak": round(dec_gbps / HBM_PEAK_GBPS, 4),
+                   "tokens_per_s": round(dec.N / dec_s, 1), "alg_bytes": dec_bytes},
+        "roofline": roof,
+    }
+
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(pre, scale)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+def cpu_baseline(pre, scale):
+    """The fp64 oracle on the host cores, on a bounded sample of the prefill
+    workload: the first value heads of the first sequence, as many as fit in
+    roughly ten seconds (the rule is independent per head)."""
+    import oracle
+    threads = len(os.sched_getaffinity(0))
+    nthr = oracle.threads(threads)
+    G = pre.Nv // pre.Nqk
+    T0, T1 = int(pre.cu_seqlens[0]), int(pre.cu_seqlens[1])
+
+    def run(heads):
+        j0, j1 = heads[0] // G, heads[-1] // G + 1
+        t = time.perf_counter()
+        oracle.recurrent(pre.q[T0:T1, j0:j1], pre.k[T0:T1, j0:j1], pre.v[T0:T1, heads[0]:heads[-1] + 1],
+                         pre.g[T0:T1, heads[0]:heads[-1] + 1], pre.beta[T0:T1, heads[0]:heads[-1] + 1],
+                         None if pre.state_in is None else pre.state_in[:1, heads[0]:heads[-1] + 1],
+                         np.array([0, T1 - T0], np.int32), scale, nthreads=nthr)
+        return time.perf_counter() - t
+
+    heads = list(range(G))           # one query/key group first
+    dt = run(heads)
+    per_head = dt / len(heads)
+    nh = int(min(pre.Nv, max(G, (10.0 / max(per_head, 1e-6)) // G * G)))
+    if nh > len(heads):
+        heads = list(range(nh))
+        dt = run(heads)
+    # tokens/s of the whole workload at this rate: every head of every token
+    tok_s = (T1 - T0) * len(heads) / pre.Nv / dt
+    cpu = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": round(tok_s, 1), "unit": "tokens/s", "cores": nthr, "kind": "oracle",
+            "sample": f"first sequence ({T1 - T0} tokens), value heads 0..{len(heads) - 1} of "
+                      f"{pre.Nv}, fp64 per-token recurrence, {dt:.1f} s on {cpu}"}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,206 @@
+"""Python binding of libgdr, the gated delta rule on MI355X (gfx950).
+
+Thin ctypes marshalling over the C ABI in ``include/gdr.h``: every step of the
+computation runs in the HIP kernels of ``libgdr.so``.  PyTorch provides device
+memory and the current stream only.  There is no fallback: if the library is
+missing, every call raises.
+
+    out, state = chunk_fwd(q, k, v, g, beta, cu_seqlens, state_in=s0)
+    out = recurrent_step(q, k, v, g, beta, state, state_out=state)   # in place
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libgdr.so")
+
+GDR_F32 = 0
+GDR_BF16 = 1
+GDR_FLAG_QK_L2NORM = 1
+CHUNK = 128
+D = 128
+
+STATUS = {0: "GDR_OK", -1: "GDR_ERR_INVALID_ARGUMENT", -2: "GDR_ERR_UNSUPPORTED",
+          -3: "GDR_ERR_WORKSPACE_TOO_SMALL", -4: "GDR_ERR_HIP"}
+
+_lib = None
+
+
+class GdrError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {STATUS.get(status, status)}")
+        self.status = status
+
+
+def load(path: str = LIB_PATH):
+    """Load libgdr.so and declare the C signatures (no GPU needed)."""
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    try:
+        # torch ships its own HIP runtime; loading torch first makes libgdr bind
+        # to that same runtime (one HIP runtime per process)
+        import torch  # noqa: F401
+    except ImportError:
+        pass
+    if not os.path.exists(path):
+        raise RuntimeError(f"libgdr.so not built at {path}: run `python -m gated_deltanet_chunked_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32, u32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_float, ctypes.c_size_t
+    lib.gdr_chunk_fwd_workspace_size.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int]
+    lib.gdr_chunk_fwd_workspace_size.restype = sz
+    lib.gdr_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_int,
+                                  f32, u32, vp, vp, vp, sz, vp]
+    lib.gdr_chunk_fwd.restype = ctypes.c_int
+    lib.gdr_recurrent_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, ctypes.c_int,
+                                       f32, u32, vp, vp]
+    lib.gdr_recurrent_step.restype = ctypes.c_int
+    lib.gdr_chunk_fwd_timed.argtypes = lib.gdr_chunk_fwd.argtypes + [
+        ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_int32), i32,
+        ctypes.POINTER(ctypes.c_int32)]
+    lib.gdr_chunk_fwd_timed.restype = ctypes.c_int
+    lib.gdr_status_string.argtypes = [ctypes.c_int]
+    lib.gdr_status_string.restype = ctypes.c_char_p
+    lib.gdr_version.argtypes = []
+    lib.gdr_version.restype = ctypes.c_char_p
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return GDR_BF16
+    if t.dtype == torch.float32:
+        return GDR_F32
+    raise TypeError(f"q/k/v must be bfloat16 or float32, got {t.dtype}")
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _check(t, name, shape, dtype, device):
+    if t is None:
+        return
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must be on {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def _stream() -> int:
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def workspace_size(T: int, N: int, Nqk: int, Nv: int, dtype_code: int) -> int:
+    return int(load().gdr_chunk_fwd_workspace_size(T, N, Nqk, Nv, D, dtype_code))
+
+
+STAGE_NAMES = {0: "table", 1: "prep", 2: "intra", 3: "inter"}
+
+
+def chunk_fwd(q, k, v, g, beta, cu_seqlens, state_in=None, *, scale: Optional[float] = None,
+              out=None, state_out=None, want_state: bool = True, workspace=None,
+              l2norm: bool = True, timings: Optional[list] = None
+              ) -> Tuple["torch.Tensor", Optional["torch.Tensor"]]:
+    """Chunkwise gated delta rule over packed sequences (``gdr_chunk_fwd``).
+
+    q, k [T, Nqk, 128], v [T, Nv, 128] (bf16 or f32); g, beta [T, Nv] f32;
+    cu_seqlens [N + 1] int32 (device); state_in [N, Nv, 128, 128] f32 or None.
+    Returns (out [T, Nv, 128] in q's dtype, state_out or None).
+    ``state_out`` may be ``state_in`` for an in-place update.
+    With a list as ``timings`` the call goes through ``gdr_chunk_fwd_timed``
+    (blocking) and appends one (stage name, GPU milliseconds) per kernel.
+    """
+    import torch
+    lib = load()
+    T, Nqk, _ = q.shape
+    Nv = v.shape[1]
+    N = cu_seqlens.shape[0] - 1
+    dev = q.device
+    dt = q.dtype
+    code = _dtype_code(q)
+    _check(q, "q", (T, Nqk, D), dt, dev)
+    _check(k, "k", (T, Nqk, D), dt, dev)
+    _check(v, "v", (T, Nv, D), dt, dev)
+    _check(g, "g", (T, Nv), torch.float32, dev)
+    _check(beta, "beta", (T, Nv), torch.float32, dev)
+    _check(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32, dev)
+    _check(state_in, "state_in", (N, Nv, D, D), torch.float32, dev)
+    if out is None:
+        out = torch.empty((T, Nv, D), dtype=dt, device=dev)
+    _check(out, "out", (T, Nv, D), dt, dev)
+    if state_out is None and want_state:
+        state_out = torch.empty((N, Nv, D, D), dtype=torch.float32, device=dev)
+    _check(state_out, "state_out", (N, Nv, D, D), torch.float32, dev)
+    need = workspace_size(T, N, Nqk, Nv, code)
+    if need == 0:
+        raise GdrError(-1, "gdr_chunk_fwd_workspace_size")
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if scale is None:
+        scale = D ** -0.5
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_in),
+            _ptr(cu_seqlens), N, T, Nqk, Nv, D, code, float(scale),
+            GDR_FLAG_QK_L2NORM if l2norm else 0, _ptr(out), _ptr(state_out),
+            _ptr(workspace), workspace.numel(), _stream())
+    if timings is None:
+        st = lib.gdr_chunk_fwd(*args)
+        if st != 0:
+            raise GdrError(st, "gdr_chunk_fwd")
+        return out, state_out
+    cap = 64
+    ms = (ctypes.c_float * cap)()
+    kind = (ctypes.c_int32 * cap)()
+    n = ctypes.c_int32(0)
+    st = lib.gdr_chunk_fwd_timed(*args, ms, kind, cap, ctypes.byref(n))
+    if st != 0:
+        raise GdrError(st, "gdr_chunk_fwd_timed")
+    timings.extend((STAGE_NAMES.get(kind[i], str(kind[i])), float(ms[i])) for i in range(n.value))
+    return out, state_out
+
+
+def recurrent_step(q, k, v, g, beta, state_in, *, state_out=None, out=None,
+                   scale: Optional[float] = None, l2norm: bool = True):
+    """One decode step for N sequences (``gdr_recurrent_step``).
+
+    q, k [N, Nqk, 128], v [N, Nv, 128]; g, beta [N, Nv]; state_in [N, Nv, 128, 128].
+    ``state_out`` defaults to ``state_in`` (in-place update).  Returns out [N, Nv, 128].
+    """
+    import torch
+    lib = load()
+    N, Nqk, _ = q.shape
+    Nv = v.shape[1]
+    dev = q.device
+    dt = q.dtype
+    code = _dtype_code(q)
+    _check(q, "q", (N, Nqk, D), dt, dev)
+    _check(k, "k", (N, Nqk, D), dt, dev)
+    _check(v, "v", (N, Nv, D), dt, dev)
+    _check(g, "g", (N, Nv), torch.float32, dev)
+    _check(beta, "beta", (N, Nv), torch.float32, dev)
+    _check(state_in, "state_in", (N, Nv, D, D), torch.float32, dev)
+    if state_out is None:
+        state_out = state_in
+    _check(state_out, "state_out", (N, Nv, D, D), torch.float32, dev)
+    if out is None:
+        out = torch.empty((N, Nv, D), dtype=dt, device=dev)
+    _check(out, "out", (N, Nv, D), dt, dev)
+    if scale is None:
+        scale = D ** -0.5
+    st = lib.gdr_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_in),
+                                _ptr(state_out), N, Nqk, Nv, D, code, float(scale),
+                                GDR_FLAG_QK_L2NORM if l2norm else 0, _ptr(out), _stream())
+    if st != 0:
+        raise GdrError(st, "gdr_recurrent_step")
+    return out

@@ -1,0 +1,179 @@
+// gdr_api.hip -- the extern "C" entry points of libgdr (declared in
+// include/gdr.h): argument validation, workspace carving and kernel launches
+// on the caller's stream.  No allocation, no synchronisation.
+#include <hip/hip_runtime.h>
+
+#include "../../include/gdr.h"
+#include "gdr_internal.h"
+#include "gdr_kernels.h"
+
+using namespace gdr;
+
+namespace {
+
+// Optional per-launch timing: an event is recorded on the stream before every
+// launch and after the last one.  With no event array it does nothing.
+struct Recorder {
+  hipEvent_t* ev = nullptr;
+  int32_t* kind = nullptr;
+  int32_t cap = 0;
+  int32_t n = 0;
+  hipStream_t st = nullptr;
+  void before(int32_t k) {
+    if (!ev) return;
+    if (n < cap) {
+      kind[n] = k;
+      hipEventRecord(ev[n], st);
+    }
+    ++n;
+  }
+  void end() {
+    if (ev && n <= cap) hipEventRecord(ev[n], st);
+  }
+};
+
+int32_t launches_needed(const Workspace& w) {
+  const int64_t segs = (w.nslots + w.seg_slots - 1) / w.seg_slots;
+  return static_cast<int32_t>(2 + 2 * segs);
+}
+
+template <typename T>
+gdr_status run_chunk(const ChunkArgs& a, hipStream_t st, Recorder& rec) {
+  const Workspace w = plan_workspace(a.T, a.N, a.Nqk, a.Nv, a.dtype);
+  char* ws = static_cast<char*>(a.workspace);
+  int4* table = reinterpret_cast<int4*>(ws + w.table);
+  int32_t* choff = reinterpret_cast<int32_t*>(ws + w.choff);
+  float* rq = reinterpret_cast<float*>(ws + w.rq);
+  float* rk = reinterpret_cast<float*>(ws + w.rk);
+  double* gcum = reinterpret_cast<double*>(ws + w.gcum);
+  T* inter = reinterpret_cast<T*>(ws + w.inter);
+  float* carry = a.state_out ? a.state_out : reinterpret_cast<float*>(ws + w.carry);
+  const T* q = static_cast<const T*>(a.q);
+  const T* k = static_cast<const T*>(a.k);
+  const T* v = static_cast<const T*>(a.v);
+  T* out = static_cast<T*>(a.out);
+  const int norm = (a.flags & GDR_FLAG_QK_L2NORM) ? 1 : 0;
+  const int32_t nslots = static_cast<int32_t>(w.nslots);
+
+  rec.before(GDR_STAGE_TABLE);
+  launch_table(a.cu_seqlens, a.N, a.T, nslots, table, choff, st);
+  rec.before(GDR_STAGE_PREP);
+  launch_prep<T>(q, k, a.g, table, nslots, a.T, a.Nqk, a.Nv, a.scale, norm, rq, rk, gcum, st);
+  for (int64_t s0 = 0; s0 < w.nslots; s0 += w.seg_slots) {
+    const int32_t nseg = static_cast<int32_t>(w.nslots - s0 < w.seg_slots ? w.nslots - s0 : w.seg_slots);
+    rec.before(GDR_STAGE_INTRA);
+    launch_intra<T>(q, k, v, a.beta, table, rq, rk, gcum, a.T, a.Nqk, a.Nv,
+                    static_cast<int32_t>(s0), nseg, inter, st);
+    rec.before(GDR_STAGE_INTER);
+    launch_inter<T>(inter, table, choff, gcum, a.state_in, carry, a.state_out, a.N, a.T, a.Nv,
+                    static_cast<int32_t>(s0), nseg, s0 == 0, out, st);
+  }
+  rec.end();
+  return hipGetLastError() == hipSuccess ? GDR_OK : GDR_ERR_HIP;
+}
+
+gdr_status dispatch_chunk(const ChunkArgs& a, hipStream_t st, Recorder& rec) {
+  if (a.dtype == GDR_BF16) return run_chunk<__bf16>(a, st, rec);
+  return run_chunk<float>(a, st, rec);
+}
+
+}  // namespace
+
+extern "C" size_t gdr_chunk_fwd_workspace_size(int32_t T, int32_t N, int32_t Nqk, int32_t Nv,
+                                               int32_t D, gdr_dtype dtype) {
+  if (T < 0 || N < 1 || Nqk < 1 || Nv < 1 || Nv % Nqk != 0 || D != 128) return 0;
+  if (dtype != GDR_F32 && dtype != GDR_BF16) return 0;
+  if (static_cast<int64_t>(T) * Nv > (int64_t(1) << 40)) return 0;
+  return static_cast<size_t>(plan_workspace(T, N, Nqk, Nv, dtype).total);
+}
+
+extern "C" gdr_status gdr_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
+                                    const float* beta, const float* state_in,
+                                    const int32_t* cu_seqlens, int32_t N, int32_t T, int32_t Nqk,
+                                    int32_t Nv, int32_t D, gdr_dtype dtype, float scale,
+                                    uint32_t flags, void* out, float* state_out, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  ChunkArgs a{q, k, v, g, beta, state_in, cu_seqlens, N, T, Nqk, Nv, D, dtype, scale, flags,
+              out, state_out, workspace, workspace_bytes};
+  const gdr_status s = validate_chunk(a);
+  if (s != GDR_OK) return s;
+  Recorder none;
+  return dispatch_chunk(a, static_cast<hipStream_t>(stream), none);
+}
+
+extern "C" gdr_status gdr_chunk_fwd_timed(const void* q, const void* k, const void* v,
+                                          const float* g, const float* beta,
+                                          const float* state_in, const int32_t* cu_seqlens,
+                                          int32_t N, int32_t T, int32_t Nqk, int32_t Nv, int32_t D,
+                                          gdr_dtype dtype, float scale, uint32_t flags, void* out,
+                                          float* state_out, void* workspace,
+                                          size_t workspace_bytes, void* stream, float* kernel_ms,
+                                          int32_t* kernel_kind, int32_t max_kernels, int32_t* n) {
+  ChunkArgs a{q, k, v, g, beta, state_in, cu_seqlens, N, T, Nqk, Nv, D, dtype, scale, flags,
+              out, state_out, workspace, workspace_bytes};
+  gdr_status s = validate_chunk(a);
+  if (s != GDR_OK) return s;
+  if (!kernel_ms || !kernel_kind || !n || max_kernels < 0) return GDR_ERR_INVALID_ARGUMENT;
+  const int32_t need = launches_needed(plan_workspace(T, N, Nqk, Nv, dtype));
+  if (need > max_kernels) return GDR_ERR_INVALID_ARGUMENT;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipEvent_t ev[64];
+  const int32_t nev = need + 1;
+  if (nev > 64) return GDR_ERR_INVALID_ARGUMENT;
+  int32_t made = 0;
+  for (; made < nev; ++made)
+    if (hipEventCreate(&ev[made]) != hipSuccess) break;
+  if (made < nev) {
+    for (int32_t i = 0; i < made; ++i) hipEventDestroy(ev[i]);
+    return GDR_ERR_HIP;
+  }
+  Recorder rec;
+  rec.ev = ev;
+  rec.kind = kernel_kind;
+  rec.cap = need;
+  rec.st = st;
+  s = dispatch_chunk(a, st, rec);
+  if (s == GDR_OK && hipEventSynchronize(ev[rec.n]) != hipSuccess) s = GDR_ERR_HIP;
+  if (s == GDR_OK) {
+    for (int32_t i = 0; i < rec.n; ++i)
+      if (hipEventElapsedTime(&kernel_ms[i], ev[i], ev[i + 1]) != hipSuccess) s = GDR_ERR_HIP;
+    *n = rec.n;
+  }
+  for (int32_t i = 0; i < nev; ++i) hipEventDestroy(ev[i]);
+  return s;
+}
+
+extern "C" gdr_status gdr_recurrent_step(const void* q, const void* k, const void* v,
+                                         const float* g, const float* beta, const float* state_in,
+                                         float* state_out, int32_t N, int32_t Nqk, int32_t Nv,
+                                         int32_t D, gdr_dtype dtype, float scale, uint32_t flags,
+                                         void* out, void* stream) {
+  StepArgs a{q, k, v, g, beta, state_in, state_out, N, Nqk, Nv, D, dtype, scale, flags, out};
+  const gdr_status s = validate_step(a);
+  if (s != GDR_OK) return s;
+  if (N == 0) return GDR_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int norm = (flags & GDR_FLAG_QK_L2NORM) ? 1 : 0;
+  if (dtype == GDR_BF16)
+    launch_decode<__bf16>(static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
+                          static_cast<const __bf16*>(v), g, beta, state_in, state_out, N, Nqk, Nv,
+                          scale, norm, static_cast<__bf16*>(out), st);
+  else
+    launch_decode<float>(static_cast<const float*>(q), static_cast<const float*>(k),
+                         static_cast<const float*>(v), g, beta, state_in, state_out, N, Nqk, Nv,
+                         scale, norm, static_cast<float*>(out), st);
+  return hipGetLastError() == hipSuccess ? GDR_OK : GDR_ERR_HIP;
+}
+
+extern "C" const char* gdr_status_string(gdr_status s) {
+  switch (s) {
+    case GDR_OK: return "ok";
+    case GDR_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case GDR_ERR_UNSUPPORTED: return "unsupported size, dtype or flag";
+    case GDR_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case GDR_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+extern "C" const char* gdr_version(void) { return "libgdr 0.1"; }

@@ -1,0 +1,114 @@
+// gdr_decode.hip -- one decode step of the gated delta rule (Qwen3-Next blog
+// post, section 5(2), a single iteration of the token loop):
+//   S  <- exp(g) S;  u = S kh;  S <- S + beta (v - u) kh^T;  o = S qh
+// computed in one pass over S as
+//   a = S_old kh,  b = S_old qh,  delta = beta (v - exp(g) a),
+//   o = exp(g) b + delta (kh . qh),  S_new = exp(g) S_old + delta kh^T.
+// Bandwidth bound: each (sequence, head) state (64 KiB fp32) is read once and
+// written once.  One workgroup of 256 threads per (sequence, head); thread t
+// holds columns 8 (t & 15) .. +7 of rows (t >> 4) + 16 i, i < 8, so each row
+// is 16 consecutive threads reading 512 contiguous bytes, and the two row dot
+// products reduce across those 16 lanes.
+#include "gdr_device.h"
+#include "gdr_kernels.h"
+
+namespace gdr {
+
+template <typename T>
+__device__ __forceinline__ void load8(const T* p, float* x);
+template <>
+__device__ __forceinline__ void load8<float>(const float* p, float* x) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+template <>
+__device__ __forceinline__ void load8<__bf16>(const __bf16* p, float* x) {
+  const bf16x8 a = *reinterpret_cast<const bf16x8*>(p);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = (float)a[e];
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void decode_kernel(const T* __restrict__ q, const T* __restrict__ k,
+                                                     const T* __restrict__ v, const float* __restrict__ g,
+                                                     const float* __restrict__ beta,
+                                                     const float* state_in, float* state_out,
+                                                     int32_t Nqk, int32_t Nv, float scale, int norm,
+                                                     T* __restrict__ out) {
+  const int bh = blockIdx.x;
+  const int n = bh / Nv, h = bh % Nv;
+  const int j = h / (Nv / Nqk);
+  const int tid = threadIdx.x, l = tid & 63;
+  const int cg = tid & 15, rg = tid >> 4;
+  const size_t sb = (size_t)bh * kD * kD;
+
+  // issue the state loads first: 16 x 16 bytes in flight per thread
+  f32x4 s[8][2];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float* p = state_in + sb + (size_t)(rg + 16 * i) * kD + 8 * cg;
+    s[i][0] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+    s[i][1] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + 4));
+  }
+
+  const T* kp = k + ((size_t)n * Nqk + j) * kD;
+  const T* qp = q + ((size_t)n * Nqk + j) * kD;
+  float kh[8], qh[8];
+  load8<T>(kp + 8 * cg, kh);
+  load8<T>(qp + 8 * cg, qh);
+  float ssk = 0.f, ssq = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) { ssk += kh[e] * kh[e]; ssq += qh[e] * qh[e]; }
+  ssk = group16_sum(ssk);
+  ssq = group16_sum(ssq);
+  const float rk = norm ? 1.0f / sqrtf(ssk + 1e-6f) : 1.0f;
+  const float rq = (norm ? 1.0f / sqrtf(ssq + 1e-6f) : 1.0f) * scale;
+  float kq = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) { kh[e] *= rk; qh[e] *= rq; kq += kh[e] * qh[e]; }
+  kq = group16_sum(kq);
+  const float alpha = expf(g[(size_t)n * Nv + h]);
+  const float bt = beta[(size_t)n * Nv + h];
+  const T* vp = v + ((size_t)n * Nv + h) * kD;
+  T* op = out + ((size_t)n * Nv + h) * kD;
+
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int row = rg + 16 * i;
+    float x[8] = {s[i][0][0], s[i][0][1], s[i][0][2], s[i][0][3],
+                  s[i][1][0], s[i][1][1], s[i][1][2], s[i][1][3]};
+    float a = 0.f, b = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) { a += x[e] * kh[e]; b += x[e] * qh[e]; }
+    a = group16_sum(a);
+    b = group16_sum(b);
+    const float delta = bt * (to_f32(vp[row]) - alpha * a);
+    if (cg == 0) op[row] = from_f32<T>(alpha * b + delta * kq);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = alpha * x[e] + delta * kh[e];
+    float* p = state_out + sb + (size_t)row * kD + 8 * cg;
+    const f32x4 y0 = {x[0], x[1], x[2], x[3]}, y1 = {x[4], x[5], x[6], x[7]};
+    __builtin_nontemporal_store(y0, reinterpret_cast<f32x4*>(p));
+    __builtin_nontemporal_store(y1, reinterpret_cast<f32x4*>(p + 4));
+  }
+  (void)l;
+}
+
+template <typename T>
+void launch_decode(const T* q, const T* k, const T* v, const float* g, const float* beta,
+                   const float* state_in, float* state_out, int32_t N, int32_t Nqk, int32_t Nv,
+                   float scale, int norm, T* out, hipStream_t stream) {
+  hipLaunchKernelGGL(decode_kernel<T>, dim3((unsigned)N * (unsigned)Nv), dim3(256), 0, stream, q, k,
+                     v, g, beta, state_in, state_out, Nqk, Nv, scale, norm, out);
+}
+
+template void launch_decode<float>(const float*, const float*, const float*, const float*,
+                                   const float*, const float*, float*, int32_t, int32_t, int32_t,
+                                   float, int, float*, hipStream_t);
+template void launch_decode<__bf16>(const __bf16*, const __bf16*, const __bf16*, const float*,
+                                    const float*, const float*, float*, int32_t, int32_t, int32_t,
+                                    float, int, __bf16*, hipStream_t);
+
+}  // namespace gdr

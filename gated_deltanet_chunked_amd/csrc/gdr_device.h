@@ -1,0 +1,149 @@
+// gdr_device.h -- device-side building blocks shared by the libgdr kernels:
+// element types, 16x16 matrix-core (MFMA) fragments for gfx950, and wave
+// reductions.  gfx950 only; wave64.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdr {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+constexpr int kD = 128;      // head dimension (Dk = Dv)
+constexpr int kL = 128;      // chunk length
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(__bf16 x) { return (float)x; }
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ __bf16 from_f32<__bf16>(float x) { return (__bf16)x; }
+
+// ---------------------------------------------------------------------------
+// 16x16 output-tile MFMA.  For every operand type the lane layout is:
+//   A fragment: row  (lane & 15), k = (lane >> 4) * E + e, e < E
+//   B fragment: col  (lane & 15), k = (lane >> 4) * E + e, e < E
+//   C (f32x4):  col  (lane & 15), row = (lane >> 4) * 4 + i, i < 4
+// with E = K / 4 values per lane (bf16: K = 32, E = 8; f32: K = 4, E = 1).
+// ---------------------------------------------------------------------------
+template <typename T> struct Mma;
+
+template <> struct Mma<__bf16> {
+  static constexpr int K = 32;
+  static constexpr int E = 8;
+  typedef bf16x8 frag;
+  static __device__ __forceinline__ f32x4 mma(const frag& a, const frag& b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  // E consecutive elements at p (16-byte aligned)
+  static __device__ __forceinline__ frag load_contig(const __bf16* p) {
+    return *reinterpret_cast<const bf16x8*>(p);
+  }
+  static __device__ __forceinline__ frag load_strided(const __bf16* p, int stride) {
+    frag f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = p[e * stride];
+    return f;
+  }
+  static __device__ __forceinline__ frag zero() {
+    frag f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = (__bf16)0.0f;
+    return f;
+  }
+};
+
+template <> struct Mma<float> {
+  static constexpr int K = 4;
+  static constexpr int E = 1;
+  typedef float frag;
+  static __device__ __forceinline__ f32x4 mma(const frag& a, const frag& b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ frag load_contig(const float* p) { return *p; }
+  static __device__ __forceinline__ frag load_strided(const float* p, int) { return *p; }
+  static __device__ __forceinline__ frag zero() { return 0.0f; }
+};
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// Operand view of a row-major matrix in memory (LDS or global):
+// element (r, c) = base[r * ld + c].  A GEMM reads operand A as (m, k) and
+// operand B as (n, k).  With KCONTIG the k index is the column c (k runs along
+// a row, one vector load per fragment); otherwise k is the row r.
+template <typename T, bool KCONTIG>
+struct Operand {
+  const T* base;
+  int ld;
+  __device__ __forceinline__ typename Mma<T>::frag frag(int mn, int k) const {
+    if (KCONTIG) return Mma<T>::load_contig(base + (size_t)mn * ld + k);
+    return Mma<T>::load_strided(base + (size_t)k * ld + mn, ld);
+  }
+};
+
+// One 16x16 output tile: acc += sum_k A(m0 + ., k) B(n0 + ., k) over k in [k0, k1).
+template <typename T, bool AK, bool BK>
+__device__ __forceinline__ void mma_tile(f32x4& acc, const Operand<T, AK>& A, const Operand<T, BK>& B,
+                                         int m0, int n0, int k0, int k1) {
+  const int l = lane_id();
+  const int r = l & 15;
+  const int kq = (l >> 4) * Mma<T>::E;
+  for (int k = k0; k < k1; k += Mma<T>::K) {
+    auto a = A.frag(m0 + r, k + kq);
+    auto b = B.frag(n0 + r, k + kq);
+    acc = Mma<T>::mma(a, b, acc);
+  }
+}
+
+// A wave's 64x64 block of a 128x128 product: tiles (m0 + 16i, n0 + 16j),
+// i, j < 4, reduction over k in [0, K).  A and B fragments are each loaded
+// once per k step and reused four times.
+template <typename T, bool AK, bool BK>
+__device__ __forceinline__ void mma_block64(f32x4 (&acc)[4][4], const Operand<T, AK>& A,
+                                            const Operand<T, BK>& B, int m0, int n0, int K) {
+  const int l = lane_id();
+  const int r = l & 15;
+  const int kq = (l >> 4) * Mma<T>::E;
+#pragma unroll 2
+  for (int k = 0; k < K; k += Mma<T>::K) {
+    typename Mma<T>::frag a[4], b[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = A.frag(m0 + 16 * i + r, k + kq);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b[j] = B.frag(n0 + 16 * j + r, k + kq);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = Mma<T>::mma(a[i], b[j], acc[i][j]);
+  }
+}
+
+template <int M, int N>
+__device__ __forceinline__ void zero_acc(f32x4 (&acc)[M][N]) {
+#pragma unroll
+  for (int i = 0; i < M; ++i)
+#pragma unroll
+    for (int j = 0; j < N; ++j) acc[i][j] = zero4();
+}
+
+// Sum over the 64 lanes of a wave; every lane gets the total.
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+
+// Sum over aligned groups of 16 lanes; every lane of the group gets the total.
+__device__ __forceinline__ float group16_sum(float x) {
+#pragma unroll
+  for (int off = 8; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+
+}  // namespace gdr

@@ -1,0 +1,75 @@
+// gdr_internal.h -- host-side plumbing of libgdr: workspace layout and the
+// HIP-free argument validation shared by the C entry points.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/gdr.h"
+
+namespace gdr {
+
+// Number of 128-token chunk slots reserved for T packed tokens in N
+// sequences.  Chunks restart at every sequence start, so sequence b needs
+// ceil(len_b / 128) <= floor(len_b / 128) + 1 slots, and the sum over b is at
+// most floor(T / 128) + N.
+inline int64_t max_slots(int64_t T, int64_t N) { return T / 128 + N; }
+
+// Chunk slots processed per segment: the intra-chunk products of one segment
+// are written to the workspace and consumed by the state pass of the same
+// segment before the next segment reuses the buffer.
+inline int64_t segment_slots(int64_t nslots, int64_t Nv) {
+  (void)Nv;
+  const int64_t seg = 64;
+  return nslots <= seg + seg / 2 ? nslots : seg;
+}
+
+// Per (chunk slot, value head): four 128x128 matrices of the chunk's affine
+// state transition and output terms (see gdr_intra.hip).
+constexpr int64_t kInterMats = 4;
+constexpr int64_t kMatElems = 128 * 128;
+
+struct Workspace {
+  int64_t table;      // int32 [nslots][4]: {sequence, first token, length, 0}; sequence -1 = unused
+  int64_t choff;      // int32 [N + 1]: first slot of each sequence
+  int64_t rq;         // float [Nqk][T]: scale / |q|
+  int64_t rk;         // float [Nqk][T]: 1 / |k|
+  int64_t gcum;       // double [Nv][T]: chunk-local cumulative sum of g
+  int64_t inter;      // [seg_slots][Nv][4][128][128] of the matrix-core operand type
+  int64_t carry;      // float [N][Nv][128][128]: state between segments
+  int64_t total;
+  int64_t nslots;
+  int64_t seg_slots;
+};
+
+Workspace plan_workspace(int64_t T, int64_t N, int64_t Nqk, int64_t Nv, gdr_dtype dtype);
+
+struct ChunkArgs {
+  const void* q; const void* k; const void* v;
+  const float* g; const float* beta;
+  const float* state_in; const int32_t* cu_seqlens;
+  int32_t N, T, Nqk, Nv, D;
+  gdr_dtype dtype;
+  float scale;
+  uint32_t flags;
+  void* out; float* state_out;
+  void* workspace; size_t workspace_bytes;
+};
+
+struct StepArgs {
+  const void* q; const void* k; const void* v;
+  const float* g; const float* beta;
+  const float* state_in; float* state_out;
+  int32_t N, Nqk, Nv, D;
+  gdr_dtype dtype;
+  float scale;
+  uint32_t flags;
+  void* out;
+};
+
+gdr_status validate_chunk(const ChunkArgs& a);
+gdr_status validate_step(const StepArgs& a);
+
+inline size_t dtype_size(gdr_dtype d) { return d == GDR_BF16 ? 2 : 4; }
+
+}  // namespace gdr

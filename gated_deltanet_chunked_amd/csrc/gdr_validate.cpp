@@ -1,0 +1,122 @@
+// gdr_validate.cpp -- argument checks and workspace layout of libgdr.
+// Plain C++: no HIP calls, so every error path runs without a GPU.
+#include <stdint.h>
+
+#include "gdr_internal.h"
+
+namespace gdr {
+namespace {
+
+constexpr uint32_t kKnownFlags = GDR_FLAG_QK_L2NORM;
+
+int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// [p, p + n) and [q, q + m) overlap (both non-empty).
+bool overlap(const void* p, int64_t n, const void* q, int64_t m) {
+  if (!p || !q || n <= 0 || m <= 0) return false;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(q);
+  return a < b + static_cast<uintptr_t>(m) && b < a + static_cast<uintptr_t>(n);
+}
+
+gdr_status common_sizes(int32_t Nqk, int32_t Nv, int32_t D, gdr_dtype dtype, uint32_t flags) {
+  if (D != 128) return GDR_ERR_UNSUPPORTED;
+  if (dtype != GDR_F32 && dtype != GDR_BF16) return GDR_ERR_UNSUPPORTED;
+  if (flags & ~kKnownFlags) return GDR_ERR_UNSUPPORTED;
+  if (Nqk <= 0 || Nv <= 0 || Nv % Nqk != 0) return GDR_ERR_INVALID_ARGUMENT;
+  return GDR_OK;
+}
+
+}  // namespace
+
+Workspace plan_workspace(int64_t T, int64_t N, int64_t Nqk, int64_t Nv, gdr_dtype dtype) {
+  Workspace w{};
+  w.nslots = max_slots(T, N);
+  w.seg_slots = segment_slots(w.nslots, Nv);
+  int64_t off = 0;
+  w.table = off; off = align256(off + w.nslots * 4 * 4);
+  w.choff = off; off = align256(off + (N + 1) * 4);
+  w.rq = off; off = align256(off + Nqk * T * 4);
+  w.rk = off; off = align256(off + Nqk * T * 4);
+  w.gcum = off; off = align256(off + Nv * T * 8);
+  w.inter = off;
+  off = align256(off + w.seg_slots * Nv * kInterMats * kMatElems * static_cast<int64_t>(dtype_size(dtype)));
+  w.carry = off; off = align256(off + N * Nv * kMatElems * 4);
+  w.total = off;
+  return w;
+}
+
+gdr_status validate_chunk(const ChunkArgs& a) {
+  gdr_status s = common_sizes(a.Nqk, a.Nv, a.D, a.dtype, a.flags);
+  if (s != GDR_OK) return s;
+  if (a.N < 1 || a.T < 0) return GDR_ERR_INVALID_ARGUMENT;
+  // every element offset must fit comfortably in 63 bits; the kernels also
+  // index tokens with 32-bit integers
+  if (static_cast<int64_t>(a.T) * a.Nv > (int64_t(1) << 40)) return GDR_ERR_INVALID_ARGUMENT;
+  if (!a.cu_seqlens || !a.workspace) return GDR_ERR_INVALID_ARGUMENT;
+  if (a.T > 0 && (!a.q || !a.k || !a.v || !a.g || !a.beta || !a.out)) return GDR_ERR_INVALID_ARGUMENT;
+  const void* ptrs[] = {a.q, a.k, a.v, a.g, a.beta, a.state_in, a.cu_seqlens, a.out, a.state_out};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return GDR_ERR_INVALID_ARGUMENT;
+  if ((reinterpret_cast<uintptr_t>(a.workspace) & 255u) != 0) return GDR_ERR_INVALID_ARGUMENT;
+  const Workspace w = plan_workspace(a.T, a.N, a.Nqk, a.Nv, a.dtype);
+  if (a.workspace_bytes < static_cast<size_t>(w.total)) return GDR_ERR_WORKSPACE_TOO_SMALL;
+
+  const int64_t es = static_cast<int64_t>(dtype_size(a.dtype));
+  const int64_t qk_bytes = static_cast<int64_t>(a.T) * a.Nqk * 128 * es;
+  const int64_t v_bytes = static_cast<int64_t>(a.T) * a.Nv * 128 * es;
+  const int64_t gb_bytes = static_cast<int64_t>(a.T) * a.Nv * 4;
+  const int64_t st_bytes = static_cast<int64_t>(a.N) * a.Nv * 128 * 128 * 4;
+  const int64_t cu_bytes = (static_cast<int64_t>(a.N) + 1) * 4;
+  // out overlaps nothing else
+  struct R { const void* p; int64_t n; } in[] = {
+      {a.q, qk_bytes}, {a.k, qk_bytes}, {a.v, v_bytes}, {a.g, gb_bytes}, {a.beta, gb_bytes},
+      {a.state_in, st_bytes}, {a.cu_seqlens, cu_bytes}, {a.state_out, st_bytes},
+      {a.workspace, static_cast<int64_t>(a.workspace_bytes)}};
+  for (const R& r : in)
+    if (overlap(a.out, v_bytes, r.p, r.n)) return GDR_ERR_INVALID_ARGUMENT;
+  // state_out may equal state_in exactly, but not overlap it partially, and
+  // overlaps no other input
+  if (a.state_out) {
+    if (a.state_out != a.state_in && overlap(a.state_out, st_bytes, a.state_in, st_bytes))
+      return GDR_ERR_INVALID_ARGUMENT;
+    R others[] = {{a.q, qk_bytes}, {a.k, qk_bytes}, {a.v, v_bytes}, {a.g, gb_bytes},
+                  {a.beta, gb_bytes}, {a.cu_seqlens, cu_bytes},
+                  {a.workspace, static_cast<int64_t>(a.workspace_bytes)}};
+    for (const R& r : others)
+      if (overlap(a.state_out, st_bytes, r.p, r.n)) return GDR_ERR_INVALID_ARGUMENT;
+  }
+  return GDR_OK;
+}
+
+gdr_status validate_step(const StepArgs& a) {
+  gdr_status s = common_sizes(a.Nqk, a.Nv, a.D, a.dtype, a.flags);
+  if (s != GDR_OK) return s;
+  if (a.N < 0) return GDR_ERR_INVALID_ARGUMENT;
+  if (static_cast<int64_t>(a.N) * a.Nv > (int64_t(1) << 31) / 4) return GDR_ERR_INVALID_ARGUMENT;
+  if (a.N == 0) return GDR_OK;
+  if (!a.q || !a.k || !a.v || !a.g || !a.beta || !a.state_in || !a.state_out || !a.out)
+    return GDR_ERR_INVALID_ARGUMENT;
+  const void* ptrs[] = {a.q, a.k, a.v, a.g, a.beta, a.state_in, a.state_out, a.out};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return GDR_ERR_INVALID_ARGUMENT;
+  const int64_t es = static_cast<int64_t>(dtype_size(a.dtype));
+  const int64_t qk_bytes = static_cast<int64_t>(a.N) * a.Nqk * 128 * es;
+  const int64_t v_bytes = static_cast<int64_t>(a.N) * a.Nv * 128 * es;
+  const int64_t gb_bytes = static_cast<int64_t>(a.N) * a.Nv * 4;
+  const int64_t st_bytes = static_cast<int64_t>(a.N) * a.Nv * 128 * 128 * 4;
+  struct R { const void* p; int64_t n; } in[] = {
+      {a.q, qk_bytes}, {a.k, qk_bytes}, {a.v, v_bytes}, {a.g, gb_bytes}, {a.beta, gb_bytes},
+      {a.state_in, st_bytes}, {a.state_out, st_bytes}};
+  for (const R& r : in)
+    if (overlap(a.out, v_bytes, r.p, r.n)) return GDR_ERR_INVALID_ARGUMENT;
+  if (a.state_out != a.state_in && overlap(a.state_out, st_bytes, a.state_in, st_bytes))
+    return GDR_ERR_INVALID_ARGUMENT;
+  R others[] = {{a.q, qk_bytes}, {a.k, qk_bytes}, {a.v, v_bytes}, {a.g, gb_bytes}, {a.beta, gb_bytes}};
+  for (const R& r : others)
+    if (overlap(a.state_out, st_bytes, r.p, r.n)) return GDR_ERR_INVALID_ARGUMENT;
+  return GDR_OK;
+}
+
+}  // namespace gdr

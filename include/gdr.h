@@ -1,0 +1,162 @@
+/*
+ * gdr.h -- libgdr: the gated delta rule of Gated DeltaNet on MI355X (gfx950).
+ *
+ * The rule (Qwen3-Next blog post "Code-Qwen3-Next", section 5; Ascend PyPTO
+ * "Qwen3Next" operator page, math formulas).  Per sequence and value head h,
+ * with query/key head j = h / (Nv / Nqk) (grouped heads, blog section 4), a
+ * state S in R^{Dv x Dk} (S[i][c]: i = value index, c = key index) evolves
+ * token by token:
+ *
+ *   kh = k_t / sqrt(|k_t|^2 + 1e-6),   qh = scale * q_t / sqrt(|q_t|^2 + 1e-6)
+ *   S  = exp(g_t) S + beta_t (v_t - exp(g_t) S kh) kh^T
+ *   o_t = S qh
+ *
+ * Two entry points compute it:
+ *   gdr_chunk_fwd      -- prefill: packed variable-length sequences, in the
+ *                         chunkwise form with chunk length 128 (blog post
+ *                         section 5(1); operator page "chunk_gated_delta_rule");
+ *   gdr_recurrent_step -- decode: one token per sequence (blog post 5(2)).
+ *
+ * Conventions shared by all calls:
+ *   - All tensor pointers are DEVICE pointers, caller-owned, contiguous,
+ *     row-major, 16-byte aligned.  The library allocates no memory and keeps
+ *     no pointer after a call returns.
+ *   - Calls only enqueue kernels on `stream` and return; results are valid
+ *     once the caller synchronises that stream.  The library keeps no mutable
+ *     global state, so calls on different streams may run concurrently as long
+ *     as their buffers do not overlap.
+ *   - D (= Dk = Dv) must be 128; Nv must be a multiple of Nqk (operator page,
+ *     parameter constraints).
+ *   - `dtype` is the storage type of q, k, v and out.  g, beta and the states
+ *     are always float32.  Arithmetic accumulates in float32; bf16 inputs are
+ *     multiplied on bf16 matrix cores, f32 inputs on f32 matrix cores.
+ *   - Errors are reported by the returned status; nothing aborts or prints.
+ *     Argument validation happens before any launch, and on a validation
+ *     error no output is touched.  Values that live only on the device
+ *     (cu_seqlens being non-decreasing with cu[N] = T, g <= 0) are the
+ *     caller's contract and are not checked.
+ */
+#ifndef GDR_H
+#define GDR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { GDR_F32 = 0, GDR_BF16 = 1 } gdr_dtype;
+
+typedef enum {
+    GDR_OK = 0,
+    GDR_ERR_INVALID_ARGUMENT = -1,   /* bad size, null pointer, misalignment, ... */
+    GDR_ERR_UNSUPPORTED = -2,        /* D != 128, unknown dtype or flag */
+    GDR_ERR_WORKSPACE_TOO_SMALL = -3,
+    GDR_ERR_HIP = -4                 /* a HIP runtime call or launch failed */
+} gdr_status;
+
+/* Normalise q and k by their L2 norm inside the call (the blog's
+ * use_qk_l2norm_in_kernel).  Without the flag, q and k are used as given
+ * (then scale still multiplies q). */
+#define GDR_FLAG_QK_L2NORM 1u
+
+/* The chunk length of the chunkwise form (operator page: fixed at 128). */
+#define GDR_CHUNK 128
+
+/*
+ * Bytes of device workspace gdr_chunk_fwd needs for these sizes.
+ * Returns 0 for invalid sizes.  The workspace is scratch: its contents on
+ * entry do not matter and are undefined on return.
+ */
+size_t gdr_chunk_fwd_workspace_size(int32_t T, int32_t N, int32_t Nqk, int32_t Nv,
+                                    int32_t D, gdr_dtype dtype);
+
+/*
+ * Chunkwise forward over N packed sequences (prefill).
+ *
+ * q, k       [T, Nqk, D]  dtype
+ * v          [T, Nv, D]   dtype
+ * g, beta    [T, Nv]      float32; g is the natural-log decay (finite, <= 0),
+ *                         beta the write strength
+ * state_in   [N, Nv, D, D] float32 initial states (row = value index), or NULL
+ *                         for zeros
+ * cu_seqlens [N + 1]      int32, device: cu[0] = 0 <= cu[1] <= ... <= cu[N] = T;
+ *                         sequence b owns tokens [cu[b], cu[b+1]).  Chunks of
+ *                         128 tokens restart at every sequence start, so a
+ *                         sequence boundary may fall anywhere.
+ * scale      multiplies the normalised query (the blog uses 1/sqrt(D))
+ * flags      GDR_FLAG_QK_L2NORM or 0
+ * out        [T, Nv, D]   dtype, written for every token; must not alias inputs
+ * state_out  [N, Nv, D, D] float32 final states, or NULL.  May equal state_in
+ *                         (in-place update); must not partially overlap it.
+ * workspace  device scratch of at least gdr_chunk_fwd_workspace_size() bytes,
+ *            256-byte aligned.
+ * stream     hipStream_t (passed as void*; NULL = the default stream)
+ *
+ * A zero-length sequence leaves its state unchanged (state_out = state_in).
+ * T = 0 is allowed.  Requires N >= 1.
+ */
+gdr_status gdr_chunk_fwd(const void* q, const void* k, const void* v,
+                         const float* g, const float* beta,
+                         const float* state_in, const int32_t* cu_seqlens,
+                         int32_t N, int32_t T, int32_t Nqk, int32_t Nv, int32_t D,
+                         gdr_dtype dtype, float scale, uint32_t flags,
+                         void* out, float* state_out,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * One decode step: one token for each of N independent sequences.
+ *
+ * q, k       [N, Nqk, D]  dtype
+ * v          [N, Nv, D]   dtype
+ * g, beta    [N, Nv]      float32
+ * state_in   [N, Nv, D, D] float32 (required)
+ * state_out  [N, Nv, D, D] float32 (required); may equal state_in for an
+ *            in-place update
+ * out        [N, Nv, D]   dtype
+ * Requires N >= 0 (N = 0 does nothing).
+ */
+gdr_status gdr_recurrent_step(const void* q, const void* k, const void* v,
+                              const float* g, const float* beta,
+                              const float* state_in, float* state_out,
+                              int32_t N, int32_t Nqk, int32_t Nv, int32_t D,
+                              gdr_dtype dtype, float scale, uint32_t flags,
+                              void* out, void* stream);
+
+/*
+ * Profiling variant of gdr_chunk_fwd: the same computation, plus the GPU time
+ * of every kernel it launches.  The call creates one HIP event per launch
+ * boundary on `stream`, waits for the last one (so, unlike gdr_chunk_fwd, it
+ * blocks the host until the work is done), and writes, for launch i < *n:
+ *   kernel_ms[i]   elapsed GPU time from the start of launch i to its end;
+ *   kernel_kind[i] which stage it was (GDR_STAGE_*).
+ * max_kernels bounds both arrays; a call needing more launches than that
+ * returns GDR_ERR_INVALID_ARGUMENT before launching anything.  The number of
+ * launches is 2 + 2 * ceil(slots / segment), a handful for every workload.
+ */
+#define GDR_STAGE_TABLE 0   /* chunk table from cu_seqlens */
+#define GDR_STAGE_PREP 1    /* query/key norms, gate cumsum */
+#define GDR_STAGE_INTRA 2   /* intra-chunk products, parallel over chunks */
+#define GDR_STAGE_INTER 3   /* chunk-serial state pass and outputs */
+gdr_status gdr_chunk_fwd_timed(const void* q, const void* k, const void* v,
+                               const float* g, const float* beta,
+                               const float* state_in, const int32_t* cu_seqlens,
+                               int32_t N, int32_t T, int32_t Nqk, int32_t Nv, int32_t D,
+                               gdr_dtype dtype, float scale, uint32_t flags,
+                               void* out, float* state_out,
+                               void* workspace, size_t workspace_bytes, void* stream,
+                               float* kernel_ms, int32_t* kernel_kind, int32_t max_kernels,
+                               int32_t* n);
+
+/* A static, human-readable name for a status code. */
+const char* gdr_status_string(gdr_status s);
+
+/* Library version, for logging: "libgdr <major>.<minor>". */
+const char* gdr_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDR_H */

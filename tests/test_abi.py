@@ -1,0 +1,161 @@
+"""CPU tests of the C ABI: the library loads, exports every declared symbol,
+sizes its workspace, and rejects bad arguments before touching the GPU.
+
+Only validation paths run here: every call below fails validation, which
+happens before any HIP call, so fake (aligned, non-null) addresses are safe.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_deltanet_chunked_amd as gdr
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdr.h")
+
+OK, INVALID, UNSUPPORTED, WS_SMALL = 0, -1, -2, -3
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdr_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("gdr_chunk_fwd", "gdr_recurrent_step", "gdr_chunk_fwd_workspace_size",
+              "gdr_status_string", "gdr_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = gdr.load()
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_version_and_status_strings():
+    lib = gdr.load()
+    assert lib.gdr_version().startswith(b"libgdr")
+    for code in (0, -1, -2, -3, -4):
+        assert lib.gdr_status_string(code)
+    assert lib.gdr_status_string(7) == b"unknown status"
+
+
+def test_workspace_size():
+    ws = lambda *a: gdr.workspace_size(*a)
+    small = ws(512, 1, 2, 4, gdr.GDR_F32)
+    assert small > 0
+    assert ws(4096, 1, 16, 32, gdr.GDR_BF16) > 0
+    # invalid sizes give 0
+    lib = gdr.load()
+    assert lib.gdr_chunk_fwd_workspace_size(512, 1, 2, 4, 64, 0) == 0   # D != 128
+    assert lib.gdr_chunk_fwd_workspace_size(512, 1, 3, 4, 128, 0) == 0  # Nv % Nqk
+    assert lib.gdr_chunk_fwd_workspace_size(512, 0, 2, 4, 128, 0) == 0  # N < 1
+    assert lib.gdr_chunk_fwd_workspace_size(-1, 1, 2, 4, 128, 0) == 0
+    assert lib.gdr_chunk_fwd_workspace_size(512, 1, 2, 4, 128, 5) == 0  # dtype
+    # bounded by the segment buffer: grows slowly with T
+    assert ws(1 << 20, 1, 16, 32, gdr.GDR_BF16) < 2 * ws(1 << 16, 1, 16, 32, gdr.GDR_BF16) + (1 << 30)
+
+
+class FakeBuffers:
+    """Distinct, 256-byte aligned, non-overlapping fake device addresses."""
+
+    def __init__(self, T=256, N=2, Nqk=2, Nv=4, es=2):
+        base = 1 << 40
+        sizes = dict(q=T * Nqk * 128 * es, k=T * Nqk * 128 * es, v=T * Nv * 128 * es,
+                     g=T * Nv * 4, beta=T * Nv * 4, state_in=N * Nv * 128 * 128 * 4,
+                     cu=(N + 1) * 4, out=T * Nv * 128 * es, state_out=N * Nv * 128 * 128 * 4,
+                     ws=gdr.workspace_size(T, N, Nqk, Nv, gdr.GDR_BF16 if es == 2 else gdr.GDR_F32))
+        self.addr = {}
+        for name, n in sizes.items():
+            self.addr[name] = base
+            base += (n + (1 << 20)) & ~255
+        self.sizes = sizes
+        self.T, self.N, self.Nqk, self.Nv = T, N, Nqk, Nv
+
+
+def call_chunk(fb, **over):
+    lib = gdr.load()
+    a = dict(q=fb.addr["q"], k=fb.addr["k"], v=fb.addr["v"], g=fb.addr["g"], beta=fb.addr["beta"],
+             state_in=fb.addr["state_in"], cu=fb.addr["cu"], N=fb.N, T=fb.T, Nqk=fb.Nqk, Nv=fb.Nv,
+             D=128, dtype=gdr.GDR_BF16, scale=0.1, flags=gdr.GDR_FLAG_QK_L2NORM,
+             out=fb.addr["out"], state_out=fb.addr["state_out"], ws=fb.addr["ws"],
+             ws_bytes=fb.sizes["ws"], stream=None)
+    a.update(over)
+    return lib.gdr_chunk_fwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["state_in"], a["cu"],
+                             a["N"], a["T"], a["Nqk"], a["Nv"], a["D"], a["dtype"], a["scale"],
+                             a["flags"], a["out"], a["state_out"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("over,expect", [
+    (dict(D=64), UNSUPPORTED),
+    (dict(dtype=7), UNSUPPORTED),
+    (dict(flags=2), UNSUPPORTED),
+    (dict(Nqk=3), INVALID),            # Nv % Nqk != 0
+    (dict(N=0), INVALID),
+    (dict(T=-1), INVALID),
+    (dict(q=None), INVALID),
+    (dict(out=None), INVALID),
+    (dict(cu=None), INVALID),
+    (dict(ws=None), INVALID),
+    (dict(ws_bytes=1024), WS_SMALL),
+], ids=lambda x: str(x))
+def test_chunk_fwd_rejects(over, expect):
+    fb = FakeBuffers()
+    assert call_chunk(fb, **over) == expect
+
+
+def test_chunk_fwd_rejects_misalignment():
+    fb = FakeBuffers()
+    assert call_chunk(fb, q=fb.addr["q"] + 8) == INVALID
+    assert call_chunk(fb, ws=fb.addr["ws"] + 16) == INVALID   # workspace needs 256 bytes
+
+
+def test_chunk_fwd_rejects_aliasing():
+    fb = FakeBuffers()
+    assert call_chunk(fb, out=fb.addr["v"]) == INVALID
+    assert call_chunk(fb, out=fb.addr["q"] + 256) == INVALID
+    # partial overlap of the two states
+    assert call_chunk(fb, state_out=fb.addr["state_in"] + 4096) == INVALID
+    assert call_chunk(fb, state_out=fb.addr["ws"]) == INVALID
+
+
+def call_step(fb, **over):
+    lib = gdr.load()
+    a = dict(q=fb.addr["q"], k=fb.addr["k"], v=fb.addr["v"], g=fb.addr["g"], beta=fb.addr["beta"],
+             state_in=fb.addr["state_in"], state_out=fb.addr["state_out"], N=fb.N, Nqk=fb.Nqk,
+             Nv=fb.Nv, D=128, dtype=gdr.GDR_BF16, scale=0.1, flags=gdr.GDR_FLAG_QK_L2NORM,
+             out=fb.addr["out"], stream=None)
+    a.update(over)
+    return lib.gdr_recurrent_step(a["q"], a["k"], a["v"], a["g"], a["beta"], a["state_in"],
+                                  a["state_out"], a["N"], a["Nqk"], a["Nv"], a["D"], a["dtype"],
+                                  a["scale"], a["flags"], a["out"], a["stream"])
+
+
+@pytest.mark.parametrize("over,expect", [
+    (dict(D=256), UNSUPPORTED),
+    (dict(dtype=3), UNSUPPORTED),
+    (dict(Nqk=3), INVALID),
+    (dict(N=-1), INVALID),
+    (dict(state_in=None), INVALID),
+    (dict(state_out=None), INVALID),
+    (dict(out=None), INVALID),
+    (dict(k=1 << 40 | 4), INVALID),
+], ids=lambda x: str(x))
+def test_recurrent_step_rejects(over, expect):
+    fb = FakeBuffers(T=2, N=2)
+    assert call_step(fb, **over) == expect
+
+
+def test_recurrent_step_zero_sequences_is_a_no_op():
+    fb = FakeBuffers(T=2, N=2)
+    assert call_step(fb, N=0, q=None, k=None, v=None, state_in=None, state_out=None, out=None) == OK
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    with pytest.raises(RuntimeError):
+        gdr.load(str(tmp_path / "missing.so"))

@@ -1,0 +1,227 @@
+"""GPU parity of libgdr against the fp64 oracle, through the C ABI.
+
+Tolerances (relative L2 over the whole compared tensor): 1e-4 for float32
+inputs, 1e-2 for bfloat16 inputs; outputs and final states are compared
+separately.  Small cases are compared in full; the full-size prefill
+workloads are compared on sampled value heads, which the rule treats
+independently, so the oracle can compute them one by one.
+"""
+import numpy as np
+import pytest
+
+import gated_deltanet_chunked_amd as gdr
+from gated_deltanet_chunked_amd.inputs import config_inputs, make_inputs
+from tests.gpu_util import (SCALE, TOL, device_tensors, oracle_full, oracle_heads, rel_l2,
+                            to_f64)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    gdr.load()
+    yield
+    torch.cuda.synchronize()
+
+
+def _chunk(inp, want_state=True, state="in", l2norm=True):
+    import torch
+    t = device_tensors(inp)
+    s_in = t["state_in"] if state == "in" else None
+    out, st = gdr.chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], t["cu"], s_in,
+                            scale=SCALE, want_state=want_state, l2norm=l2norm)
+    torch.cuda.synchronize()
+    return to_f64(out), (to_f64(st) if st is not None else None)
+
+
+def _assert_close(name, got, ref, tol):
+    err = rel_l2(got, ref)
+    assert np.isfinite(got).all(), f"{name}: non-finite values"
+    assert err <= tol, f"{name}: rel L2 {err:.3e} > {tol:.0e}"
+    return err
+
+
+# ----------------------------------------------------------------- prefill
+
+
+def test_tiny_fp32_config():
+    """B=1, T=512 (4 chunks), Nqk=2, Nv=4, fp32, zero initial state."""
+    inp = config_inputs(0)
+    out, st = _chunk(inp)
+    ro, rs = oracle_full(inp)
+    _assert_close("out", out, ro, TOL["f32"])
+    _assert_close("state", st, rs, TOL["f32"])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("lengths,Nqk,Nv", [
+    ([300, 1, 128, 129, 0, 77, 255], 2, 4),   # ragged tails, empty and one-token sequences
+    ([640], 1, 4),                            # G = 4
+    ([200, 57], 4, 4),                        # G = 1
+    ([128, 256, 384], 2, 2),                  # whole chunks only
+])
+def test_ragged(dtype, lengths, Nqk, Nv):
+    inp = make_inputs(lengths, Nqk, Nv, dtype=dtype, seed=11 + len(lengths), state_std=0.01)
+    out, st = _chunk(inp)
+    ro, rs = oracle_full(inp)
+    _assert_close("out", out, ro, TOL[dtype])
+    _assert_close("state", st, rs, TOL[dtype])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_large_initial_state(dtype):
+    """A state of unit scale (not 0.01) makes the inter-chunk terms dominate."""
+    inp = make_inputs([333, 70], 2, 4, dtype=dtype, seed=21, state_std=1.0)
+    out, st = _chunk(inp)
+    ro, rs = oracle_full(inp)
+    _assert_close("out", out, ro, TOL[dtype])
+    _assert_close("state", st, rs, TOL[dtype])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_slow_decay(dtype):
+    """A ~ U(0, 0.05): gates near 1, the state carries across many chunks."""
+    inp = make_inputs([1000], 1, 2, dtype=dtype, seed=22, state_std=0.5, A_range=(0.0, 0.05))
+    out, st = _chunk(inp)
+    ro, rs = oracle_full(inp)
+    _assert_close("out", out, ro, TOL[dtype])
+    _assert_close("state", st, rs, TOL[dtype])
+
+
+def test_no_initial_state_and_no_final_state():
+    inp = make_inputs([257, 3], 2, 4, dtype="bf16", seed=23, state_std=0.01)
+    out, st = _chunk(inp, want_state=False, state=None)
+    assert st is None
+    ro, _ = oracle_full(inp, state_in=None)
+    _assert_close("out", out, ro, TOL["bf16"])
+
+
+def test_without_l2norm():
+    """Flag off: q, k are used as given (here pre-normalised rows)."""
+    inp = make_inputs([300], 2, 4, dtype="f32", seed=24, state_std=0.01)
+    inp.q = (inp.q / np.linalg.norm(inp.q, axis=-1, keepdims=True)).astype(np.float32)
+    inp.k = (inp.k / np.linalg.norm(inp.k, axis=-1, keepdims=True)).astype(np.float32)
+    out, st = _chunk(inp, l2norm=False)
+    ro, rs = oracle_full(inp, l2norm=False)
+    _assert_close("out", out, ro, TOL["f32"])
+    _assert_close("state", st, rs, TOL["f32"])
+
+
+def test_in_place_state():
+    import torch
+    inp = make_inputs([390, 5], 2, 4, dtype="bf16", seed=25, state_std=0.01)
+    t = device_tensors(inp)
+    s = t["state_in"].clone()
+    out, st = gdr.chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], t["cu"], s, state_out=s,
+                            scale=SCALE)
+    torch.cuda.synchronize()
+    assert st.data_ptr() == s.data_ptr()
+    ro, rs = oracle_full(inp)
+    _assert_close("out", to_f64(out), ro, TOL["bf16"])
+    _assert_close("state", to_f64(s), rs, TOL["bf16"])
+
+
+def test_empty_input():
+    """T = 0: every sequence is empty and its final state is its initial state."""
+    import torch
+    dev = "cuda:0"
+    N, Nqk, Nv = 3, 2, 4
+    q = torch.empty((0, Nqk, 128), dtype=torch.bfloat16, device=dev)
+    v = torch.empty((0, Nv, 128), dtype=torch.bfloat16, device=dev)
+    g = torch.empty((0, Nv), dtype=torch.float32, device=dev)
+    cu = torch.zeros(N + 1, dtype=torch.int32, device=dev)
+    s0 = torch.randn((N, Nv, 128, 128), device=dev)
+    out, st = gdr.chunk_fwd(q, q, v, g, g, cu, s0, scale=SCALE)
+    torch.cuda.synchronize()
+    assert out.shape == (0, Nv, 128)
+    assert torch.equal(st, s0)
+    out, st = gdr.chunk_fwd(q, q, v, g, g, cu, None, scale=SCALE)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(st).item() == 0
+
+
+def test_prefill_config_full():
+    """T=4096, Nqk=16, Nv=32, bf16, initial state N(0, 0.01): every head compared."""
+    inp = config_inputs(1)
+    out, st = _chunk(inp)
+    ro, rs = oracle_full(inp)
+    _assert_close("out", out, ro, TOL["bf16"])
+    _assert_close("state", st, rs, TOL["bf16"])
+
+
+SAMPLED_HEADS = [0, 1, 17, 31]
+
+
+@pytest.mark.parametrize("cfg", [2, 3])
+def test_full_size_sampled_heads(cfg):
+    """Varlen (8 sequences, lengths U[1, 8192]) and long-context (T=32768)
+    workloads at full size, in the same launch as the benchmark; the oracle
+    runs on sampled value heads."""
+    inp = config_inputs(cfg)
+    out, st = _chunk(inp)
+    ref = oracle_heads(inp, SAMPLED_HEADS)
+    cu = inp.cu_seqlens
+    got_o, ref_o, got_s, ref_s = [], [], [], []
+    for (b, h), (o, s) in ref.items():
+        got_o.append(out[cu[b]:cu[b + 1], h])
+        ref_o.append(o)
+        got_s.append(st[b, h])
+        ref_s.append(s)
+    _assert_close("out", np.concatenate(got_o), np.concatenate(ref_o), TOL["bf16"])
+    _assert_close("state", np.stack(got_s), np.stack(ref_s), TOL["bf16"])
+    assert np.isfinite(out).all() and np.isfinite(st).all()
+
+
+# ------------------------------------------------------------------ decode
+
+
+def _step(inp, in_place=True):
+    import torch
+    t = device_tensors(inp)
+    s = t["state_in"].clone()
+    s_out = s if in_place else torch.empty_like(s)
+    out = gdr.recurrent_step(t["q"], t["k"], t["v"], t["g"], t["beta"], s, state_out=s_out,
+                             scale=SCALE)
+    torch.cuda.synchronize()
+    if not in_place:
+        assert torch.equal(s, t["state_in"]), "state_in modified by an out-of-place step"
+    return to_f64(out), to_f64(s_out)
+
+
+@pytest.mark.parametrize("in_place", [True, False])
+def test_decode_config(in_place):
+    """256 sequences x 1 token, Nqk=16, Nv=32, bf16, fp32 states N(0, 0.01)."""
+    inp = config_inputs(4)
+    out, st = _step(inp, in_place)
+    ro, rs = oracle_full(inp)
+    _assert_close("out", out, ro, TOL["bf16"])
+    _assert_close("state", st, rs, TOL["bf16"])
+
+
+def test_decode_fp32_small():
+    inp = make_inputs([1] * 5, 1, 3, dtype="f32", seed=31, state_std=1.0)
+    out, st = _step(inp)
+    ro, rs = oracle_full(inp)
+    _assert_close("out", out, ro, TOL["f32"])
+    _assert_close("state", st, rs, TOL["f32"])
+
+
+def test_chunk_equals_repeated_steps():
+    """The prefill of a sequence equals its tokens fed one by one to the decode step."""
+    import torch
+    inp = make_inputs([150], 2, 4, dtype="f32", seed=32, state_std=0.1)
+    out, st = _chunk(inp)
+    t = device_tensors(inp)
+    s = t["state_in"].clone()
+    outs = []
+    for i in range(inp.T):
+        outs.append(gdr.recurrent_step(t["q"][i:i + 1].contiguous(), t["k"][i:i + 1].contiguous(),
+                                       t["v"][i:i + 1].contiguous(), t["g"][i:i + 1].contiguous(),
+                                       t["beta"][i:i + 1].contiguous(), s, scale=SCALE))
+    torch.cuda.synchronize()
+    steps = to_f64(torch.cat(outs))
+    _assert_close("out", out, steps, 1e-4)
+    _assert_close("state", st, to_f64(s), 1e-4)
