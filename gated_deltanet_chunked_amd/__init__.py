@@ -106,7 +106,7 @@ def workspace_size(T: int, N: int, Nqk: int, Nv: int, dtype_code: int) -> int:
     return int(load().gdr_chunk_fwd_workspace_size(T, N, Nqk, Nv, D, dtype_code))
 
 
-STAGE_NAMES = {0: "table", 1: "prep", 2: "intra", 3: "inter"}
+STAGE_NAMES = {0: "table", 1: "intra", 2: "inter"}
 
 
 def chunk_fwd(q, k, v, g, beta, cu_seqlens, state_in=None, *, scale: Optional[float] = None,

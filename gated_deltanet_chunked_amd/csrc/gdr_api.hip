@@ -34,7 +34,7 @@ struct Recorder {
 
 int32_t launches_needed(const Workspace& w) {
   const int64_t segs = (w.nslots + w.seg_slots - 1) / w.seg_slots;
-  return static_cast<int32_t>(2 + 2 * segs);
+  return static_cast<int32_t>(1 + 2 * segs);
 }
 
 template <typename T>
@@ -43,9 +43,7 @@ gdr_status run_chunk(const ChunkArgs& a, hipStream_t st, Recorder& rec) {
   char* ws = static_cast<char*>(a.workspace);
   int4* table = reinterpret_cast<int4*>(ws + w.table);
   int32_t* choff = reinterpret_cast<int32_t*>(ws + w.choff);
-  float* rq = reinterpret_cast<float*>(ws + w.rq);
-  float* rk = reinterpret_cast<float*>(ws + w.rk);
-  double* gcum = reinterpret_cast<double*>(ws + w.gcum);
+  float* gam = reinterpret_cast<float*>(ws + w.gam);
   T* inter = reinterpret_cast<T*>(ws + w.inter);
   float* carry = a.state_out ? a.state_out : reinterpret_cast<float*>(ws + w.carry);
   const T* q = static_cast<const T*>(a.q);
@@ -57,15 +55,13 @@ gdr_status run_chunk(const ChunkArgs& a, hipStream_t st, Recorder& rec) {
 
   rec.before(GDR_STAGE_TABLE);
   launch_table(a.cu_seqlens, a.N, a.T, nslots, table, choff, st);
-  rec.before(GDR_STAGE_PREP);
-  launch_prep<T>(q, k, a.g, table, nslots, a.T, a.Nqk, a.Nv, a.scale, norm, rq, rk, gcum, st);
   for (int64_t s0 = 0; s0 < w.nslots; s0 += w.seg_slots) {
     const int32_t nseg = static_cast<int32_t>(w.nslots - s0 < w.seg_slots ? w.nslots - s0 : w.seg_slots);
     rec.before(GDR_STAGE_INTRA);
-    launch_intra<T>(q, k, v, a.beta, table, rq, rk, gcum, a.T, a.Nqk, a.Nv,
-                    static_cast<int32_t>(s0), nseg, inter, st);
+    launch_intra<T>(q, k, v, a.g, a.beta, table, a.Nqk, a.Nv, static_cast<int32_t>(s0), nseg,
+                    a.scale, norm, inter, gam, st);
     rec.before(GDR_STAGE_INTER);
-    launch_inter<T>(inter, table, choff, gcum, a.state_in, carry, a.state_out, a.N, a.T, a.Nv,
+    launch_inter<T>(inter, table, choff, gam, a.state_in, carry, a.state_out, a.N, a.Nv,
                     static_cast<int32_t>(s0), nseg, s0 == 0, out, st);
   }
   rec.end();

@@ -46,14 +46,47 @@ __device__ __forceinline__ void get4<__bf16>(const __bf16* p, float* x) {
   x[0] = (float)v[0]; x[1] = (float)v[1]; x[2] = (float)v[2]; x[3] = (float)v[3];
 }
 
+// Operands of one chunk held by one lane: its A fragments of [Mt; Qp], its
+// entries of Bm and Ou, and the chunk's decay exp(gc_last).
+template <typename T>
+struct ChunkOps {
+  static constexpr int KSTEPS = kD / Mma<T>::K;
+  typename Mma<T>::frag a[4][KSTEPS];
+  float bm[2][4], ou[2][4];
+  float gC;
+};
+
+template <typename T>
+__device__ __forceinline__ void load_ops(ChunkOps<T>& o, const T* __restrict__ mats,
+                                         const float* __restrict__ gam, int w, int l, int vcol) {
+  constexpr int KSTEPS = ChunkOps<T>::KSTEPS;
+  const int r16 = l & 15, kq = (l >> 4) * Mma<T>::E;
+  const T* Mt = mats;
+  const T* Qp = mats + kD * kD;
+  const T* Bm = mats + 2 * kD * kD;
+  const T* OuT = mats + 3 * kD * kD;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const T* base = (i < 2 ? Mt : Qp) + (size_t)(32 * w + 16 * (i & 1) + r16) * kD;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) o.a[i][ks] = Mma<T>::load_contig(base + ks * Mma<T>::K + kq);
+  }
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int kr = 32 * w + 16 * t + 4 * (l >> 4);
+    get4<T>(Bm + (size_t)vcol * kD + kr, o.bm[t]);
+    get4<T>(OuT + (size_t)vcol * kD + kr, o.ou[t]);
+  }
+  o.gC = *gam;
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void inter_kernel(
     const T* __restrict__ inter, const int4* __restrict__ table, const int32_t* __restrict__ choff,
-    const double* __restrict__ gcum, const float* state_in, float* carry, float* state_out,
-    int32_t N, int32_t T_, int32_t Nv, int32_t slot0, int32_t nseg, int first_segment,
-    T* __restrict__ out) {
+    const float* __restrict__ gam, const float* state_in, float* carry, float* state_out,
+    int32_t N, int32_t Nv, int32_t slot0, int32_t nseg, int first_segment, T* __restrict__ out) {
   constexpr int LDS_S = kD + 16 / (int)sizeof(T);
-  constexpr int KSTEPS = kD / Mma<T>::K;
+  constexpr int KSTEPS = ChunkOps<T>::KSTEPS;
   __shared__ T sS[2][16 * LDS_S];
 
   // Block -> (sequence b, head h, 16-row block vb).  The 8 row blocks of one
@@ -93,6 +126,8 @@ __global__ __launch_bounds__(256) void inter_kernel(
   if (cb >= ce) return;
   const float* src = (cb == c0) ? state_in : carry;
   float* dstS = (ce == c1) ? state_out : carry;
+  const size_t mstride = (size_t)Nv * 4 * (size_t)(kD * kD);
+  const T* mats0 = inter + (size_t)h * 4 * (size_t)(kD * kD) - (size_t)slot0 * mstride;
 
   // S^T tiles: rows (key index) kr(t, x) = 32 w + 16 t + 4 (l >> 4) + x, column vcol
   float S[2][4];
@@ -105,46 +140,21 @@ __global__ __launch_bounds__(256) void inter_kernel(
 
   const int r16 = l & 15, kq = (l >> 4) * Mma<T>::E;
   int buf = 0;
-#pragma unroll 1
-  for (int c = cb; c < ce; ++c) {
-    const int4 e = table[c];
-    const int start = e.y, len = e.z;
-    const T* mats = inter + ((size_t)(c - slot0) * Nv + h) * 4 * (size_t)(kD * kD);
-    const T* Mt = mats;
-    const T* Qp = mats + kD * kD;
-    const T* Bm = mats + 2 * kD * kD;
-    const T* OuT = mats + 3 * kD * kD;
-
-    // operands of this chunk: A rows of Mt and Qp, Bm and Ou entries
-    typename Mma<T>::frag a[4][KSTEPS];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const T* base = (i < 2 ? Mt : Qp) + (size_t)(32 * w + 16 * (i & 1) + r16) * kD;
-#pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) a[i][ks] = Mma<T>::load_contig(base + ks * Mma<T>::K + kq);
-    }
-    float bm[2][4], ou[2][4];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int kr = 32 * w + 16 * t + 4 * (l >> 4);
-      get4<T>(Bm + (size_t)vcol * kD + kr, bm[t]);
-      get4<T>(OuT + (size_t)vcol * kD + kr, ou[t]);
-    }
-    const float gC = expf((float)gcum[(size_t)h * T_ + start + len - 1]);
-
+  // One chunk of the state pass with its operands already in registers.
+  auto step = [&](const ChunkOps<T>& o, int c) {
     // S (this block's 16 rows) as the B operand, [v][k] in LDS
 #pragma unroll
     for (int t = 0; t < 2; ++t) put4<T>(&sS[buf][r16 * LDS_S + 32 * w + 16 * t + 4 * (l >> 4)], S[t]);
     __syncthreads();
-
     f32x4 acc[4] = {zero4(), zero4(), zero4(), zero4()};
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
       const auto bfr = Mma<T>::load_contig(&sS[buf][r16 * LDS_S + ks * Mma<T>::K + kq]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] = Mma<T>::mma(a[i][ks], bfr, acc[i]);
+      for (int i = 0; i < 4; ++i) acc[i] = Mma<T>::mma(o.a[i][ks], bfr, acc[i]);
     }
-
+    const int4 e = table[c];
+    const int start = e.y, len = e.z;
     // outputs of this chunk (from the state at its start)
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -152,14 +162,27 @@ __global__ __launch_bounds__(256) void inter_kernel(
 #pragma unroll
       for (int x = 0; x < 4; ++x)
         if (r + x < len)
-          out[((size_t)(start + r + x) * Nv + h) * kD + vcol] = from_f32<T>(acc[2 + t][x] + ou[t][x]);
+          out[((size_t)(start + r + x) * Nv + h) * kD + vcol] = from_f32<T>(acc[2 + t][x] + o.ou[t][x]);
     }
     // state update
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int x = 0; x < 4; ++x) S[t][x] = gC * S[t][x] + acc[t][x] + bm[t][x];
+      for (int x = 0; x < 4; ++x) S[t][x] = o.gC * S[t][x] + acc[t][x] + o.bm[t][x];
     buf ^= 1;
+  };
+
+  // Two register sets: the operands of the next chunk are in flight while
+  // the current one is computed (they do not depend on the state).
+  ChunkOps<T> A, B;
+  load_ops<T>(A, mats0 + (size_t)cb * mstride, gam + (size_t)cb * Nv + h, w, l, vcol);
+#pragma unroll 1
+  for (int c = cb; c < ce; c += 2) {
+    if (c + 1 < ce) load_ops<T>(B, mats0 + (size_t)(c + 1) * mstride, gam + (size_t)(c + 1) * Nv + h, w, l, vcol);
+    step(A, c);
+    if (c + 1 >= ce) break;
+    if (c + 2 < ce) load_ops<T>(A, mats0 + (size_t)(c + 2) * mstride, gam + (size_t)(c + 2) * Nv + h, w, l, vcol);
+    step(B, c + 1);
   }
 
   if (dstS) {
@@ -169,20 +192,19 @@ __global__ __launch_bounds__(256) void inter_kernel(
 }
 
 template <typename T>
-void launch_inter(const T* inter, const int4* table, const int32_t* choff, const double* gcum,
-                  const float* state_in, float* carry, float* state_out, int32_t N, int32_t T_,
-                  int32_t Nv, int32_t slot0, int32_t nseg, bool first_segment, T* out,
-                  hipStream_t stream) {
+void launch_inter(const T* inter, const int4* table, const int32_t* choff, const float* gam,
+                  const float* state_in, float* carry, float* state_out, int32_t N, int32_t Nv,
+                  int32_t slot0, int32_t nseg, bool first_segment, T* out, hipStream_t stream) {
   const unsigned blocks = (unsigned)N * (unsigned)Nv * 8u;
-  hipLaunchKernelGGL(inter_kernel<T>, dim3(blocks), dim3(256), 0, stream, inter, table, choff, gcum,
-                     state_in, carry, state_out, N, T_, Nv, slot0, nseg, first_segment ? 1 : 0, out);
+  hipLaunchKernelGGL(inter_kernel<T>, dim3(blocks), dim3(256), 0, stream, inter, table, choff, gam,
+                     state_in, carry, state_out, N, Nv, slot0, nseg, first_segment ? 1 : 0, out);
 }
 
-template void launch_inter<float>(const float*, const int4*, const int32_t*, const double*,
+template void launch_inter<float>(const float*, const int4*, const int32_t*, const float*,
                                   const float*, float*, float*, int32_t, int32_t, int32_t, int32_t,
-                                  int32_t, bool, float*, hipStream_t);
-template void launch_inter<__bf16>(const __bf16*, const int4*, const int32_t*, const double*,
+                                  bool, float*, hipStream_t);
+template void launch_inter<__bf16>(const __bf16*, const int4*, const int32_t*, const float*,
                                    const float*, float*, float*, int32_t, int32_t, int32_t, int32_t,
-                                   int32_t, bool, __bf16*, hipStream_t);
+                                   bool, __bf16*, hipStream_t);
 
 }  // namespace gdr

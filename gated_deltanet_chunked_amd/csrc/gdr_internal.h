@@ -32,9 +32,7 @@ constexpr int64_t kMatElems = 128 * 128;
 struct Workspace {
   int64_t table;      // int32 [nslots][4]: {sequence, first token, length, 0}; sequence -1 = unused
   int64_t choff;      // int32 [N + 1]: first slot of each sequence
-  int64_t rq;         // float [Nqk][T]: scale / |q|
-  int64_t rk;         // float [Nqk][T]: 1 / |k|
-  int64_t gcum;       // double [Nv][T]: chunk-local cumulative sum of g
+  int64_t gam;        // float [nslots][Nv]: exp(sum of g over the chunk)
   int64_t inter;      // [seg_slots][Nv][4][128][128] of the matrix-core operand type
   int64_t carry;      // float [N][Nv][128][128]: state between segments
   int64_t total;

@@ -27,9 +27,12 @@
 // The kernel inverts I + A+^T (upper triangular), whose inverse is T^T, the
 // operand every later product needs.
 //
-// Norms come from the prep kernel as reciprocal row scalings: K = diag(rk) k,
-// Q = diag(rq) q with rq including scale; raw bf16/fp32 inputs feed the
-// matrix cores exactly and the scalings are applied in fp32.
+// The kernel also does the per-row preparation: the L2 norms of the staged
+// key and query rows, kept as reciprocal row scalings (K = diag(rk) k,
+// Q = diag(rq) q with rq including scale), so raw bf16/fp32 inputs feed the
+// matrix cores exactly and the scalings are applied in fp32; and the
+// chunk-local gate cumsum, in fp64 because exp() is taken of differences of
+// it.  exp(gc_last) of every (chunk, head) goes to gam_out for the state pass.
 #include "gdr_device.h"
 #include "gdr_kernels.h"
 
@@ -228,9 +231,9 @@ __device__ __forceinline__ void invert_unit_upper(IntraLds<T>& s) {
 template <typename T>
 __global__ __launch_bounds__(256) void intra_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-    const float* __restrict__ beta, const int4* __restrict__ table, const float* __restrict__ rq,
-    const float* __restrict__ rk, const double* __restrict__ gcum, int32_t T_, int32_t Nqk,
-    int32_t Nv, int32_t slot0, T* __restrict__ inter) {
+    const float* __restrict__ g, const float* __restrict__ beta, const int4* __restrict__ table,
+    int32_t Nqk, int32_t Nv, int32_t slot0, float scale, int norm, T* __restrict__ inter,
+    float* __restrict__ gam_out) {
   constexpr int LD = IntraLds<T>::LD;
   __shared__ IntraLds<T> s;
   const int local_slot = blockIdx.x, h = blockIdx.y;
@@ -246,27 +249,64 @@ __global__ __launch_bounds__(256) void intra_kernel(
   const T* vc = v + ((size_t)start * Nv + h) * kD;
   T* dst = inter + ((size_t)local_slot * Nv + h) * 4 * (size_t)(kD * kD);
 
-  // per-row scalars; padded rows (r >= len) act as zero rows with g = 0
-  if (tid < 128) {
-    const int r = tid;
-    const double glast = gcum[(size_t)h * T_ + start + len - 1];
-    const bool ok = r < len;
-    const double gc = ok ? gcum[(size_t)h * T_ + start + r] : glast;
-    const float bt = ok ? beta[(size_t)(start + r) * Nv + h] : 0.0f;
-    const float rkr = ok ? rk[(size_t)j * T_ + start + r] : 0.0f;
-    const float rqr = ok ? rq[(size_t)j * T_ + start + r] : 0.0f;
-    const float gam = expf((float)gc);
-    s.gc[r] = gc;
-    s.beta[r] = bt;
-    s.rk[r] = rkr;
-    s.rq[r] = rqr;
-    s.ck[r] = expf((float)(glast - gc)) * rkr;
-    s.xk[r] = bt * gam * rkr;
-    s.qs[r] = gam * rqr;
-  }
   stage_rows<T, LD>(s.b, kc, qk_stride, len);
   stage_rows<T, LD>(s.a, qc, qk_stride, len);
+
+  // Chunk-local inclusive cumsum of g in fp64 (blog post section 5(1)c),
+  // rows r < 128 on waves 0 and 1.  Padded rows (r >= len) carry g = 0, so
+  // their cumsum equals the chunk total and they act as empty rows.
+  double gsum = 0.0;
+  float bt = 0.0f;
+  if (tid < 128) {
+    const bool ok = tid < len;
+    gsum = ok ? (double)g[(size_t)(start + tid) * Nv + h] : 0.0;
+    bt = ok ? beta[(size_t)(start + tid) * Nv + h] : 0.0f;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const double y = __shfl_up(gsum, off, 64);
+      if (l >= off) gsum += y;
+    }
+    if (tid == 63) s.gc[0] = gsum;   // wave 0's total, read by wave 1 below
+  }
   __syncthreads();
+
+  // L2 norms of the staged key and query rows (Ascend operator page,
+  // x / sqrt(sum x^2 + eps), eps = 1e-6), two threads per row.
+  {
+    const int r = tid >> 1, half = tid & 1;
+    float sk = 0.0f, sq = 0.0f;
+#pragma unroll 8
+    for (int c = 64 * half; c < 64 * half + 64; ++c) {
+      const float xk = to_f32(s.b[r * LD + c]), xq = to_f32(s.a[r * LD + c]);
+      sk += xk * xk;
+      sq += xq * xq;
+    }
+    sk += __shfl_xor(sk, 1, 64);
+    sq += __shfl_xor(sq, 1, 64);
+    if (half == 0) {
+      const bool ok = r < len;
+      s.rk[r] = ok ? (norm ? 1.0f / sqrtf(sk + 1e-6f) : 1.0f) : 0.0f;
+      s.rq[r] = ok ? (norm ? scale / sqrtf(sq + 1e-6f) : scale) : 0.0f;
+    }
+  }
+  const double wave0_total = s.gc[0];
+  __syncthreads();
+  if (tid < 128) {
+    if (w == 1) gsum += wave0_total;
+    s.gc[tid] = gsum;
+    s.beta[tid] = bt;
+  }
+  __syncthreads();
+  if (tid < 128) {
+    const int r = tid;
+    const double glast = s.gc[127];
+    const double gc = s.gc[r];
+    const float gm = __expf((float)gc);
+    s.ck[r] = __expf((float)(glast - gc)) * s.rk[r];
+    s.xk[r] = s.beta[r] * gm * s.rk[r];
+    s.qs[r] = gm * s.rq[r];
+    if (r == 0) gam_out[(size_t)(slot0 + local_slot) * Nv + h] = __expf((float)glast);
+  }
 
   // Grams on raw inputs: KK[a][c] = k_a.k_c and C2[i][r] = k_i.q_r
   f32x4 acc1[4][4], acc2[4][4];
@@ -293,10 +333,10 @@ __global__ __launch_bounds__(256) void intra_kernel(
         const int a = row + x;   // acc1: (a, c = col);  acc2: (i = a, r = col)
         nv[x] = 0.0f;
         if (col < a)
-          nv[x] = s.beta[a] * s.rk[a] * s.rk[col] * expf((float)(s.gc[a] - s.gc[col])) * acc1[i][jj][x];
+          nv[x] = s.beta[a] * s.rk[a] * s.rk[col] * __expf((float)(s.gc[a] - s.gc[col])) * acc1[i][jj][x];
         pv[x] = 0.0f;
         if (a <= col)
-          pv[x] = s.rq[col] * s.rk[a] * expf((float)(s.gc[col] - s.gc[a])) * acc2[i][jj][x];
+          pv[x] = s.rq[col] * s.rk[a] * __expf((float)(s.gc[col] - s.gc[a])) * acc2[i][jj][x];
       }
       store4<T>(s.a + col * LD + row, nv[0], nv[1], nv[2], nv[3]);
       store4<T>(s.b + col * LD + row, pv[0], pv[1], pv[2], pv[3]);
@@ -383,22 +423,19 @@ __global__ __launch_bounds__(256) void intra_kernel(
 }
 
 template <typename T>
-hipError_t launch_intra(const T* q, const T* k, const T* v, const float* beta, const int4* table,
-                        const float* rq, const float* rk, const double* gcum, int32_t T_,
-                        int32_t Nqk, int32_t Nv, int32_t slot0, int32_t nseg, T* inter,
-                        hipStream_t stream) {
-  hipLaunchKernelGGL(intra_kernel<T>, dim3(nseg, Nv), dim3(256), 0, stream, q, k, v, beta, table,
-                     rq, rk, gcum, T_, Nqk, Nv, slot0, inter);
+hipError_t launch_intra(const T* q, const T* k, const T* v, const float* g, const float* beta,
+                        const int4* table, int32_t Nqk, int32_t Nv, int32_t slot0, int32_t nseg,
+                        float scale, int norm, T* inter, float* gam, hipStream_t stream) {
+  hipLaunchKernelGGL(intra_kernel<T>, dim3(nseg, Nv), dim3(256), 0, stream, q, k, v, g, beta, table,
+                     Nqk, Nv, slot0, scale, norm, inter, gam);
   return hipGetLastError();
 }
 
 template hipError_t launch_intra<float>(const float*, const float*, const float*, const float*,
-                                        const int4*, const float*, const float*, const double*,
-                                        int32_t, int32_t, int32_t, int32_t, int32_t, float*,
-                                        hipStream_t);
+                                        const float*, const int4*, int32_t, int32_t, int32_t,
+                                        int32_t, float, int, float*, float*, hipStream_t);
 template hipError_t launch_intra<__bf16>(const __bf16*, const __bf16*, const __bf16*, const float*,
-                                         const int4*, const float*, const float*, const double*,
-                                         int32_t, int32_t, int32_t, int32_t, int32_t, __bf16*,
-                                         hipStream_t);
+                                         const float*, const int4*, int32_t, int32_t, int32_t,
+                                         int32_t, float, int, __bf16*, float*, hipStream_t);
 
 }  // namespace gdr

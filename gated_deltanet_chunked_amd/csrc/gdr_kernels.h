@@ -9,24 +9,18 @@ namespace gdr {
 void launch_table(const int32_t* cu, int32_t N, int32_t T, int32_t nslots, int4* table,
                   int32_t* choff, hipStream_t stream);
 
+// Intra-chunk products for chunk slots [slot0, slot0 + nseg) of every value head;
+// also writes exp(total gate of the chunk) to gam[slot][head].
 template <typename Tin>
-void launch_prep(const Tin* q, const Tin* k, const float* g, const int4* table, int32_t nslots,
-                 int32_t T, int32_t Nqk, int32_t Nv, float scale, int norm, float* rq, float* rk,
-                 double* gcum, hipStream_t stream);
-
-// Intra-chunk products for chunk slots [slot0, slot0 + nseg) of every value head.
-template <typename Tin>
-hipError_t launch_intra(const Tin* q, const Tin* k, const Tin* v, const float* beta,
-                        const int4* table, const float* rq, const float* rk, const double* gcum,
-                        int32_t T, int32_t Nqk, int32_t Nv, int32_t slot0, int32_t nseg,
-                        Tin* inter, hipStream_t stream);
+hipError_t launch_intra(const Tin* q, const Tin* k, const Tin* v, const float* g, const float* beta,
+                        const int4* table, int32_t Nqk, int32_t Nv, int32_t slot0, int32_t nseg,
+                        float scale, int norm, Tin* inter, float* gam, hipStream_t stream);
 
 // Chunk-serial state pass over chunk slots [slot0, slot0 + nseg).
 template <typename Tin>
-void launch_inter(const Tin* inter, const int4* table, const int32_t* choff, const double* gcum,
-                  const float* state_in, float* carry, float* state_out, int32_t N, int32_t T,
-                  int32_t Nv, int32_t slot0, int32_t nseg, bool first_segment, Tin* out,
-                  hipStream_t stream);
+void launch_inter(const Tin* inter, const int4* table, const int32_t* choff, const float* gam,
+                  const float* state_in, float* carry, float* state_out, int32_t N, int32_t Nv,
+                  int32_t slot0, int32_t nseg, bool first_segment, Tin* out, hipStream_t stream);
 
 template <typename Tin>
 void launch_decode(const Tin* q, const Tin* k, const Tin* v, const float* g, const float* beta,

@@ -37,9 +37,7 @@ Workspace plan_workspace(int64_t T, int64_t N, int64_t Nqk, int64_t Nv, gdr_dtyp
   int64_t off = 0;
   w.table = off; off = align256(off + w.nslots * 4 * 4);
   w.choff = off; off = align256(off + (N + 1) * 4);
-  w.rq = off; off = align256(off + Nqk * T * 4);
-  w.rk = off; off = align256(off + Nqk * T * 4);
-  w.gcum = off; off = align256(off + Nv * T * 8);
+  w.gam = off; off = align256(off + w.nslots * Nv * 4);
   w.inter = off;
   off = align256(off + w.seg_slots * Nv * kInterMats * kMatElems * static_cast<int64_t>(dtype_size(dtype)));
   w.carry = off; off = align256(off + N * Nv * kMatElems * 4);

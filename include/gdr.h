@@ -133,12 +133,11 @@ gdr_status gdr_recurrent_step(const void* q, const void* k, const void* v,
  *   kernel_kind[i] which stage it was (GDR_STAGE_*).
  * max_kernels bounds both arrays; a call needing more launches than that
  * returns GDR_ERR_INVALID_ARGUMENT before launching anything.  The number of
- * launches is 2 + 2 * ceil(slots / segment), a handful for every workload.
+ * launches is 1 + 2 * ceil(slots / segment), a handful for every workload.
  */
 #define GDR_STAGE_TABLE 0   /* chunk table from cu_seqlens */
-#define GDR_STAGE_PREP 1    /* query/key norms, gate cumsum */
-#define GDR_STAGE_INTRA 2   /* intra-chunk products, parallel over chunks */
-#define GDR_STAGE_INTER 3   /* chunk-serial state pass and outputs */
+#define GDR_STAGE_INTRA 1   /* norms, gate cumsum, intra-chunk products; parallel over chunks */
+#define GDR_STAGE_INTER 2   /* chunk-serial state pass and outputs */
 gdr_status gdr_chunk_fwd_timed(const void* q, const void* k, const void* v,
                                const float* g, const float* beta,
                                const float* state_in, const int32_t* cu_seqlens,
