@@ -61,6 +61,10 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", choices=["prefill", "long", "varlen"], default="prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="before the steps, copy a buffer of this many MiB device to device once; "
+                         "a profiler's byte counters on that plain copy calibrate the ones on the "
+                         "kernels")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the gated delta rule shards over sequences and "
@@ -109,6 +113,12 @@ def main() -> int:
 
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
+    if args.copy_probe_mib > 0:
+        src = torch.ones(args.copy_probe_mib << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         step([])
     torch.cuda.synchronize()
