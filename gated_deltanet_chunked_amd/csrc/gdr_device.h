@@ -11,6 +11,8 @@ namespace gdr {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 
 constexpr int kD = 128;      // head dimension (Dk = Dv)
 constexpr int kL = 128;      // chunk length
@@ -121,6 +123,79 @@ __device__ __forceinline__ void mma_block64(f32x4 (&acc)[4][4], const Operand<T,
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = Mma<T>::mma(a[i], b[j], acc[i][j]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Swizzled LDS tiles.  A tile holds rows of W elements of T (W = 128 or 64)
+// with no padding; the 16-byte chunks of row r are permuted by XOR with the
+// low bits of r.  A matrix-core fragment read (16 lanes reading 16
+// consecutive rows at the same 16-byte column chunk) and a row-wise 16-byte
+// store then both touch every LDS bank once.
+// ---------------------------------------------------------------------------
+template <typename T, int W = 128>
+struct Sw {
+  static constexpr int EPC = 16 / (int)sizeof(T);     // elements per 16-byte chunk
+  static constexpr int CPR = W / EPC;                 // chunks per row
+  static constexpr int MASK = CPR < 16 ? CPR - 1 : 15;
+  static __device__ __forceinline__ int at(int r, int c) {
+    const unsigned ur = (unsigned)r, uc = (unsigned)c;
+    return (int)(ur * W + (((uc / EPC) ^ (ur & MASK)) * EPC) + (uc % EPC));
+  }
+};
+
+// Fragment of a swizzled tile at (row, k); k is a multiple of the fragment's
+// element count, so the E elements are contiguous.
+template <typename T, int W = 128>
+__device__ __forceinline__ typename Mma<T>::frag sw_frag(const T* tile, int row, int k) {
+  return Mma<T>::load_contig(tile + Sw<T, W>::at(row, k));
+}
+
+// acc[i][j] += sum_k A(m0 + 16 i + ., k) B(n0 + 16 j + ., k), k in [0, 128),
+// both operands swizzled 128-wide LDS tiles holding rows with k along the row.
+template <typename T>
+__device__ __forceinline__ void sw_gemm64(f32x4 (&acc)[4][4], const T* A, const T* B, int m0, int n0) {
+  const int l = lane_id();
+  const int r = l & 15;
+  const int kq = (l >> 4) * Mma<T>::E;
+#pragma unroll 2
+  for (int k = 0; k < kD; k += Mma<T>::K) {
+    typename Mma<T>::frag a[4], b[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = sw_frag<T>(A, m0 + 16 * i + r, k + kq);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b[j] = sw_frag<T>(B, n0 + 16 * j + r, k + kq);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = Mma<T>::mma(a[i], b[j], acc[i][j]);
+  }
+}
+
+// Two products sharing the A operand: acc1 += A B1^T, acc2 += A B2^T.
+template <typename T>
+__device__ __forceinline__ void sw_gemm64x2(f32x4 (&acc1)[4][4], f32x4 (&acc2)[4][4], const T* A,
+                                            const T* B1, const T* B2, int m0, int n0) {
+  const int l = lane_id();
+  const int r = l & 15;
+  const int kq = (l >> 4) * Mma<T>::E;
+#pragma unroll 1
+  for (int k = 0; k < kD; k += Mma<T>::K) {
+    typename Mma<T>::frag a[4], b[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = sw_frag<T>(A, m0 + 16 * i + r, k + kq);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b[j] = sw_frag<T>(B1, n0 + 16 * j + r, k + kq);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc1[i][j] = Mma<T>::mma(a[i], b[j], acc1[i][j]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b[j] = sw_frag<T>(B2, n0 + 16 * j + r, k + kq);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc2[i][j] = Mma<T>::mma(a[i], b[j], acc2[i][j]);
   }
 }
 

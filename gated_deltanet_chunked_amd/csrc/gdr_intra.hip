@@ -20,19 +20,31 @@
 //   OuT  = (P U)^T = (R diag(beta) V)^T                         [Dv x l]
 // leaving the chunk-serial pass (gdr_inter.hip) with
 //   O = Qp S^T + Ou,   S_next = exp(gc_last) S + S M' + Bm.
+//
+// Data flow.  Every product is C = A B^T with both operands read as rows of
+// a swizzled LDS tile (k along the row), and every result leaves the
+// accumulators transposed (C^T rows are contiguous in a lane), so no operand
+// is ever read with a stride.  Two 128x128 LDS slots carry the whole chain:
+//   K, Q      -> Grams KK^T (symmetric) and KQ^T, sharing the K fragments
+//   N = A+^T  -> slot 0; P stays in registers; slot 1 holds the lower
+//                triangular inverse as it is built
+//   T^T       -> slot 0 (blocked inverse, below);  P -> slot 1
+//   R^T = T^T P^T;  Z = (T^T diag ck) K^T with K^T staged into slot 1
+//   Qp, Mt from K^T and (R, Z^T) scaled by beta exp(gc);  Ou, Bm from V^T
 // The triangular inverse follows the blog's subsection d in blocked form:
 // 16x16 diagonal blocks by substitution, then three doubling merges
 // [X Y; 0 Z]^-1 = [X^-1, -X^-1 Y Z^-1; 0, Z^-1] on the matrix cores (the
 // Ascend operator page's inverse sub-kernels use the same doubling idea).
-// The kernel inverts I + A+^T (upper triangular), whose inverse is T^T, the
-// operand every later product needs.
+// It inverts I + A+^T (upper triangular), whose inverse T^T is the operand
+// every later product needs, and keeps the transpose (lower form) of each
+// finished block beside it so that Z^-1 can also be read by rows.
 //
-// The kernel also does the per-row preparation: the L2 norms of the staged
-// key and query rows, kept as reciprocal row scalings (K = diag(rk) k,
-// Q = diag(rq) q with rq including scale), so raw bf16/fp32 inputs feed the
-// matrix cores exactly and the scalings are applied in fp32; and the
-// chunk-local gate cumsum, in fp64 because exp() is taken of differences of
-// it.  exp(gc_last) of every (chunk, head) goes to gam_out for the state pass.
+// The kernel also does the per-row preparation: the L2 norms of the key and
+// query rows, kept as reciprocal row scalings (K = diag(rk) k, Q = diag(rq) q
+// with rq including scale), so raw bf16/fp32 inputs feed the matrix cores
+// exactly and the scalings are applied in fp32; and the chunk-local gate
+// cumsum, in fp64 because exp() is taken of differences of it.  exp(gc_last)
+// of every (chunk, head) goes to gam_out for the state pass.
 #include "gdr_device.h"
 #include "gdr_kernels.h"
 
@@ -40,16 +52,15 @@ namespace gdr {
 
 template <typename T>
 struct IntraLds {
-  static constexpr int LD = kD + 16 / (int)sizeof(T);   // padded row stride (elements)
-  static constexpr int LDW = 64 + 16 / (int)sizeof(T);
-  T a[128 * LD];
-  T b[128 * LD];
-  T w[64 * LDW];
-  double gc[128];
+  T t0[kD * kD];      // slot 0
+  T t1[kD * kD];      // slot 1
+  T w[64 * 64];       // inverse scratch (a 64-wide swizzled tile)
+  double gc[128];     // chunk-local inclusive cumsum of g
   float beta[128], rk[128], rq[128];
-  float ck[128];   // exp(gc_last - gc_i) * rk_i
-  float xk[128];   // beta_i exp(gc_i) rk_i
-  float qs[128];   // exp(gc_i) rq_i
+  float ck[128];      // exp(gc_last - gc_i) rk_i
+  float xk[128];      // beta_i exp(gc_i) rk_i
+  float qs[128];      // exp(gc_i) rq_i
+  double part;        // wave 0's cumsum total
 };
 
 // 4-element vector store of fp32 values converted to T.
@@ -79,88 +90,155 @@ __device__ __forceinline__ void load4<__bf16>(const __bf16* p, float& x0, float&
   x0 = (float)v[0]; x1 = (float)v[1]; x2 = (float)v[2]; x3 = (float)v[3];
 }
 
-// Copy rows [0, len) of a 128-wide global matrix (row stride gstride
-// elements) into LDS rows of stride LD; rows [len, 128) are zeroed.
-template <typename T, int LD>
-__device__ __forceinline__ void stage_rows(T* dst, const T* src, size_t gstride, int len) {
-  constexpr int VE = 16 / sizeof(T);            // elements per 16-byte vector
-  constexpr int VPR = kD / VE;                  // vectors per row
-  typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
-  for (int idx = threadIdx.x; idx < 128 * VPR; idx += 256) {
-    const int r = idx / VPR, c = (idx % VPR) * VE;
-    u32x4 val = {0u, 0u, 0u, 0u};
-    if (r < len) val = *reinterpret_cast<const u32x4*>(src + (size_t)r * gstride + c);
-    *reinterpret_cast<u32x4*>(dst + r * LD + c) = val;
+// Accumulator values kept between products in the storage type (4 per tile).
+template <typename T> struct Pack4;
+template <> struct Pack4<__bf16> {
+  bf16x4 v;
+  __device__ __forceinline__ void set(const f32x4& a) {
+    v[0] = (__bf16)a[0]; v[1] = (__bf16)a[1]; v[2] = (__bf16)a[2]; v[3] = (__bf16)a[3];
   }
-}
+  __device__ __forceinline__ float get(int x) const { return (float)v[x]; }
+};
+template <> struct Pack4<float> {
+  f32x4 v;
+  __device__ __forceinline__ void set(const f32x4& a) { v = a; }
+  __device__ __forceinline__ float get(int x) const { return v[x]; }
+};
 
-// dst[c][r] = src[r][c] for rows r < len of a 128-wide global matrix; the
-// columns r >= len of dst are zeroed.
-template <typename T, int LD>
-__device__ __forceinline__ void stage_transposed(T* dst, const T* src, size_t gstride, int len) {
-  constexpr int VE = 16 / sizeof(T);
-  constexpr int VPR = kD / VE;
-  for (int idx = threadIdx.x; idx < 128 * VPR; idx += 256) {
-    const int r = idx / VPR, c = (idx % VPR) * VE;
-    T val[VE];
-    if (r < len) {
-      typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
-      const u32x4 raw = *reinterpret_cast<const u32x4*>(src + (size_t)r * gstride + c);
-      const T* pv = reinterpret_cast<const T*>(&raw);
-#pragma unroll
-      for (int e = 0; e < VE; ++e) val[e] = pv[e];
-    } else {
-#pragma unroll
-      for (int e = 0; e < VE; ++e) val[e] = from_f32<T>(0.0f);
-    }
-#pragma unroll
-    for (int e = 0; e < VE; ++e) dst[(c + e) * LD + r] = val[e];
-  }
-}
-
-// Writes a wave's 64x64 accumulator block transposed into LDS:
-// dst[col][row..row+3] = f(row + x, col) * acc, i.e. dst = (acc-matrix)^T,
-// each element multiplied by scale[row + x] (or 1 when scale == nullptr).
-template <typename T, int LD>
-__device__ __forceinline__ void put_transposed(T* dst, const f32x4 (&acc)[4][4], int m0, int n0,
-                                               const float* scale) {
-  const int l = lane_id();
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row = m0 + 16 * i + 4 * (l >> 4);
-      const int col = n0 + 16 * j + (l & 15);
-      float s0 = 1.f, s1 = 1.f, s2 = 1.f, s3 = 1.f;
-      if (scale) { s0 = scale[row]; s1 = scale[row + 1]; s2 = scale[row + 2]; s3 = scale[row + 3]; }
-      store4<T>(dst + col * LD + row, acc[i][j][0] * s0, acc[i][j][1] * s1, acc[i][j][2] * s2,
-                acc[i][j][3] * s3);
-    }
-}
-
-// Same, to a global 128x128 row-major matrix, values negated when neg.
+// Natural staging: rows [0, len) of a 128-wide global matrix (row stride gs
+// elements) into registers, 16 bytes per piece; rows >= len read as zero.
 template <typename T>
-__device__ __forceinline__ void store_transposed_global(T* dst, const f32x4 (&acc)[4][4], int m0,
-                                                        int n0, float sign) {
-  const int l = lane_id();
+struct RowPieces {
+  static constexpr int EPC = 16 / (int)sizeof(T);
+  static constexpr int CPR = kD / EPC;              // pieces per row
+  static constexpr int N = kD * CPR / 256;          // pieces per thread
+  u32x4 p[N];
+  __device__ __forceinline__ void load(const T* src, size_t gs, int len) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row = m0 + 16 * i + 4 * (l >> 4);
-      const int col = n0 + 16 * j + (l & 15);
-      store4<T>(dst + col * kD + row, sign * acc[i][j][0], sign * acc[i][j][1],
-                sign * acc[i][j][2], sign * acc[i][j][3]);
+    for (int it = 0; it < N; ++it) {
+      const int idx = threadIdx.x + 256 * it;
+      const int r = idx / CPR, c = (idx % CPR) * EPC;
+      p[it] = u32x4{0u, 0u, 0u, 0u};
+      if (r < len) p[it] = *reinterpret_cast<const u32x4*>(src + (size_t)r * gs + c);
     }
+  }
+  __device__ __forceinline__ void store(T* tile) const {
+#pragma unroll
+    for (int it = 0; it < N; ++it) {
+      const int idx = threadIdx.x + 256 * it;
+      const int r = idx / CPR, c = (idx % CPR) * EPC;
+      *reinterpret_cast<u32x4*>(tile + Sw<T>::at(r, c)) = p[it];
+    }
+  }
+  // sum of squares of the piece's elements
+  __device__ __forceinline__ float sumsq(int it) const {
+    const T* e = reinterpret_cast<const T*>(&p[it]);
+    float s = 0.0f;
+#pragma unroll
+    for (int x = 0; x < EPC; ++x) { const float f = to_f32(e[x]); s += f * f; }
+    return s;
+  }
+};
+
+// Sum over aligned groups of CPR lanes (CPR = 16 or 32).
+template <int CPR>
+__device__ __forceinline__ float row_sum(float x) {
+#pragma unroll
+  for (int off = CPR / 2; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+  return x;
 }
 
-// (I + N)^-1 in place for N strictly upper triangular, 128x128 in s.a.
+// Transposed staging: tile[d][i] = src[i][d] for tokens i < len (zero
+// beyond).  Loaded into registers first (load), written later (store).
+template <typename T> struct ColPieces;
+
+// bf16: a wave owns 8-dimension groups cg = w, w + 4, w + 8, w + 12; lane p
+// holds tokens 2p and 2p + 1, so each LDS write is one 32-bit word holding a
+// token pair, and the 64 lanes of a write cover one full row of the tile.
+template <> struct ColPieces<__bf16> {
+  u32x4 a[4], b[4];
+  __device__ __forceinline__ void load(const __bf16* src, size_t gs, int len) {
+    const int w = threadIdx.x >> 6, p = threadIdx.x & 63;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = 8 * (w + 4 * u);
+      a[u] = b[u] = u32x4{0u, 0u, 0u, 0u};
+      if (2 * p < len) a[u] = *reinterpret_cast<const u32x4*>(src + (size_t)(2 * p) * gs + c);
+      if (2 * p + 1 < len) b[u] = *reinterpret_cast<const u32x4*>(src + (size_t)(2 * p + 1) * gs + c);
+    }
+  }
+  __device__ __forceinline__ void store(__bf16* tile) const {
+    // opaque lane index: keeps the compiler from holding these addresses
+    // live from one staging to the next
+    int t = threadIdx.x;
+    asm volatile("" : "+v"(t));
+    const int w = t >> 6, p = t & 63;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = 8 * (w + 4 * u);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t lo = (a[u][e >> 1] >> (16 * (e & 1))) & 0xffffu;
+        const uint32_t hi = (b[u][e >> 1] >> (16 * (e & 1))) & 0xffffu;
+        *reinterpret_cast<uint32_t*>(tile + Sw<__bf16>::at(c + e, 2 * p)) = lo | (hi << 16);
+      }
+    }
+  }
+};
+
+// fp32: a wave owns 4-dimension groups cg = w + 4 u (u < 8) for both token
+// halves; lane l holds token l (+ 64).
+template <> struct ColPieces<float> {
+  f32x4 a[16];
+  __device__ __forceinline__ void load(const float* src, size_t gs, int len) {
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int c = 4 * (w + 4 * (u >> 1)), i = l + 64 * (u & 1);
+      a[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (i < len) a[u] = *reinterpret_cast<const f32x4*>(src + (size_t)i * gs + c);
+    }
+  }
+  __device__ __forceinline__ void store(float* tile) const {
+    int t = threadIdx.x;
+    asm volatile("" : "+v"(t));
+    const int w = t >> 6, l = t & 63;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int c = 4 * (w + 4 * (u >> 1)), i = l + 64 * (u & 1);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) tile[Sw<float>::at(c + e, i)] = a[u][e];
+    }
+  }
+};
+
+// One 16x16 tile of C = A B^T over k in [0, K): A rows ar + (lane & 15) from
+// columns ac + k of a WA-wide swizzled tile, B likewise.  k positions past K
+// read as zero (the bf16 fragment spans 32 values of k).
+template <typename T, int WA, int WB>
+__device__ __forceinline__ f32x4 tile_mma(const T* A, int ar, int ac, const T* B, int br, int bc,
+                                          int K) {
+  const int l = lane_id();
+  const int r = l & 15, kq = (l >> 4) * Mma<T>::E;
+  f32x4 acc = zero4();
+  for (int k = 0; k < K; k += Mma<T>::K) {
+    const bool live = k + kq < K;
+    const auto a = live ? sw_frag<T, WA>(A, ar + r, ac + k + kq) : Mma<T>::zero();
+    const auto b = live ? sw_frag<T, WB>(B, br + r, bc + k + kq) : Mma<T>::zero();
+    acc = Mma<T>::mma(a, b, acc);
+  }
+  return acc;
+}
+
+// (I + N)^-1 for N strictly upper triangular, 128x128, in place in s.t0
+// (upper form U); s.t1 receives the lower form L = U^T block by block (it
+// must hold zeros above the diagonal on entry).
 template <typename T>
 __device__ __forceinline__ void invert_unit_upper(IntraLds<T>& s) {
-  constexpr int LD = IntraLds<T>::LD, LDW = IntraLds<T>::LDW;
-  const int tid = threadIdx.x, w = tid >> 6;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   // 1) 16x16 diagonal blocks by back substitution, one column per thread:
-  //    V[i][c] = delta_ic - sum_{i < m <= c} N[i][m] V[m][c].
+  //    x_i = delta_ic - sum_{m > i} N[i][m] x_m.  The 16 threads of a block
+  //    are lanes of one wave, so every read of N precedes every write.
   if (tid < 128) {
     const int b0 = 16 * (tid >> 4), c = tid & 15;
     float col[16];
@@ -168,73 +246,95 @@ __device__ __forceinline__ void invert_unit_upper(IntraLds<T>& s) {
     for (int i = 0; i < 16; ++i) col[i] = (i == c) ? 1.0f : 0.0f;
 #pragma unroll
     for (int i = 14; i >= 0; --i) {
-      const T* nrow = s.a + (b0 + i) * LD + b0;
       float acc = 0.0f;
 #pragma unroll
-      for (int m = i + 1; m < 16; ++m) acc += to_f32(nrow[m]) * col[m];
+      for (int m = i + 1; m < 16; ++m) acc += to_f32(s.t0[Sw<T>::at(b0 + i, b0 + m)]) * col[m];
       if (i < c) col[i] = -acc;
     }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) s.a[(b0 + i) * LD + b0 + c] = from_f32<T>(col[i]);
+    for (int i = 0; i < 16; ++i) s.t0[Sw<T>::at(b0 + i, b0 + c)] = from_f32<T>(col[i]);
+    // row c of the lower form is column c of the upper form
+#pragma unroll
+    for (int i = 0; i < 16; i += 4)
+      store4<T>(s.t1 + Sw<T>::at(b0 + c, b0 + i), col[i], col[i + 1], col[i + 2], col[i + 3]);
   }
   __syncthreads();
-  // 2) doubling merges: the top-right block of each 2s x 2s diagonal block
-  //    becomes -X Y Z with X, Z its (already inverted) diagonal blocks and Y
-  //    the original top-right block.
-  const int l = lane_id();
+  // 2) doubling merges.  For the pair of finished sz-blocks at b0: X = U
+  //    block (b0, b0), Z = U block (b0+sz, b0+sz) whose rows-as-columns are
+  //    the L block, Y = the original N block (b0, b0+sz).  The new top-right
+  //    block is -X (Y Z); its transpose goes to L's bottom-left block.
 #pragma unroll 1
   for (int sz = 16; sz < 128; sz *= 2) {
-    const int tiles_side = sz / 16;
-    const int tiles_pair = tiles_side * tiles_side;
-    const int ntiles = (128 / (2 * sz)) * tiles_pair;   // sz / 4
-    // W1 = Y Z into s.w (pair p at rows p * sz)
+    const int side = sz / 16, per = side * side;
+    const int ntiles = (128 / (2 * sz)) * per;
+    // W^T = (Y Z)^T into the scratch: pair p at scratch rows p * sz
     for (int tt = w; tt < ntiles; tt += 4) {
-      const int p = tt / tiles_pair, ti = (tt % tiles_pair) / tiles_side, tj = tt % tiles_side;
+      const int p = tt / per, ti = (tt % per) / side, tj = tt % side;
       const int b0 = 2 * sz * p;
-      const Operand<T, true> Y{s.a + b0 * LD + (b0 + sz), LD};
-      const Operand<T, false> Z{s.a + (b0 + sz) * LD + (b0 + sz), LD};
-      f32x4 acc = zero4();
-      const int r = l & 15, kq = (l >> 4) * Mma<T>::E;
-      for (int k = 0; k < sz; k += Mma<T>::K) {
-        const bool live = k + kq < sz;
-        auto a = live ? Y.frag(16 * ti + r, k + kq) : Mma<T>::zero();
-        auto bf = live ? Z.frag(16 * tj + r, k + kq) : Mma<T>::zero();
-        acc = Mma<T>::mma(a, bf, acc);
-      }
-      const int row = 16 * ti + 4 * (l >> 4), col = 16 * tj + (l & 15);
-#pragma unroll
-      for (int x = 0; x < 4; ++x) s.w[(p * sz + row + x) * LDW + col] = from_f32<T>(acc[x]);
+      const f32x4 acc = tile_mma<T, 128, 128>(s.t0, b0 + 16 * ti, b0 + sz, s.t1,
+                                               b0 + sz + 16 * tj, b0 + sz, sz);
+      const int row = p * sz + 16 * tj + (l & 15), col = 16 * ti + 4 * (l >> 4);
+      store4<T>(s.w + Sw<T, 64>::at(row, col), acc[0], acc[1], acc[2], acc[3]);
     }
     __syncthreads();
-    // top-right = -X W1
     for (int tt = w; tt < ntiles; tt += 4) {
-      const int p = tt / tiles_pair, ti = (tt % tiles_pair) / tiles_side, tj = tt % tiles_side;
+      const int p = tt / per, ti = (tt % per) / side, tj = tt % side;
       const int b0 = 2 * sz * p;
-      const Operand<T, true> X{s.a + b0 * LD + b0, LD};
-      const Operand<T, false> W1{s.w + (p * sz) * LDW, LDW};
-      f32x4 acc = zero4();
-      const int r = l & 15, kq = (l >> 4) * Mma<T>::E;
-      for (int k = 0; k < sz; k += Mma<T>::K) {
-        const bool live = k + kq < sz;
-        auto a = live ? X.frag(16 * ti + r, k + kq) : Mma<T>::zero();
-        auto bf = live ? W1.frag(16 * tj + r, k + kq) : Mma<T>::zero();
-        acc = Mma<T>::mma(a, bf, acc);
-      }
-      const int row = 16 * ti + 4 * (l >> 4), col = 16 * tj + (l & 15);
+      // C = X W  (rows i of X, rows j of W^T)
+      const f32x4 acc = tile_mma<T, 128, 64>(s.t0, b0 + 16 * ti, b0, s.w, p * sz + 16 * tj, 0, sz);
+      const int i0 = b0 + 16 * ti + 4 * (l >> 4), j0 = b0 + sz + 16 * tj + (l & 15);
 #pragma unroll
-      for (int x = 0; x < 4; ++x) s.a[(b0 + row + x) * LD + (b0 + sz + col)] = from_f32<T>(-acc[x]);
+      for (int x = 0; x < 4; ++x) s.t0[Sw<T>::at(i0 + x, j0)] = from_f32<T>(-acc[x]);
+      if (sz < 64) store4<T>(s.t1 + Sw<T>::at(j0, i0), -acc[0], -acc[1], -acc[2], -acc[3]);
     }
     __syncthreads();
   }
 }
 
+// Scale-and-store of a wave's 64x64 accumulator block, transposed, into a
+// swizzled tile: tile[n][m..m+3] = acc(m.., n) * f[m..m+3] (f == nullptr: 1).
+template <typename T, typename Acc>
+__device__ __forceinline__ void put_t(T* tile, const Acc (&acc)[4][4], int m0, int n0, const float* f) {
+  const int l = lane_id();
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int m = m0 + 16 * i + 4 * (l >> 4), n = n0 + 16 * j + (l & 15);
+      float s0 = 1.f, s1 = 1.f, s2 = 1.f, s3 = 1.f;
+      if (f) { s0 = f[m]; s1 = f[m + 1]; s2 = f[m + 2]; s3 = f[m + 3]; }
+      store4<T>(tile + Sw<T>::at(n, m), acc[i][j].get(0) * s0, acc[i][j].get(1) * s1,
+                acc[i][j].get(2) * s2, acc[i][j].get(3) * s3);
+    }
+}
+
+// Same from raw accumulators into a plain 128x128 row-major global matrix,
+// times sign.
 template <typename T>
-__global__ __launch_bounds__(256) void intra_kernel(
+__device__ __forceinline__ void store_t_global(T* dst, const f32x4 (&acc)[4][4], int m0, int n0,
+                                               float sign) {
+  const int l = lane_id();
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int m = m0 + 16 * i + 4 * (l >> 4), n = n0 + 16 * j + (l & 15);
+      store4<T>(dst + n * kD + m, sign * acc[i][j][0], sign * acc[i][j][1], sign * acc[i][j][2],
+                sign * acc[i][j][3]);
+    }
+}
+
+struct F4 {   // adapter so raw accumulators fit put_t
+  f32x4 v;
+  __device__ __forceinline__ float get(int x) const { return v[x]; }
+};
+
+template <typename T>
+__global__ __launch_bounds__(256, 2) void intra_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, const int4* __restrict__ table,
     int32_t Nqk, int32_t Nv, int32_t slot0, float scale, int norm, T* __restrict__ inter,
     float* __restrict__ gam_out) {
-  constexpr int LD = IntraLds<T>::LD;
   __shared__ IntraLds<T> s;
   const int local_slot = blockIdx.x, h = blockIdx.y;
   const int4 e = table[slot0 + local_slot];
@@ -249,12 +349,14 @@ __global__ __launch_bounds__(256) void intra_kernel(
   const T* vc = v + ((size_t)start * Nv + h) * kD;
   T* dst = inter + ((size_t)local_slot * Nv + h) * 4 * (size_t)(kD * kD);
 
-  stage_rows<T, LD>(s.b, kc, qk_stride, len);
-  stage_rows<T, LD>(s.a, qc, qk_stride, len);
+  // ---- 1. k and q rows into registers; gate cumsum; row norms
+  RowPieces<T> kr, qr;
+  kr.load(kc, qk_stride, len);
+  qr.load(qc, qk_stride, len);
 
-  // Chunk-local inclusive cumsum of g in fp64 (blog post section 5(1)c),
-  // rows r < 128 on waves 0 and 1.  Padded rows (r >= len) carry g = 0, so
-  // their cumsum equals the chunk total and they act as empty rows.
+  // chunk-local inclusive cumsum of g in fp64 (blog post section 5(1)c) on
+  // waves 0 and 1; padded rows (r >= len) carry g = 0 and beta = 0, so they
+  // act as empty rows
   double gsum = 0.0;
   float bt = 0.0f;
   if (tid < 128) {
@@ -266,123 +368,157 @@ __global__ __launch_bounds__(256) void intra_kernel(
       const double y = __shfl_up(gsum, off, 64);
       if (l >= off) gsum += y;
     }
-    if (tid == 63) s.gc[0] = gsum;   // wave 0's total, read by wave 1 below
+    if (tid == 63) s.part = gsum;
   }
-  __syncthreads();
 
-  // L2 norms of the staged key and query rows (Ascend operator page,
-  // x / sqrt(sum x^2 + eps), eps = 1e-6), two threads per row.
-  {
-    const int r = tid >> 1, half = tid & 1;
-    float sk = 0.0f, sq = 0.0f;
-#pragma unroll 8
-    for (int c = 64 * half; c < 64 * half + 64; ++c) {
-      const float xk = to_f32(s.b[r * LD + c]), xq = to_f32(s.a[r * LD + c]);
-      sk += xk * xk;
-      sq += xq * xq;
-    }
-    sk += __shfl_xor(sk, 1, 64);
-    sq += __shfl_xor(sq, 1, 64);
-    if (half == 0) {
+  // L2 norms (Ascend operator page, x / sqrt(sum x^2 + eps), eps = 1e-6)
+  constexpr int CPR = RowPieces<T>::CPR;
+#pragma unroll
+  for (int it = 0; it < RowPieces<T>::N; ++it) {
+    const float sk = row_sum<CPR>(kr.sumsq(it));
+    const float sq = row_sum<CPR>(qr.sumsq(it));
+    const int idx = tid + 256 * it;
+    if (idx % CPR == 0) {
+      const int r = idx / CPR;
       const bool ok = r < len;
       s.rk[r] = ok ? (norm ? 1.0f / sqrtf(sk + 1e-6f) : 1.0f) : 0.0f;
       s.rq[r] = ok ? (norm ? scale / sqrtf(sq + 1e-6f) : scale) : 0.0f;
     }
   }
-  const double wave0_total = s.gc[0];
+  kr.store(s.t0);
+  qr.store(s.t1);
   __syncthreads();
   if (tid < 128) {
-    if (w == 1) gsum += wave0_total;
+    if (w == 1) gsum += s.part;
     s.gc[tid] = gsum;
     s.beta[tid] = bt;
   }
-  __syncthreads();
-  if (tid < 128) {
-    const int r = tid;
-    const double glast = s.gc[127];
-    const double gc = s.gc[r];
-    const float gm = __expf((float)gc);
-    s.ck[r] = __expf((float)(glast - gc)) * s.rk[r];
-    s.xk[r] = s.beta[r] * gm * s.rk[r];
-    s.qs[r] = gm * s.rq[r];
-    if (r == 0) gam_out[(size_t)(slot0 + local_slot) * Nv + h] = __expf((float)glast);
-  }
 
-  // Grams on raw inputs: KK[a][c] = k_a.k_c and C2[i][r] = k_i.q_r
-  f32x4 acc1[4][4], acc2[4][4];
-  zero_acc(acc1);
-  zero_acc(acc2);
-  {
-    const Operand<T, true> Kop{s.b, LD}, Qop{s.a, LD};
-    mma_block64(acc1, Kop, Kop, m0, n0, kD);
-    mma_block64(acc2, Kop, Qop, m0, n0, kD);
-  }
+  // ---- 2. Grams on raw inputs: G1[a][c] = k_a.k_c, G2[i][r] = k_i.q_r
+  f32x4 a1[4][4], a2[4][4];
+  zero_acc(a1);
+  zero_acc(a2);
+  sw_gemm64x2<T>(a1, a2, s.t0, s.t0, s.t1, m0, n0);
   __syncthreads();
 
-  // N = A+^T into s.a:  N[c][a] = beta_a rk_a rk_c Gamma[a][c] KK[a][c] for c < a
-  // P into s.b:         P[r][i] = rq_r rk_i Gamma[r][i] (q_r.k_i)   for i <= r
+  // ---- 3. decay mask and scalings.  Per element (a, c) one exponential
+  // serves all three matrices: exp(-|gc_a - gc_c|) is Gamma[a][c] below the
+  // diagonal and Gamma[c][a] above it (gc is non-increasing for g <= 0).
+  //   N[c][a]  = beta_a rk_a rk_c Gamma[a][c] G1[a][c]   (c < a)  -> slot 0
+  //   P[r][i]  = rq_r rk_i Gamma[r][i] G2[i][r]          (i <= r) -> registers
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
-      const int row = m0 + 16 * i + 4 * (l >> 4);
-      const int col = n0 + 16 * jj + (l & 15);
-      float nv[4], pv[4];
+      const int a = m0 + 16 * i + 4 * (l >> 4);
+      const int c = n0 + 16 * jj + (l & 15);
+      const double gcc = s.gc[c];
+      const float rkc = s.rk[c], rqc = s.rq[c];
+      float nv[4];
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
-        const int a = row + x;   // acc1: (a, c = col);  acc2: (i = a, r = col)
-        nv[x] = 0.0f;
-        if (col < a)
-          nv[x] = s.beta[a] * s.rk[a] * s.rk[col] * __expf((float)(s.gc[a] - s.gc[col])) * acc1[i][jj][x];
-        pv[x] = 0.0f;
-        if (a <= col)
-          pv[x] = s.rq[col] * s.rk[a] * __expf((float)(s.gc[col] - s.gc[a])) * acc2[i][jj][x];
+        const int ax = a + x;
+        const float ex = __expf(-(float)fabs(s.gc[ax] - gcc));
+        const float rka = s.rk[ax];
+        nv[x] = (c < ax) ? s.beta[ax] * rka * rkc * ex * a1[i][jj][x] : 0.0f;
+        a2[i][jj][x] = (ax <= c) ? rqc * rka * ex * a2[i][jj][x] : 0.0f;
       }
-      store4<T>(s.a + col * LD + row, nv[0], nv[1], nv[2], nv[3]);
-      store4<T>(s.b + col * LD + row, pv[0], pv[1], pv[2], pv[3]);
+      store4<T>(s.t0 + Sw<T>::at(c, a), nv[0], nv[1], nv[2], nv[3]);
     }
-  __syncthreads();
-
-  invert_unit_upper<T>(s);   // s.a = T^T
-
-  // R^T = T^T P^T:  accR[j][r] = sum_i T^T[j][i] P[r][i]  (so lane holds R[r][j..j+3])
-  f32x4 accR[4][4];
-  zero_acc(accR);
-  mma_block64(accR, Operand<T, true>{s.a, LD}, Operand<T, true>{s.b, LD}, m0, n0, kD);
-  __syncthreads();
-
-  // T^T diag(ck) in place; raw K^T into s.b
-  for (int idx = tid; idx < 128 * 128; idx += 256) {
-    const int r = idx >> 7, c = idx & 127;
-    s.a[r * LD + c] = from_f32<T>(to_f32(s.a[r * LD + c]) * s.ck[c]);
-  }
-  stage_transposed<T, LD>(s.b, kc, qk_stride, len);
-  __syncthreads();
-
-  // Z = T^T K_dec:  accZ[j][d] = sum_i (T^T diag(ck))[j][i] K^T[d][i]
-  f32x4 accZ[4][4];
-  zero_acc(accZ);
-  mma_block64(accZ, Operand<T, true>{s.a, LD}, Operand<T, true>{s.b, LD}, m0, n0, kD);
-  __syncthreads();
-
-  // M' = -K^T diag(xk) Z:  C[e][d] = sum_j K^T[e][j] (Z[j][d] xk_j);  store Mt[d][e] = M'[e][d]
-  put_transposed<T, LD>(s.a, accZ, m0, n0, s.xk);   // s.a[d][j] = Z[j][d] xk_j
-  __syncthreads();
+  // zero slot 1: the lower form of the inverse is built into it
   {
-    f32x4 acc[4][4];
-    zero_acc(acc);
-    mma_block64(acc, Operand<T, true>{s.b, LD}, Operand<T, true>{s.a, LD}, m0, n0, kD);
-    store_transposed_global<T>(dst + 0 * kD * kD, acc, m0, n0, -1.0f);
+    constexpr int NZ = kD * kD * (int)sizeof(T) / 16 / 256;
+#pragma unroll
+    for (int it = 0; it < NZ; ++it)
+      reinterpret_cast<u32x4*>(s.t1)[tid + 256 * it] = u32x4{0u, 0u, 0u, 0u};
+  }
+  if (tid < 128) {
+    const int r = tid;
+    const double glast = s.gc[127];
+    const double gcr = s.gc[r];
+    const float gm = __expf((float)gcr);
+    s.ck[r] = __expf((float)(glast - gcr)) * s.rk[r];
+    s.xk[r] = s.beta[r] * gm * s.rk[r];
+    s.qs[r] = gm * s.rq[r];
+    if (r == 0) gam_out[(size_t)(slot0 + local_slot) * Nv + h] = __expf((float)glast);
   }
   __syncthreads();
 
-  // Qp = Q_dec - R diag(xk) K:  C[d][r] = sum_j K^T[d][j] (R[r][j] xk_j)
-  put_transposed<T, LD>(s.a, accR, m0, n0, s.xk);   // s.a[r][j] = R[r][j] xk_j
+  // ---- 4. T^T = (I + A+^T)^-1 in slot 0
+  invert_unit_upper<T>(s);
+
+  // ---- 5. P into slot 1 (the lower form is no longer needed)
+  {
+    const int lr = l;
+    (void)lr;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int m = m0 + 16 * i + 4 * (l >> 4), n = n0 + 16 * jj + (l & 15);
+        store4<T>(s.t1 + Sw<T>::at(n, m), a2[i][jj][0], a2[i][jj][1], a2[i][jj][2], a2[i][jj][3]);
+      }
+  }
   __syncthreads();
+
+  // ---- 6. R^T = T^T P^T: acc[j][r] = sum_i T^T[j][i] P[r][i] = R[r][j]
+  Pack4<T> Rp[4][4];
   {
     f32x4 acc[4][4];
     zero_acc(acc);
-    mma_block64(acc, Operand<T, true>{s.b, LD}, Operand<T, true>{s.a, LD}, m0, n0, kD);
+    sw_gemm64<T>(acc, s.t0, s.t1, m0, n0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) Rp[i][jj].set(acc[i][jj]);
+  }
+  __syncthreads();
+
+  // ---- 7. T^T diag(ck) in place; K^T into slot 1
+  {
+    constexpr int EPC = 16 / (int)sizeof(T);
+    constexpr int NP = kD * kD / EPC / 256;
+#pragma unroll
+    for (int it = 0; it < NP; ++it) {
+      const int idx = tid + 256 * it;
+      const int r = idx / (kD / EPC), c = (idx % (kD / EPC)) * EPC;
+      T* p = s.t0 + Sw<T>::at(r, c);
+      u32x4 raw = *reinterpret_cast<const u32x4*>(p);
+      T* ev = reinterpret_cast<T*>(&raw);
+#pragma unroll
+      for (int x = 0; x < EPC; ++x) ev[x] = from_f32<T>(to_f32(ev[x]) * s.ck[c + x]);
+      *reinterpret_cast<u32x4*>(p) = raw;
+    }
+  }
+  {
+    ColPieces<T> kt;
+    kt.load(kc, qk_stride, len);
+    kt.store(s.t1);
+  }
+  __syncthreads();
+
+  // ---- 8. Z = T^T diag(ck) K:  acc[j][d] = sum_i (T^T ck)[j][i] K^T[d][i]
+  Pack4<T> Zp[4][4];
+  {
+    f32x4 acc[4][4];
+    zero_acc(acc);
+    sw_gemm64<T>(acc, s.t0, s.t1, m0, n0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) Zp[i][jj].set(acc[i][jj]);
+  }
+  __syncthreads();
+
+  // ---- 9. R diag(xk) into slot 0:  t0[r][j] = R[r][j] xk_j
+  put_t<T>(s.t0, Rp, m0, n0, s.xk);
+  __syncthreads();
+
+  // ---- 10. Qp = Q_dec - R diag(xk) K:  acc[d][r] = sum_j K^T[d][j] (R xk)[r][j]
+  {
+    f32x4 acc[4][4];
+    zero_acc(acc);
+    sw_gemm64<T>(acc, s.t1, s.t0, m0, n0);
     T* qp = dst + 1 * kD * kD;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -399,26 +535,47 @@ __global__ __launch_bounds__(256) void intra_kernel(
   }
   __syncthreads();
 
-  // Ou = R diag(beta) V:  C[r][e] = sum_j (R[r][j] beta_j) V^T[e][j];  store OuT[e][r]
-  stage_transposed<T, LD>(s.b, vc, v_stride, len);
-  put_transposed<T, LD>(s.a, accR, m0, n0, s.beta);   // s.a[r][j] = R[r][j] beta_j
+  // ---- 11. Z^T diag(xk) into slot 0:  t0[d][j] = Z[j][d] xk_j
+  put_t<T>(s.t0, Zp, m0, n0, s.xk);
   __syncthreads();
+
+  // ---- 12. M' = -K^T diag(xk) Z:  acc[e][d] = sum_j K^T[e][j] (Z^T xk)[d][j];  Mt[d][e] = -acc
   {
     f32x4 acc[4][4];
     zero_acc(acc);
-    mma_block64(acc, Operand<T, true>{s.a, LD}, Operand<T, true>{s.b, LD}, m0, n0, kD);
-    store_transposed_global<T>(dst + 3 * kD * kD, acc, m0, n0, 1.0f);
+    sw_gemm64<T>(acc, s.t1, s.t0, m0, n0);
+    store_t_global<T>(dst + 0 * kD * kD, acc, m0, n0, -1.0f);
   }
   __syncthreads();
 
-  // Bm = V^T diag(beta) Z:  C[d][e] = sum_j (Z[j][d] beta_j) V^T[e][j];  store Bm[e][d]
-  put_transposed<T, LD>(s.a, accZ, m0, n0, s.beta);   // s.a[d][j] = Z[j][d] beta_j
+  // ---- 13. V^T into slot 1; R diag(beta) into slot 0
+  {
+    ColPieces<T> vt;
+    vt.load(vc, v_stride, len);
+    vt.store(s.t1);
+  }
+  put_t<T>(s.t0, Rp, m0, n0, s.beta);
   __syncthreads();
+
+  // ---- 14. Ou = R diag(beta) V:  acc[r][e] = sum_j (R beta)[r][j] V^T[e][j];  OuT[e][r]
   {
     f32x4 acc[4][4];
     zero_acc(acc);
-    mma_block64(acc, Operand<T, true>{s.a, LD}, Operand<T, true>{s.b, LD}, m0, n0, kD);
-    store_transposed_global<T>(dst + 2 * kD * kD, acc, m0, n0, 1.0f);
+    sw_gemm64<T>(acc, s.t0, s.t1, m0, n0);
+    store_t_global<T>(dst + 3 * kD * kD, acc, m0, n0, 1.0f);
+  }
+  __syncthreads();
+
+  // ---- 15. Z^T diag(beta) into slot 0
+  put_t<T>(s.t0, Zp, m0, n0, s.beta);
+  __syncthreads();
+
+  // ---- 16. Bm = V^T diag(beta) Z:  acc[d][e] = sum_j (Z^T beta)[d][j] V^T[e][j];  Bm[e][d]
+  {
+    f32x4 acc[4][4];
+    zero_acc(acc);
+    sw_gemm64<T>(acc, s.t0, s.t1, m0, n0);
+    store_t_global<T>(dst + 2 * kD * kD, acc, m0, n0, 1.0f);
   }
 }
 
