@@ -199,6 +199,37 @@ __device__ __forceinline__ void sw_gemm64x2(f32x4 (&acc1)[4][4], f32x4 (&acc2)[4
   }
 }
 
+// ---------------------------------------------------------------------------
+// Workspace order of the four per-(chunk, head) matrices, chosen so that the
+// chunk-serial pass reads every operand as whole contiguous blocks (one
+// 16-byte, or 8-byte, piece per lane, lanes in order):
+//   frag_off(row, k): matrix-core operand order.  Block (row / 16, k / K)
+//     holds the 16 x K tile; lane (row % 16) + 16 ((k % K) / E) holds its E
+//     consecutive k values.  Used for Mt (rows d) and Qp (rows r).
+//   bm_off(v, d): accumulator order of the state waves of the pass
+//     (value row v, key column d).
+//   ou_off(r, v): accumulator order of its output waves (chunk row r, value v).
+// ---------------------------------------------------------------------------
+template <typename T>
+__device__ __forceinline__ int frag_off(int row, int k) {
+  constexpr int K = Mma<T>::K, E = Mma<T>::E;
+  const int blk = (row >> 4) * (kD / K) + k / K;
+  const int lane = (row & 15) + 16 * ((k % K) / E);
+  return blk * 64 * E + lane * E + (k % E);
+}
+// block (vb, wave half, 16-row tile i, 16-column tile t) of 64 lanes x 4 values
+__device__ __forceinline__ int pass_blk(int vb, int wh, int i, int t) {
+  return (((vb * 2 + wh) * 4 + i) * 2 + t) * 256;
+}
+__device__ __forceinline__ int bm_off(int v, int d) {
+  return pass_blk(v >> 5, d >> 6, (d & 63) >> 4, (v & 31) >> 4) + ((v & 15) + 16 * ((d & 15) >> 2)) * 4 +
+         (d & 3);
+}
+__device__ __forceinline__ int ou_off(int r, int v) {
+  return pass_blk(v >> 5, r >> 6, (r & 63) >> 4, (v & 31) >> 4) + ((r & 15) + 16 * ((v & 15) >> 2)) * 4 +
+         (v & 3);
+}
+
 template <int M, int N>
 __device__ __forceinline__ void zero_acc(f32x4 (&acc)[M][N]) {
 #pragma unroll

@@ -6,115 +6,119 @@
 //   S_next = exp(gc_last) S + S M' + Bm         (the state after the chunk)
 // with S in R^{Dv x Dk} (row = value index, as in the Ascend operator page's
 // state_new [Dv, Dk]).  Rows of S never mix (every term acts on each row of
-// S alone), so a workgroup owns 16 rows of S of one (sequence, value head)
-// and keeps them in registers, fp32, for the whole sequence: 8 workgroups per
-// (sequence, head).  Each of the 4 waves owns 32 key columns of those rows
-// (two 16x16 tiles of S^T) and 32 output rows of the chunk; per chunk the
-// waves exchange S once through LDS, as the shared B operand of one
-// [Mt; Qp] (256 x 128) x S^T (128 x 16) product on the matrix cores.
-// Chunk boundaries restart at sequence starts, so a varlen boundary inside a
-// 128-token grid needs no special case: a short last chunk only writes its
-// first len output rows.
+// S alone), so a workgroup owns BV = 32 rows of S of one (sequence, value
+// head): 4 workgroups per (sequence, head), placed on one XCD so they share
+// its L2.
+//
+// Per chunk the workgroup computes two products on the matrix cores, both
+// reading S (bf16 copy of the fp32 state, exchanged once through LDS) by rows:
+//   waves 0, 1 (state):  C[d][v] = sum_e Mt[d][e] S[v][e] = (S M')[v][d],
+//                        64 key rows d each; they keep S^T in fp32 registers
+//                        and apply S = exp(gc_last) S + S M' + Bm;
+//   waves 2, 3 (output): C[v][r] = sum_d S[v][d] Qp[r][d] = (Qp S^T)[r][v],
+//                        64 chunk rows r each; out[r][v..v+3] = C + Ou.
+// The per-chunk operands (rows of Mt or Qp, entries of Bm or Ou, the chunk's
+// decay and table entry) do not depend on S, so each lane loads them DEPTH
+// chunks ahead into a ring of register sets.  Chunk boundaries restart at
+// sequence starts, so a varlen boundary inside a 128-token grid needs no
+// special case: a short last chunk only writes its first len output rows.
 #include "gdr_device.h"
+#include "gdr_internal.h"
 #include "gdr_kernels.h"
 
 namespace gdr {
 
-template <typename T>
-__device__ __forceinline__ void put4(T* p, const float* x);
-template <>
-__device__ __forceinline__ void put4<float>(float* p, const float* x) {
-  *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
-}
-template <>
-__device__ __forceinline__ void put4<__bf16>(__bf16* p, const float* x) {
+constexpr int kBV = 32;   // state rows (value indices) per workgroup
+
+// Four consecutive elements of T as fp32.
+template <typename T> struct Quad;
+template <> struct Quad<__bf16> {
   bf16x4 v;
-  v[0] = (__bf16)x[0]; v[1] = (__bf16)x[1]; v[2] = (__bf16)x[2]; v[3] = (__bf16)x[3];
-  *reinterpret_cast<bf16x4*>(p) = v;
-}
-
-template <typename T>
-__device__ __forceinline__ void get4(const T* p, float* x);
-template <>
-__device__ __forceinline__ void get4<float>(const float* p, float* x) {
-  const float4 v = *reinterpret_cast<const float4*>(p);
-  x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
-}
-template <>
-__device__ __forceinline__ void get4<__bf16>(const __bf16* p, float* x) {
-  const bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
-  x[0] = (float)v[0]; x[1] = (float)v[1]; x[2] = (float)v[2]; x[3] = (float)v[3];
-}
-
-// Operands of one chunk held by one lane: its A fragments of [Mt; Qp], its
-// entries of Bm and Ou, and the chunk's decay exp(gc_last).
-template <typename T>
-struct ChunkOps {
-  static constexpr int KSTEPS = kD / Mma<T>::K;
-  typename Mma<T>::frag a[4][KSTEPS];
-  float bm[2][4], ou[2][4];
-  float gC;
+  __device__ __forceinline__ void load(const __bf16* p) { v = *reinterpret_cast<const bf16x4*>(p); }
+  __device__ __forceinline__ float operator[](int x) const { return (float)v[x]; }
+};
+template <> struct Quad<float> {
+  f32x4 v;
+  __device__ __forceinline__ void load(const float* p) { v = *reinterpret_cast<const f32x4*>(p); }
+  __device__ __forceinline__ float operator[](int x) const { return v[x]; }
 };
 
 template <typename T>
-__device__ __forceinline__ void load_ops(ChunkOps<T>& o, const T* __restrict__ mats,
-                                         const float* __restrict__ gam, int w, int l, int vcol) {
-  constexpr int KSTEPS = ChunkOps<T>::KSTEPS;
-  const int r16 = l & 15, kq = (l >> 4) * Mma<T>::E;
-  const T* Mt = mats;
-  const T* Qp = mats + kD * kD;
-  const T* Bm = mats + 2 * kD * kD;
-  const T* OuT = mats + 3 * kD * kD;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const T* base = (i < 2 ? Mt : Qp) + (size_t)(32 * w + 16 * (i & 1) + r16) * kD;
-#pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) o.a[i][ks] = Mma<T>::load_contig(base + ks * Mma<T>::K + kq);
-  }
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int kr = 32 * w + 16 * t + 4 * (l >> 4);
-    get4<T>(Bm + (size_t)vcol * kD + kr, o.bm[t]);
-    get4<T>(OuT + (size_t)vcol * kD + kr, o.ou[t]);
-  }
-  o.gC = *gam;
+__device__ __forceinline__ void put4(T* p, float x0, float x1, float x2, float x3);
+template <>
+__device__ __forceinline__ void put4<float>(float* p, float x0, float x1, float x2, float x3) {
+  *reinterpret_cast<float4*>(p) = make_float4(x0, x1, x2, x3);
+}
+template <>
+__device__ __forceinline__ void put4<__bf16>(__bf16* p, float x0, float x1, float x2, float x3) {
+  bf16x4 v;
+  v[0] = (__bf16)x0; v[1] = (__bf16)x1; v[2] = (__bf16)x2; v[3] = (__bf16)x3;
+  *reinterpret_cast<bf16x4*>(p) = v;
 }
 
+// Prefetch depth per operand type: how many chunks ahead a lane's operands
+// are loaded (fp32 fragments take twice the registers).
+template <typename T> struct Depth { static constexpr int value = 2; };
+template <> struct Depth<float> { static constexpr int value = 1; };
+
+// One chunk's operands held by one lane.
 template <typename T>
-__global__ __launch_bounds__(256) void inter_kernel(
+struct ChunkOps {
+  static constexpr int KSTEPS = kD / Mma<T>::K;
+  typename Mma<T>::frag a[4][KSTEPS];   // rows of Mt (state waves) or Qp (output waves)
+  Quad<T> x[4][2];                      // Bm (state waves) or Ou (output waves) entries
+  float gC;                             // exp(gc_last) of the chunk
+  int start, len;                       // the chunk's tokens
+  uint32_t warm[2];                     // L2 warming loads in flight (values unused)
+};
+
+// Chunks ahead whose operands are pulled into L2 by touch loads: one 4-byte
+// load per 128-byte line, so a warming instruction covers 8 KiB where an
+// operand load covers 1 KiB, and the operand loads later hit in L2.
+constexpr int kWarmAhead = 5;
+
+template <typename T>
+__global__ __launch_bounds__(256, 1) void inter_kernel(
     const T* __restrict__ inter, const int4* __restrict__ table, const int32_t* __restrict__ choff,
     const float* __restrict__ gam, const float* state_in, float* carry, float* state_out,
     int32_t N, int32_t Nv, int32_t slot0, int32_t nseg, int first_segment, T* __restrict__ out) {
-  constexpr int LDS_S = kD + 16 / (int)sizeof(T);
   constexpr int KSTEPS = ChunkOps<T>::KSTEPS;
-  __shared__ T sS[2][16 * LDS_S];
+  constexpr int DEPTH = Depth<T>::value;
+  constexpr int NSET = DEPTH + 1;
+  constexpr int VB = kD / kBV;   // workgroups per (sequence, head)
+  __shared__ T sS[2][kBV * kD];  // bf16/fp32 copy of S rows [v][k], swizzled
+  // the segment's chunk table and decays, staged once: a scalar load in the
+  // chunk loop would make every LDS wait also wait for global memory
+  __shared__ int2 sTab[kMaxSegSlots];
+  __shared__ float sGam[kMaxSegSlots];
 
-  // Block -> (sequence b, head h, 16-row block vb).  The 8 row blocks of one
-  // (b, h) read the same Mt / Qp matrices, so when possible they are placed
-  // on the same XCD (blocks are dealt to the 8 XCDs round-robin) to share
-  // that XCD's L2.
+  // Block -> (sequence b, head h, row block vb).  Blocks are dealt to the 8
+  // XCDs round-robin; the VB row blocks of one (b, h) read the same Mt and Qp,
+  // so when possible they land on the same XCD.
   const int id = blockIdx.x;
   const int pairs = N * Nv;
   int bh, vb;
   if ((pairs & 7) == 0) {
-    bh = (id & 7) + 8 * (id >> 6);
-    vb = (id >> 3) & 7;
+    bh = (id & 7) + 8 * (id / (8 * VB));
+    vb = (id >> 3) % VB;
   } else {
-    bh = id >> 3;
-    vb = id & 7;
+    bh = id / VB;
+    vb = id % VB;
   }
   const int b = bh / Nv, h = bh % Nv;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-  const int vcol = 16 * vb + (l & 15);          // value row of S held by this lane
-  const size_t sbase = (size_t)bh * kD * kD + (size_t)vcol * kD;
+  const bool state_wave = w < 2;
+  const int rb = 64 * (w & 1);               // first row (d or r) of this wave's block
+  const int v0 = kBV * vb;                   // first state row of the workgroup
+  const size_t sb = (size_t)bh * kD * kD;    // this (b, h)'s state
   const int c0 = choff[b], c1 = choff[b + 1];
 
   if (c0 == c1) {
     // empty sequence: its final state is its initial state
     if (first_segment && state_out && state_out != state_in) {
-      for (int idx = tid; idx < 16 * kD / 4; idx += 256) {
+      for (int idx = tid; idx < kBV * kD / 4; idx += 256) {
         const int r = idx / (kD / 4), c = (idx % (kD / 4)) * 4;
-        const size_t off = (size_t)bh * kD * kD + (size_t)(16 * vb + r) * kD + c;
+        const size_t off = sb + (size_t)(v0 + r) * kD + c;
         float4 val = make_float4(0.f, 0.f, 0.f, 0.f);
         if (state_in) val = *reinterpret_cast<const float4*>(state_in + off);
         *reinterpret_cast<float4*>(state_out + off) = val;
@@ -127,67 +131,161 @@ __global__ __launch_bounds__(256) void inter_kernel(
   const float* src = (cb == c0) ? state_in : carry;
   float* dstS = (ce == c1) ? state_out : carry;
   const size_t mstride = (size_t)Nv * 4 * (size_t)(kD * kD);
+  // matrices of (slot c, head h): Mt, Qp, Bm, Ou
   const T* mats0 = inter + (size_t)h * 4 * (size_t)(kD * kD) - (size_t)slot0 * mstride;
 
-  // S^T tiles: rows (key index) kr(t, x) = 32 w + 16 t + 4 (l >> 4) + x, column vcol
-  float S[2][4];
+  const int r16 = l & 15, q4 = l >> 4, kq = q4 * Mma<T>::E;
+  for (int idx = tid; idx < ce - cb; idx += 256) {
+    const int4 e = table[cb + idx];
+    sTab[idx] = make_int2(e.y, e.z);
+    sGam[idx] = gam[(size_t)(cb + idx) * Nv + h];
+  }
+  __syncthreads();
+
+  // Every operand load below is one contiguous block per wave: the workspace
+  // holds Mt and Qp in matrix-core operand order (frag_off) and Bm and Ou in
+  // this pass's accumulator order (bm_off, ou_off).
+  auto load_ops = [&](ChunkOps<T>& o, int c) {
+    const T* m = mats0 + (size_t)c * mstride;
+    // rows rb + 16 i + r16 of Mt (state waves) or Qp (output waves)
+    const T* A = m + (state_wave ? 0 : kD * kD) + (size_t)(rb >> 4) * KSTEPS * 64 * Mma<T>::E +
+                 l * Mma<T>::E;
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int kr = 32 * w + 16 * t + 4 * (l >> 4);
-    if (src) get4<float>(src + sbase + kr, S[t]);
-    else S[t][0] = S[t][1] = S[t][2] = S[t][3] = 0.f;
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks)
+        o.a[i][ks] = Mma<T>::load_contig(A + (size_t)(i * KSTEPS + ks) * 64 * Mma<T>::E);
+    // state waves: Bm[v][d..d+3], v = v0 + 16 t + r16, d = rb + 16 i + 4 q4;
+    // output waves: Ou[r][v..v+3], r = rb + 16 i + r16, v = v0 + 16 t + 4 q4
+    const T* X = m + (state_wave ? 2 : 3) * kD * kD + l * 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) o.x[i][t].load(X + pass_blk(vb, rb >> 6, i, t));
+    o.gC = sGam[c - cb];
+    const int2 e = sTab[c - cb];
+    o.start = e.x;
+    o.len = e.y;
+  };
+
+  // State waves: S^T tiles st[i][t] hold S[v][d..d+3] for d = rb + 16 i + 4 q4 + x,
+  // v = v0 + 16 t + r16 (the layout of the state product's accumulators).
+  f32x4 st[4][2];
+  if (state_wave) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        st[i][t] = zero4();
+        if (src)
+          st[i][t] = *reinterpret_cast<const f32x4*>(
+              src + sb + (size_t)(v0 + 16 * t + r16) * kD + rb + 16 * i + 4 * q4);
+      }
   }
 
-  const int r16 = l & 15, kq = (l >> 4) * Mma<T>::E;
-  int buf = 0;
-  // One chunk of the state pass with its operands already in registers.
-  auto step = [&](const ChunkOps<T>& o, int c) {
-    // S (this block's 16 rows) as the B operand, [v][k] in LDS
+  // Lines this workgroup warms per chunk: its quarter of Mt and of Qp (the
+  // other row blocks of the (b, h) warm the rest, through the shared L2) and
+  // its own quarters of Bm and Ou.  Each quarter is a contiguous range.
+  constexpr int QB = kD * kD * (int)sizeof(T) / 4;   // bytes per quarter matrix
+  constexpr int NWARM = 4 * QB / 128;                // lines per chunk
+  auto warm = [&](ChunkOps<T>& o, int c) {
+    const char* m = reinterpret_cast<const char*>(mats0 + (size_t)c * mstride);
 #pragma unroll
-    for (int t = 0; t < 2; ++t) put4<T>(&sS[buf][r16 * LDS_S + 32 * w + 16 * t + 4 * (l >> 4)], S[t]);
+    for (int u = 0; u < 2; ++u) {
+      int L = tid + 256 * u;
+      if (L >= NWARM) L -= NWARM;                // duplicates are harmless
+      const int mat = L / (QB / 128), k = L % (QB / 128);
+      o.warm[u] = *reinterpret_cast<const uint32_t*>(m + (size_t)mat * 4 * QB + (size_t)vb * QB + k * 128);
+    }
+  };
+  uint32_t sink = 0;
+
+  ChunkOps<T> ops[NSET];
+#pragma unroll
+  for (int k = 0; k < NSET; ++k) ops[k].warm[0] = ops[k].warm[1] = 0u;
+#pragma unroll
+  for (int k = 0; k < DEPTH; ++k)
+    if (cb + k < ce) load_ops(ops[k], cb + k);
+
+  int buf = 0;
+  auto step = [&](ChunkOps<T>& o, ChunkOps<T>& next, int c) {
+    T* sbuf = sS[buf];
+    if (state_wave) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          put4<T>(sbuf + Sw<T>::at(16 * t + r16, rb + 16 * i + 4 * q4), st[i][t][0], st[i][t][1],
+                  st[i][t][2], st[i][t][3]);
+    }
     __syncthreads();
-    f32x4 acc[4] = {zero4(), zero4(), zero4(), zero4()};
+    f32x4 acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i][0] = acc[i][1] = zero4();
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
-      const auto bfr = Mma<T>::load_contig(&sS[buf][r16 * LDS_S + ks * Mma<T>::K + kq]);
+      const auto s0 = sw_frag<T>(sbuf, r16, ks * Mma<T>::K + kq);
+      const auto s1 = sw_frag<T>(sbuf, 16 + r16, ks * Mma<T>::K + kq);
+      if (state_wave) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] = Mma<T>::mma(o.a[i][ks], bfr, acc[i]);
+        for (int i = 0; i < 4; ++i) {
+          acc[i][0] = Mma<T>::mma(o.a[i][ks], s0, acc[i][0]);
+          acc[i][1] = Mma<T>::mma(o.a[i][ks], s1, acc[i][1]);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[i][0] = Mma<T>::mma(s0, o.a[i][ks], acc[i][0]);
+          acc[i][1] = Mma<T>::mma(s1, o.a[i][ks], acc[i][1]);
+        }
+      }
     }
-    const int4 e = table[c];
-    const int start = e.y, len = e.z;
-    // outputs of this chunk (from the state at its start)
+    if (c + DEPTH < ce) load_ops(next, c + DEPTH);
+    // the warming loads held in this set were issued NSET chunks ago
+    sink ^= o.warm[0] ^ o.warm[1];
+    if (c + kWarmAhead < ce) warm(o, c + kWarmAhead);
+    else o.warm[0] = o.warm[1] = 0u;
+    if (state_wave) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int r = 32 * w + 16 * t + 4 * (l >> 4);
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int x = 0; x < 4; ++x)
-        if (r + x < len)
-          out[((size_t)(start + r + x) * Nv + h) * kD + vcol] = from_f32<T>(acc[2 + t][x] + o.ou[t][x]);
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int x = 0; x < 4; ++x)
+            st[i][t][x] = o.gC * st[i][t][x] + acc[i][t][x] + o.x[i][t][x];
+    } else {
+      // acc[i][t] holds O[r][v..v+3] - Ou for r = rb + 16 i + r16, v = 16 t + 4 q4
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = rb + 16 * i + r16;
+        if (r < o.len) {
+          T* orow = out + ((size_t)(o.start + r) * Nv + h) * kD + v0;
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+            put4<T>(orow + 16 * t + 4 * q4, acc[i][t][0] + o.x[i][t][0], acc[i][t][1] + o.x[i][t][1],
+                    acc[i][t][2] + o.x[i][t][2], acc[i][t][3] + o.x[i][t][3]);
+        }
+      }
     }
-    // state update
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int x = 0; x < 4; ++x) S[t][x] = o.gC * S[t][x] + acc[t][x] + o.bm[t][x];
     buf ^= 1;
   };
 
-  // Two register sets: the operands of the next chunk are in flight while
-  // the current one is computed (they do not depend on the state).
-  ChunkOps<T> A, B;
-  load_ops<T>(A, mats0 + (size_t)cb * mstride, gam + (size_t)cb * Nv + h, w, l, vcol);
+  // The ring of NSET register sets, unrolled so every set index is static.
 #pragma unroll 1
-  for (int c = cb; c < ce; c += 2) {
-    if (c + 1 < ce) load_ops<T>(B, mats0 + (size_t)(c + 1) * mstride, gam + (size_t)(c + 1) * Nv + h, w, l, vcol);
-    step(A, c);
-    if (c + 1 >= ce) break;
-    if (c + 2 < ce) load_ops<T>(A, mats0 + (size_t)(c + 2) * mstride, gam + (size_t)(c + 2) * Nv + h, w, l, vcol);
-    step(B, c + 1);
+  for (int c = cb; c < ce; c += NSET) {
+#pragma unroll
+    for (int k = 0; k < NSET; ++k)
+      if (c + k < ce) step(ops[k], ops[(k + DEPTH) % NSET], c + k);
   }
 
-  if (dstS) {
+  asm volatile("" ::"v"(sink));   // keeps the warming loads alive
+  if (state_wave && dstS) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t) put4<float>(dstS + sbase + 32 * w + 16 * t + 4 * (l >> 4), S[t]);
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+        *reinterpret_cast<f32x4*>(dstS + sb + (size_t)(v0 + 16 * t + r16) * kD + rb + 16 * i +
+                                  4 * q4) = st[i][t];
   }
 }
 
@@ -195,7 +293,7 @@ template <typename T>
 void launch_inter(const T* inter, const int4* table, const int32_t* choff, const float* gam,
                   const float* state_in, float* carry, float* state_out, int32_t N, int32_t Nv,
                   int32_t slot0, int32_t nseg, bool first_segment, T* out, hipStream_t stream) {
-  const unsigned blocks = (unsigned)N * (unsigned)Nv * 8u;
+  const unsigned blocks = (unsigned)N * (unsigned)Nv * (unsigned)(kD / kBV);
   hipLaunchKernelGGL(inter_kernel<T>, dim3(blocks), dim3(256), 0, stream, inter, table, choff, gam,
                      state_in, carry, state_out, N, Nv, slot0, nseg, first_segment ? 1 : 0, out);
 }

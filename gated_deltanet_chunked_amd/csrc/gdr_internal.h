@@ -15,13 +15,24 @@ namespace gdr {
 // most floor(T / 128) + N.
 inline int64_t max_slots(int64_t T, int64_t N) { return T / 128 + N; }
 
+// Upper bound on the chunk slots of one segment (the state pass stages a
+// segment's chunk table in LDS).
+constexpr int kMaxSegSlots = 2048;
+
 // Chunk slots processed per segment: the intra-chunk products of one segment
 // are written to the workspace and consumed by the state pass of the same
-// segment before the next segment reuses the buffer.
-inline int64_t segment_slots(int64_t nslots, int64_t Nv) {
-  (void)Nv;
-  const int64_t seg = 64;
-  return nslots <= seg + seg / 2 ? nslots : seg;
+// segment before the next segment reuses the buffer.  A segment's matrices
+// are kept to about 128 MiB (at most 1.5x that) so they stay in the 256 MB Infinity Cache between
+// the two kernels, and the slots are split evenly over the segments.
+inline int64_t segment_slots(int64_t nslots, int64_t Nv, int64_t elem_bytes) {
+  const int64_t per_slot = Nv * 4 * 128 * 128 * elem_bytes;
+  int64_t cap = (int64_t(128) << 20) / per_slot;
+  if (cap < 8) cap = 8;
+  int64_t nsegs = (nslots + cap / 2) / cap;   // nearest whole number of segments
+  if (nsegs < 1) nsegs = 1;
+  const int64_t most = (nslots + kMaxSegSlots - 1) / kMaxSegSlots;
+  if (nsegs < most) nsegs = most;
+  return (nslots + nsegs - 1) / nsegs;
 }
 
 // Per (chunk slot, value head): four 128x128 matrices of the chunk's affine

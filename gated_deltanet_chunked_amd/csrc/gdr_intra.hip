@@ -17,7 +17,7 @@
 //   Mt   = M'^T,  M' = -W^T K_dec = -K^T diag(beta exp(gc)) Z   [Dk x Dk]
 //   Qp   = Q_dec - P W = Q_dec - R diag(beta exp(gc)) K         [l x Dk]
 //   Bm   = U^T K_dec = V^T diag(beta) Z                         [Dv x Dk]
-//   OuT  = (P U)^T = (R diag(beta) V)^T                         [Dv x l]
+//   Ou   = P U = R diag(beta) V                                 [l x Dv]
 // leaving the chunk-serial pass (gdr_inter.hip) with
 //   O = Qp S^T + Ou,   S_next = exp(gc_last) S + S M' + Bm.
 //
@@ -31,6 +31,9 @@
 //   T^T       -> slot 0 (blocked inverse, below);  P -> slot 1
 //   R^T = T^T P^T;  Z = (T^T diag ck) K^T with K^T staged into slot 1
 //   Qp, Mt from K^T and (R, Z^T) scaled by beta exp(gc);  Ou, Bm from V^T
+// The four matrices go to the workspace in the order Mt, Qp, Bm, Ou, each in
+// the element order the state pass reads (frag_off, bm_off, ou_off in
+// gdr_device.h), so that pass loads them as contiguous blocks.
 // The triangular inverse follows the blog's subsection d in blocked form:
 // 16x16 diagonal blocks by substitution, then three doubling merges
 // [X Y; 0 Z]^-1 = [X^-1, -X^-1 Y Z^-1; 0, Z^-1] on the matrix cores (the
@@ -308,9 +311,31 @@ __device__ __forceinline__ void put_t(T* tile, const Acc (&acc)[4][4], int m0, i
     }
 }
 
-// Same from raw accumulators into a plain 128x128 row-major global matrix,
-// times sign.
-template <typename T>
+// Four values of row n, columns m..m+3 (m a multiple of 4), stored at
+// dst + off(n, m + x).  The pass layouts keep the four contiguous; the
+// operand layout does for bf16 (8 consecutive k per lane) but not for fp32.
+enum class Lay { Frag, Bm, Ou };
+template <typename T, Lay L>
+__device__ __forceinline__ int lay_off(int n, int m) {
+  if (L == Lay::Frag) return frag_off<T>(n, m);
+  if (L == Lay::Bm) return bm_off(n, m);
+  return ou_off(n, m);
+}
+template <typename T, Lay L>
+__device__ __forceinline__ void store4_lay(T* dst, int n, int m, float x0, float x1, float x2, float x3) {
+  if (L == Lay::Frag && sizeof(T) == 4) {
+    dst[lay_off<T, L>(n, m)] = from_f32<T>(x0);
+    dst[lay_off<T, L>(n, m + 1)] = from_f32<T>(x1);
+    dst[lay_off<T, L>(n, m + 2)] = from_f32<T>(x2);
+    dst[lay_off<T, L>(n, m + 3)] = from_f32<T>(x3);
+  } else {
+    store4<T>(dst + lay_off<T, L>(n, m), x0, x1, x2, x3);
+  }
+}
+
+// Transposed store of a wave's 64x64 accumulator block into a workspace
+// matrix: element (row n, column m) = sign * acc(m, n).
+template <typename T, Lay L>
 __device__ __forceinline__ void store_t_global(T* dst, const f32x4 (&acc)[4][4], int m0, int n0,
                                                float sign) {
   const int l = lane_id();
@@ -319,8 +344,8 @@ __device__ __forceinline__ void store_t_global(T* dst, const f32x4 (&acc)[4][4],
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int m = m0 + 16 * i + 4 * (l >> 4), n = n0 + 16 * j + (l & 15);
-      store4<T>(dst + n * kD + m, sign * acc[i][j][0], sign * acc[i][j][1], sign * acc[i][j][2],
-                sign * acc[i][j][3]);
+      store4_lay<T, L>(dst, n, m, sign * acc[i][j][0], sign * acc[i][j][1], sign * acc[i][j][2],
+                       sign * acc[i][j][3]);
     }
 }
 
@@ -529,8 +554,8 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(
         float x0 = 0.f, x1 = 0.f, x2 = 0.f, x3 = 0.f;
         if (r < len) load4<T>(qc + (size_t)r * qk_stride + d, x0, x1, x2, x3);
         const float qsr = s.qs[r];
-        store4<T>(qp + r * kD + d, qsr * x0 - acc[i][jj][0], qsr * x1 - acc[i][jj][1],
-                  qsr * x2 - acc[i][jj][2], qsr * x3 - acc[i][jj][3]);
+        store4_lay<T, Lay::Frag>(qp, r, d, qsr * x0 - acc[i][jj][0], qsr * x1 - acc[i][jj][1],
+                                 qsr * x2 - acc[i][jj][2], qsr * x3 - acc[i][jj][3]);
       }
   }
   __syncthreads();
@@ -544,7 +569,7 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(
     f32x4 acc[4][4];
     zero_acc(acc);
     sw_gemm64<T>(acc, s.t1, s.t0, m0, n0);
-    store_t_global<T>(dst + 0 * kD * kD, acc, m0, n0, -1.0f);
+    store_t_global<T, Lay::Frag>(dst + 0 * kD * kD, acc, m0, n0, -1.0f);
   }
   __syncthreads();
 
@@ -557,12 +582,12 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(
   put_t<T>(s.t0, Rp, m0, n0, s.beta);
   __syncthreads();
 
-  // ---- 14. Ou = R diag(beta) V:  acc[r][e] = sum_j (R beta)[r][j] V^T[e][j];  OuT[e][r]
+  // ---- 14. Ou = R diag(beta) V:  acc[e][r] = sum_j V^T[e][j] (R beta)[r][j];  Ou[r][e]
   {
     f32x4 acc[4][4];
     zero_acc(acc);
-    sw_gemm64<T>(acc, s.t0, s.t1, m0, n0);
-    store_t_global<T>(dst + 3 * kD * kD, acc, m0, n0, 1.0f);
+    sw_gemm64<T>(acc, s.t1, s.t0, m0, n0);
+    store_t_global<T, Lay::Ou>(dst + 3 * kD * kD, acc, m0, n0, 1.0f);
   }
   __syncthreads();
 
@@ -575,7 +600,7 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(
     f32x4 acc[4][4];
     zero_acc(acc);
     sw_gemm64<T>(acc, s.t0, s.t1, m0, n0);
-    store_t_global<T>(dst + 2 * kD * kD, acc, m0, n0, 1.0f);
+    store_t_global<T, Lay::Bm>(dst + 2 * kD * kD, acc, m0, n0, 1.0f);
   }
 }
 

@@ -33,7 +33,7 @@ gdr_status common_sizes(int32_t Nqk, int32_t Nv, int32_t D, gdr_dtype dtype, uin
 Workspace plan_workspace(int64_t T, int64_t N, int64_t Nqk, int64_t Nv, gdr_dtype dtype) {
   Workspace w{};
   w.nslots = max_slots(T, N);
-  w.seg_slots = segment_slots(w.nslots, Nv);
+  w.seg_slots = segment_slots(w.nslots, Nv, static_cast<int64_t>(dtype_size(dtype)));
   int64_t off = 0;
   w.table = off; off = align256(off + w.nslots * 4 * 4);
   w.choff = off; off = align256(off + (N + 1) * 4);
