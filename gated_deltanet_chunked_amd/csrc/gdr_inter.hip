@@ -22,6 +22,8 @@
 // chunks ahead into a ring of register sets.  Chunk boundaries restart at
 // sequence starts, so a varlen boundary inside a 128-token grid needs no
 // special case: a short last chunk only writes its first len output rows.
+#include <type_traits>
+
 #include "gdr_device.h"
 #include "gdr_internal.h"
 #include "gdr_kernels.h"
@@ -204,13 +206,16 @@ __global__ __launch_bounds__(256, 1) void inter_kernel(
 #pragma unroll
   for (int k = 0; k < NSET; ++k) ops[k].warm[0] = ops[k].warm[1] = 0u;
 #pragma unroll
-  for (int k = 0; k < DEPTH; ++k)
-    if (cb + k < ce) load_ops(ops[k], cb + k);
+  for (int k = 0; k < DEPTH; ++k) load_ops(ops[k], min(cb + k, ce - 1));
 
+  // One chunk of the pass for one wave role (STATE: state product and update;
+  // else output product and stores).  The two roles run as separate loops so
+  // each is straight-line code and the memory waits are counted exactly.
   int buf = 0;
-  auto step = [&](ChunkOps<T>& o, ChunkOps<T>& next, int c) {
+  auto step = [&](auto role, ChunkOps<T>& o, ChunkOps<T>& next, int c) {
+    constexpr bool STATE = decltype(role)::value;
     T* sbuf = sS[buf];
-    if (state_wave) {
+    if (STATE) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -226,26 +231,24 @@ __global__ __launch_bounds__(256, 1) void inter_kernel(
     for (int ks = 0; ks < KSTEPS; ++ks) {
       const auto s0 = sw_frag<T>(sbuf, r16, ks * Mma<T>::K + kq);
       const auto s1 = sw_frag<T>(sbuf, 16 + r16, ks * Mma<T>::K + kq);
-      if (state_wave) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < 4; ++i) {
+        if (STATE) {
           acc[i][0] = Mma<T>::mma(o.a[i][ks], s0, acc[i][0]);
           acc[i][1] = Mma<T>::mma(o.a[i][ks], s1, acc[i][1]);
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        } else {
           acc[i][0] = Mma<T>::mma(s0, o.a[i][ks], acc[i][0]);
           acc[i][1] = Mma<T>::mma(s1, o.a[i][ks], acc[i][1]);
         }
       }
     }
-    if (c + DEPTH < ce) load_ops(next, c + DEPTH);
+    // next operands: chunk c + DEPTH (clamped: past the end it reloads the
+    // last chunk, which keeps the loop free of branches)
+    load_ops(next, min(c + DEPTH, ce - 1));
     // the warming loads held in this set were issued NSET chunks ago
     sink ^= o.warm[0] ^ o.warm[1];
-    if (c + kWarmAhead < ce) warm(o, c + kWarmAhead);
-    else o.warm[0] = o.warm[1] = 0u;
-    if (state_wave) {
+    warm(o, min(c + kWarmAhead, ce - 1));
+    if (STATE) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -270,13 +273,21 @@ __global__ __launch_bounds__(256, 1) void inter_kernel(
     buf ^= 1;
   };
 
-  // The ring of NSET register sets, unrolled so every set index is static.
+  // The ring of NSET register sets, unrolled so every set index is static;
+  // whole groups of NSET chunks first, then the remainder.
+  auto chunk_loop = [&](auto role) {
+    int c = cb;
 #pragma unroll 1
-  for (int c = cb; c < ce; c += NSET) {
+    for (; c + NSET <= ce; c += NSET) {
 #pragma unroll
-    for (int k = 0; k < NSET; ++k)
-      if (c + k < ce) step(ops[k], ops[(k + DEPTH) % NSET], c + k);
-  }
+      for (int k = 0; k < NSET; ++k) step(role, ops[k], ops[(k + DEPTH) % NSET], c + k);
+    }
+#pragma unroll
+    for (int k = 0; k < NSET - 1; ++k)
+      if (c + k < ce) step(role, ops[k], ops[(k + DEPTH) % NSET], c + k);
+  };
+  if (state_wave) chunk_loop(std::true_type{});
+  else chunk_loop(std::false_type{});
 
   asm volatile("" ::"v"(sink));   // keeps the warming loads alive
   if (state_wave && dstS) {
