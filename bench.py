@@ -54,6 +54,27 @@ def alg_bytes_decode(N, Nqk, Nv, es=2):
     return state + qkv + gb + out
 
 
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from profiles/traffic.json (two rocprofv3
+    --pmc runs, FETCH_SIZE and WRITE_SIZE, scaled by what the same counters
+    read for a plain 512 MiB copy), or None when the kernel's sources have
+    changed since the counters were taken."""
+    import hashlib
+    here = os.path.dirname(os.path.abspath(__file__))
+    try:
+        with open(os.path.join(here, "profiles", "traffic.json")) as f:
+            rec = json.load(f)["kernels"][kernel]
+        h = hashlib.sha256()
+        for src in rec["sources"]:
+            with open(os.path.join(here, src), "rb") as f:
+                h.update(f.read())
+        if h.hexdigest() != rec["sha256"]:
+            return None
+        return int(rec["hbm_bytes"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -114,11 +135,16 @@ def main() -> int:
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     if args.copy_probe_mib > 0:
+        # a plain device-to-device copy of known size whose source is cold:
+        # 1 GiB written after the source pushes it out of the 256 MB
+        # Infinity Cache, so a byte counter sees the whole copy
         src = torch.ones(args.copy_probe_mib << 18, dtype=torch.float32, device=dev)
+        flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
+        torch.cuda.synchronize()
         dst.copy_(src)
         torch.cuda.synchronize()
-        del src, dst
+        del src, dst, flush
     for _ in range(args.warmup):
         step([])
     torch.cuda.synchronize()
@@ -158,7 +184,8 @@ def main() -> int:
     dom = max(per_step, key=per_step.get)
     if dom == "decode":
         roof = dict(kernel="decode", bound="hbm", achieved=round(dec_gbps, 1), peak=HBM_PEAK_GBPS,
-                    unit="GB/s", frac=round(dec_gbps / HBM_PEAK_GBPS, 4), traffic=None,
+                    unit="GB/s", frac=round(dec_gbps / HBM_PEAK_GBPS, 4),
+                    traffic=measured_traffic("decode"),
                     per_launch=f"{dec_bytes} algorithmic bytes")
     else:
         f_dom = {"intra": f_intra, "inter": f_inter}.get(dom, 0.0)
@@ -166,7 +193,8 @@ def main() -> int:
         per_launch_flops = f_dom / kstats[dom]["launches_per_call"]
         ach = per_launch_flops / (kstats[dom]["avg_ms"] * 1e-3) / 1e12
         roof = dict(kernel=dom, bound="mfma", achieved=round(ach, 2), peak=MFMA_PEAK_TFLOPS["bf16"],
-                    unit="TFLOP/s", frac=round(ach / MFMA_PEAK_TFLOPS["bf16"], 4), traffic=None,
+                    unit="TFLOP/s", frac=round(ach / MFMA_PEAK_TFLOPS["bf16"], 4),
+                    traffic=measured_traffic(dom) if args.workload == "prefill" else None,
                     per_launch=f"{per_launch_flops:.4g} algorithmic FLOP")
         del launches
 
