@@ -245,10 +245,21 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
+// Lane permutation within rows of 16 lanes by a DPP control (no LDS trip).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
+                                                               0xF, 0xF, false));
+}
+
 // Sum over aligned groups of 16 lanes; every lane of the group gets the total.
+// Butterfly on DPP: swap neighbours, swap pairs (quad sums), mirror within 8
+// (half-row sums), mirror within 16 (row sums).
 __device__ __forceinline__ float group16_sum(float x) {
-#pragma unroll
-  for (int off = 8; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+  x += dpp_f32<0xB1>(x);    // quad_perm [1,0,3,2]
+  x += dpp_f32<0x4E>(x);    // quad_perm [2,3,0,1]
+  x += dpp_f32<0x141>(x);   // row_half_mirror
+  x += dpp_f32<0x140>(x);   // row_mirror
   return x;
 }
 
