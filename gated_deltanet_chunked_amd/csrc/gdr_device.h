@@ -230,6 +230,51 @@ __device__ __forceinline__ int ou_off(int r, int v) {
          (v & 3);
 }
 
+// Fragment of a k-major swizzled 128-wide bf16 tile X (row index = k):
+// lane (i = lane & 15, q = lane >> 4) gets X[k0 + 8 q + e][o0 + i], e < 8,
+// from two LDS transpose reads (gfx950 ds_read_b64_tr_b16).  Within each
+// group of 16 lanes that instruction hands output lane 4a + b element b of
+// the 4 values read by lanes a, a + 4, a + 8 and a + 12, so lane s of the
+// group points at X[k0 + 8 q + s / 4][o0 + 4 (s % 4)] (4 values in one
+// 16-byte chunk of the tile).
+__device__ __forceinline__ bf16x8 sw_frag_tr(const __bf16* tile, int o0, int k0) {
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  const int l = lane_id(), sl = l & 15, q = l >> 4;
+  const int row = k0 + 8 * q + (sl >> 2), col = o0 + 4 * (sl & 3);
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16*)(tile + Sw<__bf16>::at(row, col)));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16*)(tile + Sw<__bf16>::at(row + 4, col)));
+  typedef short v8i16 __attribute__((ext_vector_type(8)));
+  const v8i16 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, both);
+}
+
+// sw_gemm64 with either operand read from a k-major tile (ATR / BTR) through
+// transpose reads; bf16 only.
+template <bool ATR, bool BTR>
+__device__ __forceinline__ void sw_gemm64_tr(f32x4 (&acc)[4][4], const __bf16* A, const __bf16* B,
+                                             int m0, int n0) {
+  typedef __bf16 T;
+  const int l = lane_id();
+  const int r = l & 15;
+  const int kq = (l >> 4) * Mma<T>::E;
+#pragma unroll 1
+  for (int k = 0; k < kD; k += Mma<T>::K) {
+    typename Mma<T>::frag a[4], b[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      a[i] = ATR ? sw_frag_tr(A, m0 + 16 * i, k) : sw_frag<T>(A, m0 + 16 * i + r, k + kq);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      b[j] = BTR ? sw_frag_tr(B, n0 + 16 * j, k) : sw_frag<T>(B, n0 + 16 * j + r, k + kq);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = Mma<T>::mma(a[i], b[j], acc[i][j]);
+  }
+}
+
 template <int M, int N>
 __device__ __forceinline__ void zero_acc(f32x4 (&acc)[M][N]) {
 #pragma unroll

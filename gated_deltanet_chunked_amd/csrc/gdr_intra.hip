@@ -116,19 +116,25 @@ struct RowPieces {
   static constexpr int CPR = kD / EPC;              // pieces per row
   static constexpr int N = kD * CPR / 256;          // pieces per thread
   u32x4 p[N];
+  // The thread index is made opaque in load and store so the compiler does
+  // not hold these addresses live from one staging to the next.
   __device__ __forceinline__ void load(const T* src, size_t gs, int len) {
+    int t = threadIdx.x;
+    asm volatile("" : "+v"(t));
 #pragma unroll
     for (int it = 0; it < N; ++it) {
-      const int idx = threadIdx.x + 256 * it;
+      const int idx = t + 256 * it;
       const int r = idx / CPR, c = (idx % CPR) * EPC;
       p[it] = u32x4{0u, 0u, 0u, 0u};
       if (r < len) p[it] = *reinterpret_cast<const u32x4*>(src + (size_t)r * gs + c);
     }
   }
   __device__ __forceinline__ void store(T* tile) const {
+    int t = threadIdx.x;
+    asm volatile("" : "+v"(t));
 #pragma unroll
     for (int it = 0; it < N; ++it) {
-      const int idx = threadIdx.x + 256 * it;
+      const int idx = t + 256 * it;
       const int r = idx / CPR, c = (idx % CPR) * EPC;
       *reinterpret_cast<u32x4*>(tile + Sw<T>::at(r, c)) = p[it];
     }
@@ -298,7 +304,8 @@ __device__ __forceinline__ void invert_unit_upper(IntraLds<T>& s) {
 // swizzled tile: tile[n][m..m+3] = acc(m.., n) * f[m..m+3] (f == nullptr: 1).
 template <typename T, typename Acc>
 __device__ __forceinline__ void put_t(T* tile, const Acc (&acc)[4][4], int m0, int n0, const float* f) {
-  const int l = lane_id();
+  int l = lane_id();
+  asm volatile("" : "+v"(l));   // recompute the addresses at every call
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -361,6 +368,9 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(
     int32_t Nqk, int32_t Nv, int32_t slot0, float scale, int norm, T* __restrict__ inter,
     float* __restrict__ gam_out) {
   __shared__ IntraLds<T> s;
+  // bf16 reads K^T and V^T straight from the row-major K and V tiles with
+  // LDS transpose reads; fp32 (no 32-bit transpose read) stages K^T and V^T
+  constexpr bool kTr = sizeof(T) == 2;
   const int local_slot = blockIdx.x, h = blockIdx.y;
   const int4 e = table[slot0 + local_slot];
   if (e.x < 0) return;
@@ -515,7 +525,13 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(
       *reinterpret_cast<u32x4*>(p) = raw;
     }
   }
-  {
+  // bf16: K rows as they are (coalesced loads), read transposed by the
+  // products below; fp32: K^T staged through registers
+  if constexpr (kTr) {
+    RowPieces<T> kn;
+    kn.load(kc, qk_stride, len);
+    kn.store(s.t1);
+  } else {
     ColPieces<T> kt;
     kt.load(kc, qk_stride, len);
     kt.store(s.t1);
@@ -527,7 +543,8 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(
   {
     f32x4 acc[4][4];
     zero_acc(acc);
-    sw_gemm64<T>(acc, s.t0, s.t1, m0, n0);
+    if constexpr (kTr) sw_gemm64_tr<false, true>(acc, s.t0, s.t1, m0, n0);
+    else sw_gemm64<T>(acc, s.t0, s.t1, m0, n0);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -543,7 +560,8 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(
   {
     f32x4 acc[4][4];
     zero_acc(acc);
-    sw_gemm64<T>(acc, s.t1, s.t0, m0, n0);
+    if constexpr (kTr) sw_gemm64_tr<true, false>(acc, s.t1, s.t0, m0, n0);
+    else sw_gemm64<T>(acc, s.t1, s.t0, m0, n0);
     T* qp = dst + 1 * kD * kD;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -568,13 +586,18 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(
   {
     f32x4 acc[4][4];
     zero_acc(acc);
-    sw_gemm64<T>(acc, s.t1, s.t0, m0, n0);
+    if constexpr (kTr) sw_gemm64_tr<true, false>(acc, s.t1, s.t0, m0, n0);
+    else sw_gemm64<T>(acc, s.t1, s.t0, m0, n0);
     store_t_global<T, Lay::Frag>(dst + 0 * kD * kD, acc, m0, n0, -1.0f);
   }
   __syncthreads();
 
   // ---- 13. V^T into slot 1; R diag(beta) into slot 0
-  {
+  if constexpr (kTr) {
+    RowPieces<T> vn;
+    vn.load(vc, v_stride, len);
+    vn.store(s.t1);
+  } else {
     ColPieces<T> vt;
     vt.load(vc, v_stride, len);
     vt.store(s.t1);
@@ -586,7 +609,8 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(
   {
     f32x4 acc[4][4];
     zero_acc(acc);
-    sw_gemm64<T>(acc, s.t1, s.t0, m0, n0);
+    if constexpr (kTr) sw_gemm64_tr<true, false>(acc, s.t1, s.t0, m0, n0);
+    else sw_gemm64<T>(acc, s.t1, s.t0, m0, n0);
     store_t_global<T, Lay::Ou>(dst + 3 * kD * kD, acc, m0, n0, 1.0f);
   }
   __syncthreads();
@@ -599,7 +623,8 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(
   {
     f32x4 acc[4][4];
     zero_acc(acc);
-    sw_gemm64<T>(acc, s.t0, s.t1, m0, n0);
+    if constexpr (kTr) sw_gemm64_tr<false, true>(acc, s.t0, s.t1, m0, n0);
+    else sw_gemm64<T>(acc, s.t0, s.t1, m0, n0);
     store_t_global<T, Lay::Bm>(dst + 2 * kD * kD, acc, m0, n0, 1.0f);
   }
 }
