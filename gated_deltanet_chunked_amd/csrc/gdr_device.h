@@ -73,7 +73,14 @@ template <> struct Mma<float> {
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
-__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+// Lane index, opaque to the optimiser: every use recomputes the addresses
+// derived from it instead of keeping them live across phases (and out of
+// loops), which keeps the register pressure of the long kernels down.
+__device__ __forceinline__ int lane_id() {
+  int l = threadIdx.x & 63;
+  asm volatile("" : "+v"(l));
+  return l;
+}
 
 // Operand view of a row-major matrix in memory (LDS or global):
 // element (r, c) = base[r * ld + c].  A GEMM reads operand A as (m, k) and

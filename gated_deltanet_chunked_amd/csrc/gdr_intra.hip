@@ -108,6 +108,25 @@ template <> struct Pack4<float> {
   __device__ __forceinline__ float get(int x) const { return v[x]; }
 };
 
+// Four consecutive elements of T loaded raw from global memory (or zeros).
+template <typename T> struct Quad4;
+template <> struct Quad4<__bf16> {
+  bf16x4 v;
+  __device__ __forceinline__ void load(const __bf16* p, bool ok) {
+    v = bf16x4{(__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f};
+    if (ok) v = *reinterpret_cast<const bf16x4*>(p);
+  }
+  __device__ __forceinline__ float get(int x) const { return (float)v[x]; }
+};
+template <> struct Quad4<float> {
+  f32x4 v;
+  __device__ __forceinline__ void load(const float* p, bool ok) {
+    v = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (ok) v = *reinterpret_cast<const f32x4*>(p);
+  }
+  __device__ __forceinline__ float get(int x) const { return v[x]; }
+};
+
 // Natural staging: rows [0, len) of a 128-wide global matrix (row stride gs
 // elements) into registers, 16 bytes per piece; rows >= len read as zero.
 template <typename T>
@@ -558,6 +577,16 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(
 
   // ---- 10. Qp = Q_dec - R diag(xk) K:  acc[d][r] = sum_j K^T[d][j] (R xk)[r][j]
   {
+    // q[r][d..d+3] in the layout of this product, loaded (raw) before it
+    Quad4<T> qx[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int d = m0 + 16 * i + 4 * (l >> 4);
+        const int r = n0 + 16 * jj + (l & 15);
+        qx[i][jj].load(qc + (size_t)r * qk_stride + d, r < len);
+      }
     f32x4 acc[4][4];
     zero_acc(acc);
     if constexpr (kTr) sw_gemm64_tr<true, false>(acc, s.t1, s.t0, m0, n0);
@@ -569,11 +598,11 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(
       for (int jj = 0; jj < 4; ++jj) {
         const int d = m0 + 16 * i + 4 * (l >> 4);
         const int r = n0 + 16 * jj + (l & 15);
-        float x0 = 0.f, x1 = 0.f, x2 = 0.f, x3 = 0.f;
-        if (r < len) load4<T>(qc + (size_t)r * qk_stride + d, x0, x1, x2, x3);
         const float qsr = s.qs[r];
-        store4_lay<T, Lay::Frag>(qp, r, d, qsr * x0 - acc[i][jj][0], qsr * x1 - acc[i][jj][1],
-                                 qsr * x2 - acc[i][jj][2], qsr * x3 - acc[i][jj][3]);
+        store4_lay<T, Lay::Frag>(qp, r, d, qsr * qx[i][jj].get(0) - acc[i][jj][0],
+                                 qsr * qx[i][jj].get(1) - acc[i][jj][1],
+                                 qsr * qx[i][jj].get(2) - acc[i][jj][2],
+                                 qsr * qx[i][jj].get(3) - acc[i][jj][3]);
       }
   }
   __syncthreads();
@@ -581,6 +610,12 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(
   // ---- 11. Z^T diag(xk) into slot 0:  t0[d][j] = Z[j][d] xk_j
   put_t<T>(s.t0, Zp, m0, n0, s.xk);
   __syncthreads();
+
+  // bf16: the V rows are loaded before the Mt product and staged after it
+  // (their loads then overlap that product instead of waiting behind the
+  // output stores)
+  RowPieces<T> vn;
+  if constexpr (kTr) vn.load(vc, v_stride, len);
 
   // ---- 12. M' = -K^T diag(xk) Z:  acc[e][d] = sum_j K^T[e][j] (Z^T xk)[d][j];  Mt[d][e] = -acc
   {
@@ -594,8 +629,6 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(
 
   // ---- 13. V^T into slot 1; R diag(beta) into slot 0
   if constexpr (kTr) {
-    RowPieces<T> vn;
-    vn.load(vc, v_stride, len);
     vn.store(s.t1);
   } else {
     ColPieces<T> vt;
