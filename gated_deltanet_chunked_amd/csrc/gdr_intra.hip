@@ -108,27 +108,34 @@ template <> struct Pack4<float> {
   __device__ __forceinline__ float get(int x) const { return v[x]; }
 };
 
-// Four consecutive elements of T loaded raw from global memory (or zeros).
+// Global loads of padded rows.  A chunk's rows past its length are read
+// from a clamped, valid row and then replaced by zeros with a select: a load
+// under a branch would be waited for inside the branch, serialising every
+// load of a staging loop behind the previous one.
+
+// Four consecutive elements of T loaded raw from global memory; zeros when
+// !ok (p must still be a valid address).
 template <typename T> struct Quad4;
 template <> struct Quad4<__bf16> {
   bf16x4 v;
   __device__ __forceinline__ void load(const __bf16* p, bool ok) {
-    v = bf16x4{(__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f};
-    if (ok) v = *reinterpret_cast<const bf16x4*>(p);
+    const bf16x4 x = *reinterpret_cast<const bf16x4*>(p);
+    v = ok ? x : bf16x4{(__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f};
   }
   __device__ __forceinline__ float get(int x) const { return (float)v[x]; }
 };
 template <> struct Quad4<float> {
   f32x4 v;
   __device__ __forceinline__ void load(const float* p, bool ok) {
-    v = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (ok) v = *reinterpret_cast<const f32x4*>(p);
+    const f32x4 x = *reinterpret_cast<const f32x4*>(p);
+    v = ok ? x : f32x4{0.f, 0.f, 0.f, 0.f};
   }
   __device__ __forceinline__ float get(int x) const { return v[x]; }
 };
 
 // Natural staging: rows [0, len) of a 128-wide global matrix (row stride gs
-// elements) into registers, 16 bytes per piece; rows >= len read as zero.
+// elements) into registers, 16 bytes per piece; rows >= len read as zero
+// (len >= 1).
 template <typename T>
 struct RowPieces {
   static constexpr int EPC = 16 / (int)sizeof(T);
@@ -144,8 +151,8 @@ struct RowPieces {
     for (int it = 0; it < N; ++it) {
       const int idx = t + 256 * it;
       const int r = idx / CPR, c = (idx % CPR) * EPC;
-      p[it] = u32x4{0u, 0u, 0u, 0u};
-      if (r < len) p[it] = *reinterpret_cast<const u32x4*>(src + (size_t)r * gs + c);
+      const u32x4 x = *reinterpret_cast<const u32x4*>(src + (size_t)min(r, len - 1) * gs + c);
+      p[it] = r < len ? x : u32x4{0u, 0u, 0u, 0u};
     }
   }
   __device__ __forceinline__ void store(T* tile) const {
@@ -190,9 +197,10 @@ template <> struct ColPieces<__bf16> {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int c = 8 * (w + 4 * u);
-      a[u] = b[u] = u32x4{0u, 0u, 0u, 0u};
-      if (2 * p < len) a[u] = *reinterpret_cast<const u32x4*>(src + (size_t)(2 * p) * gs + c);
-      if (2 * p + 1 < len) b[u] = *reinterpret_cast<const u32x4*>(src + (size_t)(2 * p + 1) * gs + c);
+      const u32x4 x = *reinterpret_cast<const u32x4*>(src + (size_t)min(2 * p, len - 1) * gs + c);
+      const u32x4 y = *reinterpret_cast<const u32x4*>(src + (size_t)min(2 * p + 1, len - 1) * gs + c);
+      a[u] = 2 * p < len ? x : u32x4{0u, 0u, 0u, 0u};
+      b[u] = 2 * p + 1 < len ? y : u32x4{0u, 0u, 0u, 0u};
     }
   }
   __device__ __forceinline__ void store(__bf16* tile) const {
@@ -223,8 +231,8 @@ template <> struct ColPieces<float> {
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
       const int c = 4 * (w + 4 * (u >> 1)), i = l + 64 * (u & 1);
-      a[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (i < len) a[u] = *reinterpret_cast<const f32x4*>(src + (size_t)i * gs + c);
+      const f32x4 x = *reinterpret_cast<const f32x4*>(src + (size_t)min(i, len - 1) * gs + c);
+      a[u] = i < len ? x : f32x4{0.f, 0.f, 0.f, 0.f};
     }
   }
   __device__ __forceinline__ void store(float* tile) const {
@@ -415,8 +423,10 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(
   float bt = 0.0f;
   if (tid < 128) {
     const bool ok = tid < len;
-    gsum = ok ? (double)g[(size_t)(start + tid) * Nv + h] : 0.0;
-    bt = ok ? beta[(size_t)(start + tid) * Nv + h] : 0.0f;
+    const size_t gi = (size_t)(start + min(tid, len - 1)) * Nv + h;
+    const float gv = g[gi], bv = beta[gi];
+    gsum = ok ? (double)gv : 0.0;
+    bt = ok ? bv : 0.0f;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const double y = __shfl_up(gsum, off, 64);
@@ -585,7 +595,7 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(
       for (int jj = 0; jj < 4; ++jj) {
         const int d = m0 + 16 * i + 4 * (l >> 4);
         const int r = n0 + 16 * jj + (l & 15);
-        qx[i][jj].load(qc + (size_t)r * qk_stride + d, r < len);
+        qx[i][jj].load(qc + (size_t)min(r, len - 1) * qk_stride + d, r < len);
       }
     f32x4 acc[4][4];
     zero_acc(acc);
