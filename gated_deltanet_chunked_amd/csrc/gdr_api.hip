@@ -77,7 +77,7 @@ gdr_status dispatch_chunk(const ChunkArgs& a, hipStream_t st, Recorder& rec) {
 
 extern "C" size_t gdr_chunk_fwd_workspace_size(int32_t T, int32_t N, int32_t Nqk, int32_t Nv,
                                                int32_t D, gdr_dtype dtype) {
-  if (T < 0 || N < 1 || Nqk < 1 || Nv < 1 || Nv % Nqk != 0 || D != 128) return 0;
+  if (T < 0 || N < 1 || Nqk < 1 || Nv < 1 || Nv > kMaxNv || Nv % Nqk != 0 || D != 128) return 0;
   if (dtype != GDR_F32 && dtype != GDR_BF16) return 0;
   if (static_cast<int64_t>(T) * Nv > (int64_t(1) << 40)) return 0;
   return static_cast<size_t>(plan_workspace(T, N, Nqk, Nv, dtype).total);

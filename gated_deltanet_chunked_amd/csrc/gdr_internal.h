@@ -19,6 +19,11 @@ inline int64_t max_slots(int64_t T, int64_t N) { return T / 128 + N; }
 // segment's chunk table in LDS).
 constexpr int kMaxSegSlots = 2048;
 
+// Largest number of value heads.  It keeps the 128 rows of a chunk of v (row
+// stride Nv * 128 elements of at most 4 bytes) within 2 GiB, so the kernels
+// address a chunk's rows with 32-bit byte offsets from a per-chunk base.
+constexpr int32_t kMaxNv = 32768;
+
 // Chunk slots processed per segment: the intra-chunk products of one segment
 // are written to the workspace and consumed by the state pass of the same
 // segment before the next segment reuses the buffer.  A segment's matrices

@@ -29,8 +29,13 @@
 //   N = A+^T  -> slot 0; P stays in registers; slot 1 holds the lower
 //                triangular inverse as it is built
 //   T^T       -> slot 0 (blocked inverse, below);  P -> slot 1
-//   R^T = T^T P^T;  Z = (T^T diag ck) K^T with K^T staged into slot 1
-//   Qp, Mt from K^T and (R, Z^T) scaled by beta exp(gc);  Ou, Bm from V^T
+//   R^T = T^T P^T;  Z = (T^T diag ck) K^T with K staged into slot 1
+//   K's rows scaled by xk = beta exp(gc) rk in place; R, then Z^T, into
+//   slot 0:  Qp from (R, xk K), Mt from (xk K, Z^T)
+//   V's rows scaled by beta into slot 1:  Bm from (Z^T, beta V), then R
+//   into slot 0 again:  Ou from (R, beta V)
+// so R and Z leave registers for LDS unscaled, and Z's registers are free
+// from the Mt product on.
 // The four matrices go to the workspace in the order Mt, Qp, Bm, Ou, each in
 // the element order the state pass reads (frag_off, bm_off, ou_off in
 // gdr_device.h), so that pass loads them as contiguous blocks.
@@ -65,6 +70,10 @@ struct IntraLds {
   float qs[128];      // exp(gc_i) rq_i
   double part;        // wave 0's cumsum total
 };
+// 16-byte vector reads of four consecutive rows of gc, beta, rk
+static_assert(offsetof(IntraLds<__bf16>, gc) % 16 == 0 && offsetof(IntraLds<float>, gc) % 16 == 0);
+static_assert(offsetof(IntraLds<__bf16>, beta) % 16 == 0 && offsetof(IntraLds<float>, beta) % 16 == 0);
+static_assert(offsetof(IntraLds<__bf16>, rk) % 16 == 0 && offsetof(IntraLds<float>, rk) % 16 == 0);
 
 // 4-element vector store of fp32 values converted to T.
 template <typename T>
@@ -107,6 +116,16 @@ template <> struct Pack4<float> {
   __device__ __forceinline__ void set(const f32x4& a) { v = a; }
   __device__ __forceinline__ float get(int x) const { return v[x]; }
 };
+
+// Element (r, c) of a row-major chunk with row stride gs elements, addressed
+// with a 32-bit byte offset from the chunk's (workgroup-uniform) base, so a
+// load needs one address register.  The host limits head counts so that
+// 128 rows of any input span less than 2 GiB.
+template <typename T>
+__device__ __forceinline__ const T* at_row(const T* base, int r, size_t gs, int c) {
+  const uint32_t off = ((uint32_t)r * (uint32_t)gs + (uint32_t)c) * (uint32_t)sizeof(T);
+  return reinterpret_cast<const T*>(reinterpret_cast<const char*>(base) + off);
+}
 
 // Global loads of padded rows.  A chunk's rows past its length are read
 // from a clamped, valid row and then replaced by zeros with a select: a load
@@ -151,7 +170,7 @@ struct RowPieces {
     for (int it = 0; it < N; ++it) {
       const int idx = t + 256 * it;
       const int r = idx / CPR, c = (idx % CPR) * EPC;
-      const u32x4 x = *reinterpret_cast<const u32x4*>(src + (size_t)min(r, len - 1) * gs + c);
+      const u32x4 x = *reinterpret_cast<const u32x4*>(at_row(src, min(r, len - 1), gs, c));
       p[it] = r < len ? x : u32x4{0u, 0u, 0u, 0u};
     }
   }
@@ -165,6 +184,22 @@ struct RowPieces {
       *reinterpret_cast<u32x4*>(tile + Sw<T>::at(r, c)) = p[it];
     }
   }
+  // store with row r of the tile scaled by f[r]
+  __device__ __forceinline__ void store_scaled(T* tile, const float* f) const {
+    int t = threadIdx.x;
+    asm volatile("" : "+v"(t));
+#pragma unroll
+    for (int it = 0; it < N; ++it) {
+      const int idx = t + 256 * it;
+      const int r = idx / CPR, c = (idx % CPR) * EPC;
+      const float fr = f[r];
+      u32x4 raw = p[it];
+      T* e = reinterpret_cast<T*>(&raw);
+#pragma unroll
+      for (int x = 0; x < EPC; ++x) e[x] = from_f32<T>(to_f32(e[x]) * fr);
+      *reinterpret_cast<u32x4*>(tile + Sw<T>::at(r, c)) = raw;
+    }
+  }
   // sum of squares of the piece's elements
   __device__ __forceinline__ float sumsq(int it) const {
     const T* e = reinterpret_cast<const T*>(&p[it]);
@@ -175,11 +210,12 @@ struct RowPieces {
   }
 };
 
-// Sum over aligned groups of CPR lanes (CPR = 16 or 32).
+// Sum over aligned groups of CPR lanes (CPR = 16 or 32), on DPP within
+// each 16-lane row (no LDS round trip), one lane swap across row pairs.
 template <int CPR>
 __device__ __forceinline__ float row_sum(float x) {
-#pragma unroll
-  for (int off = CPR / 2; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+  x = group16_sum(x);
+  if constexpr (CPR == 32) x += __shfl_xor(x, 16, 64);
   return x;
 }
 
@@ -235,15 +271,17 @@ template <> struct ColPieces<float> {
       a[u] = i < len ? x : f32x4{0.f, 0.f, 0.f, 0.f};
     }
   }
-  __device__ __forceinline__ void store(float* tile) const {
+  // tile[d][i] = src[i][d] * f[i] (f == nullptr: 1)
+  __device__ __forceinline__ void store(float* tile, const float* f = nullptr) const {
     int t = threadIdx.x;
     asm volatile("" : "+v"(t));
     const int w = t >> 6, l = t & 63;
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
       const int c = 4 * (w + 4 * (u >> 1)), i = l + 64 * (u & 1);
+      const float fi = f ? f[i] : 1.0f;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) tile[Sw<float>::at(c + e, i)] = a[u][e];
+      for (int e = 0; e < 4; ++e) tile[Sw<float>::at(c + e, i)] = a[u][e] * fi;
     }
   }
 };
@@ -273,8 +311,8 @@ template <typename T>
 __device__ __forceinline__ void invert_unit_upper(IntraLds<T>& s) {
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   // 1) 16x16 diagonal blocks by back substitution, one column per thread:
-  //    x_i = delta_ic - sum_{m > i} N[i][m] x_m.  The 16 threads of a block
-  //    are lanes of one wave, so every read of N precedes every write.
+  //    x_i = delta_ic - sum_{m > i} N[i][m] x_m, then the block is
+  //    overwritten in place.  The 16 threads of a block are lanes of one wave.
   if (tid < 128) {
     const int b0 = 16 * (tid >> 4), c = tid & 15;
     float col[16];
@@ -287,6 +325,10 @@ __device__ __forceinline__ void invert_unit_upper(IntraLds<T>& s) {
       for (int m = i + 1; m < 16; ++m) acc += to_f32(s.t0[Sw<T>::at(b0 + i, b0 + m)]) * col[m];
       if (i < c) col[i] = -acc;
     }
+    // every lane's reads of the block come before any lane's writes: the
+    // wave issues its LDS accesses in order, and this barrier keeps the
+    // compiler from moving the writes above the reads
+    __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int i = 0; i < 16; ++i) s.t0[Sw<T>::at(b0 + i, b0 + c)] = from_f32<T>(col[i]);
     // row c of the lower form is column c of the upper form
@@ -324,6 +366,27 @@ __device__ __forceinline__ void invert_unit_upper(IntraLds<T>& s) {
       if (sz < 64) store4<T>(s.t1 + Sw<T>::at(j0, i0), -acc[0], -acc[1], -acc[2], -acc[3]);
     }
     __syncthreads();
+  }
+}
+
+// In-place scaling of a 128x128 swizzled tile: element (r, c) times f[r]
+// (ROWS) or f[c].
+template <typename T, bool ROWS>
+__device__ __forceinline__ void scale_tile(T* tile, const float* f) {
+  constexpr int EPC = 16 / (int)sizeof(T);
+  constexpr int NP = kD * kD / EPC / 256;
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+#pragma unroll
+  for (int it = 0; it < NP; ++it) {
+    const int idx = t + 256 * it;
+    const int r = idx / (kD / EPC), c = (idx % (kD / EPC)) * EPC;
+    T* p = tile + Sw<T>::at(r, c);
+    u32x4 raw = *reinterpret_cast<const u32x4*>(p);
+    T* ev = reinterpret_cast<T*>(&raw);
+#pragma unroll
+    for (int x = 0; x < EPC; ++x) ev[x] = from_f32<T>(to_f32(ev[x]) * (ROWS ? f[r] : f[c + x]));
+    *reinterpret_cast<u32x4*>(p) = raw;
   }
 }
 
@@ -470,25 +533,40 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(
   // diagonal and Gamma[c][a] above it (gc is non-increasing for g <= 0).
   //   N[c][a]  = beta_a rk_a rk_c Gamma[a][c] G1[a][c]   (c < a)  -> slot 0
   //   P[r][i]  = rq_r rk_i Gamma[r][i] G2[i][r]          (i <= r) -> registers
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
+  // The row and column scalars of a lane are read once, rows as vectors
+  // (4 consecutive rows a..a+3), before the element loop.
+  {
+    double gcc[4];
+    float rkc[4], rqc[4];
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
-      const int a = m0 + 16 * i + 4 * (l >> 4);
       const int c = n0 + 16 * jj + (l & 15);
-      const double gcc = s.gc[c];
-      const float rkc = s.rk[c], rqc = s.rq[c];
-      float nv[4];
-#pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        const int ax = a + x;
-        const float ex = __expf(-(float)fabs(s.gc[ax] - gcc));
-        const float rka = s.rk[ax];
-        nv[x] = (c < ax) ? s.beta[ax] * rka * rkc * ex * a1[i][jj][x] : 0.0f;
-        a2[i][jj][x] = (ax <= c) ? rqc * rka * ex * a2[i][jj][x] : 0.0f;
-      }
-      store4<T>(s.t0 + Sw<T>::at(c, a), nv[0], nv[1], nv[2], nv[3]);
+      gcc[jj] = s.gc[c];
+      rkc[jj] = s.rk[c];
+      rqc[jj] = s.rq[c];
     }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int a = m0 + 16 * i + 4 * (l >> 4);
+      const double2 g01 = *reinterpret_cast<const double2*>(&s.gc[a]);
+      const double2 g23 = *reinterpret_cast<const double2*>(&s.gc[a + 2]);
+      const f32x4 rka = *reinterpret_cast<const f32x4*>(&s.rk[a]);
+      const f32x4 bta = *reinterpret_cast<const f32x4*>(&s.beta[a]);
+      const double ga[4] = {g01.x, g01.y, g23.x, g23.y};
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int c = n0 + 16 * jj + (l & 15);
+        float nv[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const float ex = __expf(-(float)fabs(ga[x] - gcc[jj]));
+          nv[x] = (c < a + x) ? bta[x] * rka[x] * rkc[jj] * ex * a1[i][jj][x] : 0.0f;
+          a2[i][jj][x] = (a + x <= c) ? rqc[jj] * rka[x] * ex * a2[i][jj][x] : 0.0f;
+        }
+        store4<T>(s.t0 + Sw<T>::at(c, a), nv[0], nv[1], nv[2], nv[3]);
+      }
+    }
+  }
   // zero slot 1: the lower form of the inverse is built into it
   {
     constexpr int NZ = kD * kD * (int)sizeof(T) / 16 / 256;
@@ -507,6 +585,11 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(
     if (r == 0) gam_out[(size_t)(slot0 + local_slot) * Nv + h] = __expf((float)glast);
   }
   __syncthreads();
+
+  // bf16: the K rows that phase 7 stages again are loaded here, so the
+  // inverse hides their latency (no stores are outstanding yet)
+  RowPieces<T> kn;
+  if constexpr (kTr) kn.load(kc, qk_stride, len);
 
   // ---- 4. T^T = (I + A+^T)^-1 in slot 0
   invert_unit_upper<T>(s);
@@ -539,26 +622,10 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(
   __syncthreads();
 
   // ---- 7. T^T diag(ck) in place; K^T into slot 1
-  {
-    constexpr int EPC = 16 / (int)sizeof(T);
-    constexpr int NP = kD * kD / EPC / 256;
-#pragma unroll
-    for (int it = 0; it < NP; ++it) {
-      const int idx = tid + 256 * it;
-      const int r = idx / (kD / EPC), c = (idx % (kD / EPC)) * EPC;
-      T* p = s.t0 + Sw<T>::at(r, c);
-      u32x4 raw = *reinterpret_cast<const u32x4*>(p);
-      T* ev = reinterpret_cast<T*>(&raw);
-#pragma unroll
-      for (int x = 0; x < EPC; ++x) ev[x] = from_f32<T>(to_f32(ev[x]) * s.ck[c + x]);
-      *reinterpret_cast<u32x4*>(p) = raw;
-    }
-  }
+  scale_tile<T, false>(s.t0, s.ck);
   // bf16: K rows as they are (coalesced loads), read transposed by the
   // products below; fp32: K^T staged through registers
   if constexpr (kTr) {
-    RowPieces<T> kn;
-    kn.load(kc, qk_stride, len);
     kn.store(s.t1);
   } else {
     ColPieces<T> kt;
@@ -581,13 +648,20 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(
   }
   __syncthreads();
 
-  // ---- 9. R diag(xk) into slot 0:  t0[r][j] = R[r][j] xk_j
-  put_t<T>(s.t0, Rp, m0, n0, s.xk);
+  // ---- 9. K rows scaled by xk in slot 1, in place (both products with K
+  // take diag(xk) on the same side); R into slot 0
+  scale_tile<T, kTr>(s.t1, s.xk);   // bf16: rows of K; fp32: columns of K^T
+  put_t<T>(s.t0, Rp, m0, n0, nullptr);
   __syncthreads();
 
-  // ---- 10. Qp = Q_dec - R diag(xk) K:  acc[d][r] = sum_j K^T[d][j] (R xk)[r][j]
+  // ---- 10. Qp = Q_dec - R (xk K):  acc[d][r] = sum_j (xk K)^T[d][j] R[r][j]
+  RowPieces<T> vn;
   {
-    // q[r][d..d+3] in the layout of this product, loaded (raw) before it
+    f32x4 acc[4][4];
+    zero_acc(acc);
+    if constexpr (kTr) sw_gemm64_tr<true, false>(acc, s.t1, s.t0, m0, n0);
+    else sw_gemm64<T>(acc, s.t1, s.t0, m0, n0);
+    // q[r][d..d+3] in the layout of this product
     Quad4<T> qx[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -595,12 +669,23 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(
       for (int jj = 0; jj < 4; ++jj) {
         const int d = m0 + 16 * i + 4 * (l >> 4);
         const int r = n0 + 16 * jj + (l & 15);
-        qx[i][jj].load(qc + (size_t)min(r, len - 1) * qk_stride + d, r < len);
+        qx[i][jj].load(at_row(qc, min(r, len - 1), qk_stride, d), r < len);
       }
-    f32x4 acc[4][4];
-    zero_acc(acc);
-    if constexpr (kTr) sw_gemm64_tr<true, false>(acc, s.t1, s.t0, m0, n0);
-    else sw_gemm64<T>(acc, s.t1, s.t0, m0, n0);
+    Pack4<T> res[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const float qsr = s.qs[n0 + 16 * jj + (l & 15)];
+        res[i][jj].set(f32x4{qsr * qx[i][jj].get(0) - acc[i][jj][0],
+                             qsr * qx[i][jj].get(1) - acc[i][jj][1],
+                             qsr * qx[i][jj].get(2) - acc[i][jj][2],
+                             qsr * qx[i][jj].get(3) - acc[i][jj][3]});
+      }
+    // bf16: the V rows staged in phase 13 are loaded between the product and
+    // its stores: a wave's memory counter retires in order, so loads issued
+    // after the stores would wait for them
+    if constexpr (kTr) vn.load(vc, v_stride, len);
     T* qp = dst + 1 * kD * kD;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -608,26 +693,17 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(
       for (int jj = 0; jj < 4; ++jj) {
         const int d = m0 + 16 * i + 4 * (l >> 4);
         const int r = n0 + 16 * jj + (l & 15);
-        const float qsr = s.qs[r];
-        store4_lay<T, Lay::Frag>(qp, r, d, qsr * qx[i][jj].get(0) - acc[i][jj][0],
-                                 qsr * qx[i][jj].get(1) - acc[i][jj][1],
-                                 qsr * qx[i][jj].get(2) - acc[i][jj][2],
-                                 qsr * qx[i][jj].get(3) - acc[i][jj][3]);
+        store4_lay<T, Lay::Frag>(qp, r, d, res[i][jj].get(0), res[i][jj].get(1), res[i][jj].get(2),
+                                 res[i][jj].get(3));
       }
   }
   __syncthreads();
 
-  // ---- 11. Z^T diag(xk) into slot 0:  t0[d][j] = Z[j][d] xk_j
-  put_t<T>(s.t0, Zp, m0, n0, s.xk);
+  // ---- 11. Z^T into slot 0:  t0[d][j] = Z[j][d]
+  put_t<T>(s.t0, Zp, m0, n0, nullptr);
   __syncthreads();
 
-  // bf16: the V rows are loaded before the Mt product and staged after it
-  // (their loads then overlap that product instead of waiting behind the
-  // output stores)
-  RowPieces<T> vn;
-  if constexpr (kTr) vn.load(vc, v_stride, len);
-
-  // ---- 12. M' = -K^T diag(xk) Z:  acc[e][d] = sum_j K^T[e][j] (Z^T xk)[d][j];  Mt[d][e] = -acc
+  // ---- 12. M' = -(xk K)^T Z:  acc[e][d] = sum_j (xk K)^T[e][j] Z^T[d][j];  Mt[d][e] = -acc
   {
     f32x4 acc[4][4];
     zero_acc(acc);
@@ -637,38 +713,37 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(
   }
   __syncthreads();
 
-  // ---- 13. V^T into slot 1; R diag(beta) into slot 0
+  // ---- 13. V rows scaled by beta into slot 1 (Z^T stays in slot 0)
   if constexpr (kTr) {
-    vn.store(s.t1);
+    vn.store_scaled(s.t1, s.beta);
   } else {
     ColPieces<T> vt;
     vt.load(vc, v_stride, len);
-    vt.store(s.t1);
-  }
-  put_t<T>(s.t0, Rp, m0, n0, s.beta);
-  __syncthreads();
-
-  // ---- 14. Ou = R diag(beta) V:  acc[e][r] = sum_j V^T[e][j] (R beta)[r][j];  Ou[r][e]
-  {
-    f32x4 acc[4][4];
-    zero_acc(acc);
-    if constexpr (kTr) sw_gemm64_tr<true, false>(acc, s.t1, s.t0, m0, n0);
-    else sw_gemm64<T>(acc, s.t1, s.t0, m0, n0);
-    store_t_global<T, Lay::Ou>(dst + 3 * kD * kD, acc, m0, n0, 1.0f);
+    vt.store(s.t1, s.beta);
   }
   __syncthreads();
 
-  // ---- 15. Z^T diag(beta) into slot 0
-  put_t<T>(s.t0, Zp, m0, n0, s.beta);
-  __syncthreads();
-
-  // ---- 16. Bm = V^T diag(beta) Z:  acc[d][e] = sum_j (Z^T beta)[d][j] V^T[e][j];  Bm[e][d]
+  // ---- 14. Bm = (beta V)^T Z:  acc[d][e] = sum_j Z^T[d][j] (beta V)^T[e][j];  Bm[e][d]
   {
     f32x4 acc[4][4];
     zero_acc(acc);
     if constexpr (kTr) sw_gemm64_tr<false, true>(acc, s.t0, s.t1, m0, n0);
     else sw_gemm64<T>(acc, s.t0, s.t1, m0, n0);
     store_t_global<T, Lay::Bm>(dst + 2 * kD * kD, acc, m0, n0, 1.0f);
+  }
+  __syncthreads();
+
+  // ---- 15. R into slot 0
+  put_t<T>(s.t0, Rp, m0, n0, nullptr);
+  __syncthreads();
+
+  // ---- 16. Ou = R (beta V):  acc[e][r] = sum_j (beta V)^T[e][j] R[r][j];  Ou[r][e]
+  {
+    f32x4 acc[4][4];
+    zero_acc(acc);
+    if constexpr (kTr) sw_gemm64_tr<true, false>(acc, s.t1, s.t0, m0, n0);
+    else sw_gemm64<T>(acc, s.t1, s.t0, m0, n0);
+    store_t_global<T, Lay::Ou>(dst + 3 * kD * kD, acc, m0, n0, 1.0f);
   }
 }
 

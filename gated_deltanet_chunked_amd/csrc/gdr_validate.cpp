@@ -21,7 +21,7 @@ bool overlap(const void* p, int64_t n, const void* q, int64_t m) {
 }
 
 gdr_status common_sizes(int32_t Nqk, int32_t Nv, int32_t D, gdr_dtype dtype, uint32_t flags) {
-  if (D != 128) return GDR_ERR_UNSUPPORTED;
+  if (D != 128 || Nv > kMaxNv) return GDR_ERR_UNSUPPORTED;
   if (dtype != GDR_F32 && dtype != GDR_BF16) return GDR_ERR_UNSUPPORTED;
   if (flags & ~kKnownFlags) return GDR_ERR_UNSUPPORTED;
   if (Nqk <= 0 || Nv <= 0 || Nv % Nqk != 0) return GDR_ERR_INVALID_ARGUMENT;

@@ -26,7 +26,8 @@
  *     global state, so calls on different streams may run concurrently as long
  *     as their buffers do not overlap.
  *   - D (= Dk = Dv) must be 128; Nv must be a multiple of Nqk (operator page,
- *     parameter constraints).
+ *     parameter constraints) and at most 32768 (GDR_ERR_UNSUPPORTED beyond,
+ *     so that a chunk's rows span less than 2 GiB of any input).
  *   - `dtype` is the storage type of q, k, v and out.  g, beta and the states
  *     are always float32.  Arithmetic accumulates in float32; bf16 inputs are
  *     multiplied on bf16 matrix cores, f32 inputs on f32 matrix cores.
@@ -51,7 +52,7 @@ typedef enum { GDR_F32 = 0, GDR_BF16 = 1 } gdr_dtype;
 typedef enum {
     GDR_OK = 0,
     GDR_ERR_INVALID_ARGUMENT = -1,   /* bad size, null pointer, misalignment, ... */
-    GDR_ERR_UNSUPPORTED = -2,        /* D != 128, unknown dtype or flag */
+    GDR_ERR_UNSUPPORTED = -2,        /* D != 128, Nv > 32768, unknown dtype or flag */
     GDR_ERR_WORKSPACE_TOO_SMALL = -3,
     GDR_ERR_HIP = -4                 /* a HIP runtime call or launch failed */
 } gdr_status;

@@ -57,6 +57,7 @@ def test_workspace_size():
     assert lib.gdr_chunk_fwd_workspace_size(512, 0, 2, 4, 128, 0) == 0  # N < 1
     assert lib.gdr_chunk_fwd_workspace_size(-1, 1, 2, 4, 128, 0) == 0
     assert lib.gdr_chunk_fwd_workspace_size(512, 1, 2, 4, 128, 5) == 0  # dtype
+    assert lib.gdr_chunk_fwd_workspace_size(512, 1, 1, 65536, 128, 0) == 0  # Nv > 32768
     # bounded by the segment buffer: grows slowly with T
     assert ws(1 << 20, 1, 16, 32, gdr.GDR_BF16) < 2 * ws(1 << 16, 1, 16, 32, gdr.GDR_BF16) + (1 << 30)
 
@@ -95,6 +96,7 @@ def call_chunk(fb, **over):
     (dict(D=64), UNSUPPORTED),
     (dict(dtype=7), UNSUPPORTED),
     (dict(flags=2), UNSUPPORTED),
+    (dict(Nqk=1, Nv=65536), UNSUPPORTED),   # more than 32768 value heads
     (dict(Nqk=3), INVALID),            # Nv % Nqk != 0
     (dict(N=0), INVALID),
     (dict(T=-1), INVALID),

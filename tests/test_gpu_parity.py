@@ -39,6 +39,7 @@ def _chunk(inp, want_state=True, state="in", l2norm=True):
 
 def _assert_close(name, got, ref, tol):
     err = rel_l2(got, ref)
+    print(f"{name}: rel L2 {err:.3e} (tolerance {tol:.0e})")
     assert np.isfinite(got).all(), f"{name}: non-finite values"
     assert err <= tol, f"{name}: rel L2 {err:.3e} > {tol:.0e}"
     return err
