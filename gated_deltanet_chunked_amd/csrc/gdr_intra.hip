@@ -304,6 +304,58 @@ __device__ __forceinline__ f32x4 tile_mma(const T* A, int ar, int ac, const T* B
   return acc;
 }
 
+// One doubling merge of the blocked inverse for finished SZ-blocks: for the
+// pair at b0, X = U block (b0, b0), Z = U block (b0+SZ, b0+SZ) whose rows-as-
+// columns are the L block, Y = the original N block (b0, b0+SZ).  The new
+// top-right block is -X (Y Z); its transpose goes to L's bottom-left block
+// (not needed after the last level).
+template <typename T, int SZ>
+__device__ __forceinline__ void merge_level(IntraLds<T>& s, int w, int l) {
+  constexpr int side = SZ / 16, per = side * side;
+  constexpr int TPW = (128 / (2 * SZ)) * per / 4;   // 16x16 tiles per wave
+  // W^T = (Y Z)^T into the scratch: pair p at scratch rows p * SZ
+  {
+    f32x4 acc[TPW];
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      const int tt = w + 4 * u;
+      const int p = tt / per, ti = (tt % per) / side, tj = tt % side;
+      const int b0 = 2 * SZ * p;
+      acc[u] = tile_mma<T, 128, 128>(s.t0, b0 + 16 * ti, b0 + SZ, s.t1, b0 + SZ + 16 * tj, b0 + SZ, SZ);
+    }
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      const int tt = w + 4 * u;
+      const int p = tt / per, ti = (tt % per) / side, tj = tt % side;
+      const int row = p * SZ + 16 * tj + (l & 15), col = 16 * ti + 4 * (l >> 4);
+      store4<T>(s.w + Sw<T, 64>::at(row, col), acc[u][0], acc[u][1], acc[u][2], acc[u][3]);
+    }
+  }
+  __syncthreads();
+  {
+    f32x4 acc[TPW];
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      const int tt = w + 4 * u;
+      const int p = tt / per, ti = (tt % per) / side, tj = tt % side;
+      const int b0 = 2 * SZ * p;
+      // C = X W  (rows i of X, rows j of W^T)
+      acc[u] = tile_mma<T, 128, 64>(s.t0, b0 + 16 * ti, b0, s.w, p * SZ + 16 * tj, 0, SZ);
+    }
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      const int tt = w + 4 * u;
+      const int p = tt / per, ti = (tt % per) / side, tj = tt % side;
+      const int b0 = 2 * SZ * p;
+      const int i0 = b0 + 16 * ti + 4 * (l >> 4), j0 = b0 + SZ + 16 * tj + (l & 15);
+#pragma unroll
+      for (int x = 0; x < 4; ++x) s.t0[Sw<T>::at(i0 + x, j0)] = from_f32<T>(-acc[u][x]);
+      if (SZ < 64) store4<T>(s.t1 + Sw<T>::at(j0, i0), -acc[u][0], -acc[u][1], -acc[u][2], -acc[u][3]);
+    }
+  }
+  __syncthreads();
+}
+
 // (I + N)^-1 for N strictly upper triangular, 128x128, in place in s.t0
 // (upper form U); s.t1 receives the lower form L = U^T block by block (it
 // must hold zeros above the diagonal on entry).
@@ -313,18 +365,47 @@ __device__ __forceinline__ void invert_unit_upper(IntraLds<T>& s) {
   // 1) 16x16 diagonal blocks by back substitution, one column per thread:
   //    x_i = delta_ic - sum_{m > i} N[i][m] x_m, then the block is
   //    overwritten in place.  The 16 threads of a block are lanes of one wave.
+  //    The block's rows are read as 16-byte pieces (row i needs the pieces
+  //    holding columns > i), four rows at a time and one group ahead of the
+  //    rows being solved, so each group costs one LDS round trip.
   if (tid < 128) {
+    constexpr int EPC = 16 / (int)sizeof(T);   // elements per piece
+    constexpr int PPR = 16 / EPC;               // pieces per block row
     const int b0 = 16 * (tid >> 4), c = tid & 15;
+    u32x4 piece[16][PPR];
+    auto read_rows = [&](int lo, int hi) {     // rows lo..hi-1
+#pragma unroll
+      for (int i = lo; i < hi; ++i)
+#pragma unroll
+        for (int pc = 0; pc < PPR; ++pc)
+          if (i < 15 && EPC * pc + EPC - 1 > i)
+            piece[i][pc] = *reinterpret_cast<const u32x4*>(s.t0 + Sw<T>::at(b0 + i, b0 + EPC * pc));
+    };
     float col[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) col[i] = (i == c) ? 1.0f : 0.0f;
+    auto solve_rows = [&](int lo, int hi) {    // rows hi-1 down to lo
 #pragma unroll
-    for (int i = 14; i >= 0; --i) {
-      float acc = 0.0f;
+      for (int i = hi - 1; i >= lo; --i) {
+        if (i == 15) continue;
+        float acc = 0.0f;
 #pragma unroll
-      for (int m = i + 1; m < 16; ++m) acc += to_f32(s.t0[Sw<T>::at(b0 + i, b0 + m)]) * col[m];
-      if (i < c) col[i] = -acc;
-    }
+        for (int m = i + 1; m < 16; ++m)
+          acc += to_f32(reinterpret_cast<const T*>(&piece[i][m / EPC])[m % EPC]) * col[m];
+        if (i < c) col[i] = -acc;
+      }
+    };
+    read_rows(12, 16);
+    read_rows(8, 12);
+    __builtin_amdgcn_sched_barrier(0);
+    solve_rows(12, 16);
+    read_rows(4, 8);
+    __builtin_amdgcn_sched_barrier(0);
+    solve_rows(8, 12);
+    read_rows(0, 4);
+    __builtin_amdgcn_sched_barrier(0);
+    solve_rows(4, 8);
+    solve_rows(0, 4);
     // every lane's reads of the block come before any lane's writes: the
     // wave issues its LDS accesses in order, and this barrier keeps the
     // compiler from moving the writes above the reads
@@ -337,36 +418,10 @@ __device__ __forceinline__ void invert_unit_upper(IntraLds<T>& s) {
       store4<T>(s.t1 + Sw<T>::at(b0 + c, b0 + i), col[i], col[i + 1], col[i + 2], col[i + 3]);
   }
   __syncthreads();
-  // 2) doubling merges.  For the pair of finished sz-blocks at b0: X = U
-  //    block (b0, b0), Z = U block (b0+sz, b0+sz) whose rows-as-columns are
-  //    the L block, Y = the original N block (b0, b0+sz).  The new top-right
-  //    block is -X (Y Z); its transpose goes to L's bottom-left block.
-#pragma unroll 1
-  for (int sz = 16; sz < 128; sz *= 2) {
-    const int side = sz / 16, per = side * side;
-    const int ntiles = (128 / (2 * sz)) * per;
-    // W^T = (Y Z)^T into the scratch: pair p at scratch rows p * sz
-    for (int tt = w; tt < ntiles; tt += 4) {
-      const int p = tt / per, ti = (tt % per) / side, tj = tt % side;
-      const int b0 = 2 * sz * p;
-      const f32x4 acc = tile_mma<T, 128, 128>(s.t0, b0 + 16 * ti, b0 + sz, s.t1,
-                                               b0 + sz + 16 * tj, b0 + sz, sz);
-      const int row = p * sz + 16 * tj + (l & 15), col = 16 * ti + 4 * (l >> 4);
-      store4<T>(s.w + Sw<T, 64>::at(row, col), acc[0], acc[1], acc[2], acc[3]);
-    }
-    __syncthreads();
-    for (int tt = w; tt < ntiles; tt += 4) {
-      const int p = tt / per, ti = (tt % per) / side, tj = tt % side;
-      const int b0 = 2 * sz * p;
-      // C = X W  (rows i of X, rows j of W^T)
-      const f32x4 acc = tile_mma<T, 128, 64>(s.t0, b0 + 16 * ti, b0, s.w, p * sz + 16 * tj, 0, sz);
-      const int i0 = b0 + 16 * ti + 4 * (l >> 4), j0 = b0 + sz + 16 * tj + (l & 15);
-#pragma unroll
-      for (int x = 0; x < 4; ++x) s.t0[Sw<T>::at(i0 + x, j0)] = from_f32<T>(-acc[x]);
-      if (sz < 64) store4<T>(s.t1 + Sw<T>::at(j0, i0), -acc[0], -acc[1], -acc[2], -acc[3]);
-    }
-    __syncthreads();
-  }
+  // 2) doubling merges 16 -> 32 -> 64 -> 128
+  merge_level<T, 16>(s, w, l);
+  merge_level<T, 32>(s, w, l);
+  merge_level<T, 64>(s, w, l);
 }
 
 // In-place scaling of a 128x128 swizzled tile: element (r, c) times f[r]
@@ -534,7 +589,9 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(
   //   N[c][a]  = beta_a rk_a rk_c Gamma[a][c] G1[a][c]   (c < a)  -> slot 0
   //   P[r][i]  = rq_r rk_i Gamma[r][i] G2[i][r]          (i <= r) -> registers
   // The row and column scalars of a lane are read once, rows as vectors
-  // (4 consecutive rows a..a+3), before the element loop.
+  // (4 consecutive rows a..a+3), before the element loop.  P is kept packed
+  // in the storage type (it is stored as such after the inverse).
+  Pack4<T> Pp[4][4];
   {
     double gcc[4];
     float rkc[4], rqc[4];
@@ -563,6 +620,7 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(
           nv[x] = (c < a + x) ? bta[x] * rka[x] * rkc[jj] * ex * a1[i][jj][x] : 0.0f;
           a2[i][jj][x] = (a + x <= c) ? rqc[jj] * rka[x] * ex * a2[i][jj][x] : 0.0f;
         }
+        Pp[i][jj].set(a2[i][jj]);
         store4<T>(s.t0 + Sw<T>::at(c, a), nv[0], nv[1], nv[2], nv[3]);
       }
     }
@@ -595,17 +653,7 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(
   invert_unit_upper<T>(s);
 
   // ---- 5. P into slot 1 (the lower form is no longer needed)
-  {
-    const int lr = l;
-    (void)lr;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int m = m0 + 16 * i + 4 * (l >> 4), n = n0 + 16 * jj + (l & 15);
-        store4<T>(s.t1 + Sw<T>::at(n, m), a2[i][jj][0], a2[i][jj][1], a2[i][jj][2], a2[i][jj][3]);
-      }
-  }
+  put_t<T>(s.t1, Pp, m0, n0, nullptr);
   __syncthreads();
 
   // ---- 6. R^T = T^T P^T: acc[j][r] = sum_i T^T[j][i] P[r][i] = R[r][j]
