@@ -46,6 +46,7 @@ gdr_status run_chunk(const ChunkArgs& a, hipStream_t st, Recorder& rec) {
   float* gam = reinterpret_cast<float*>(ws + w.gam);
   T* inter = reinterpret_cast<T*>(ws + w.inter);
   float* carry = a.state_out ? a.state_out : reinterpret_cast<float*>(ws + w.carry);
+  T* discard = reinterpret_cast<T*>(ws + w.discard);
   const T* q = static_cast<const T*>(a.q);
   const T* k = static_cast<const T*>(a.k);
   const T* v = static_cast<const T*>(a.v);
@@ -62,7 +63,7 @@ gdr_status run_chunk(const ChunkArgs& a, hipStream_t st, Recorder& rec) {
                     a.scale, norm, inter, gam, st);
     rec.before(GDR_STAGE_INTER);
     launch_inter<T>(inter, table, choff, gam, a.state_in, carry, a.state_out, a.N, a.Nv,
-                    static_cast<int32_t>(s0), nseg, s0 == 0, out, st);
+                    static_cast<int32_t>(s0), nseg, s0 == 0, out, discard, st);
   }
   rec.end();
   return hipGetLastError() == hipSuccess ? GDR_OK : GDR_ERR_HIP;

@@ -83,7 +83,8 @@ template <typename T>
 __global__ __launch_bounds__(256, 1) void inter_kernel(
     const T* __restrict__ inter, const int4* __restrict__ table, const int32_t* __restrict__ choff,
     const float* __restrict__ gam, const float* state_in, float* carry, float* state_out,
-    int32_t N, int32_t Nv, int32_t slot0, int32_t nseg, int first_segment, T* __restrict__ out) {
+    int32_t N, int32_t Nv, int32_t slot0, int32_t nseg, int first_segment, T* __restrict__ out,
+    T* __restrict__ discard) {
   constexpr int KSTEPS = ChunkOps<T>::KSTEPS;
   constexpr int DEPTH = Depth<T>::value;
   constexpr int NSET = DEPTH + 1;
@@ -259,15 +260,16 @@ __global__ __launch_bounds__(256, 1) void inter_kernel(
     } else {
       // acc[i][t] holds O[r][v..v+3] - Ou for r = rb + 16 i + r16, v = 16 t + 4 q4
 #pragma unroll
+      // rows past the chunk's end are written to the discard line instead, so
+      // every step issues the same stores and the memory waits of later
+      // steps never cover them
       for (int i = 0; i < 4; ++i) {
         const int r = rb + 16 * i + r16;
-        if (r < o.len) {
-          T* orow = out + ((size_t)(o.start + r) * Nv + h) * kD + v0;
+        T* orow = r < o.len ? out + ((size_t)(o.start + r) * Nv + h) * kD + v0 : discard;
 #pragma unroll
-          for (int t = 0; t < 2; ++t)
-            put4<T>(orow + 16 * t + 4 * q4, acc[i][t][0] + o.x[i][t][0], acc[i][t][1] + o.x[i][t][1],
-                    acc[i][t][2] + o.x[i][t][2], acc[i][t][3] + o.x[i][t][3]);
-        }
+        for (int t = 0; t < 2; ++t)
+          put4<T>(orow + 16 * t + 4 * q4, acc[i][t][0] + o.x[i][t][0], acc[i][t][1] + o.x[i][t][1],
+                  acc[i][t][2] + o.x[i][t][2], acc[i][t][3] + o.x[i][t][3]);
       }
     }
     buf ^= 1;
@@ -303,17 +305,19 @@ __global__ __launch_bounds__(256, 1) void inter_kernel(
 template <typename T>
 void launch_inter(const T* inter, const int4* table, const int32_t* choff, const float* gam,
                   const float* state_in, float* carry, float* state_out, int32_t N, int32_t Nv,
-                  int32_t slot0, int32_t nseg, bool first_segment, T* out, hipStream_t stream) {
+                  int32_t slot0, int32_t nseg, bool first_segment, T* out, T* discard,
+                  hipStream_t stream) {
   const unsigned blocks = (unsigned)N * (unsigned)Nv * (unsigned)(kD / kBV);
   hipLaunchKernelGGL(inter_kernel<T>, dim3(blocks), dim3(256), 0, stream, inter, table, choff, gam,
-                     state_in, carry, state_out, N, Nv, slot0, nseg, first_segment ? 1 : 0, out);
+                     state_in, carry, state_out, N, Nv, slot0, nseg, first_segment ? 1 : 0, out,
+                     discard);
 }
 
 template void launch_inter<float>(const float*, const int4*, const int32_t*, const float*,
                                   const float*, float*, float*, int32_t, int32_t, int32_t, int32_t,
-                                  bool, float*, hipStream_t);
+                                  bool, float*, float*, hipStream_t);
 template void launch_inter<__bf16>(const __bf16*, const int4*, const int32_t*, const float*,
                                    const float*, float*, float*, int32_t, int32_t, int32_t, int32_t,
-                                   bool, __bf16*, hipStream_t);
+                                   bool, __bf16*, __bf16*, hipStream_t);
 
 }  // namespace gdr

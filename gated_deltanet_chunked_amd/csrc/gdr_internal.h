@@ -51,6 +51,7 @@ struct Workspace {
   int64_t gam;        // float [nslots][Nv]: exp(sum of g over the chunk)
   int64_t inter;      // [seg_slots][Nv][4][128][128] of the matrix-core operand type
   int64_t carry;      // float [N][Nv][128][128]: state between segments
+  int64_t discard;    // 256 bytes: target of the state pass's stores for rows past a chunk's end
   int64_t total;
   int64_t nslots;
   int64_t seg_slots;

@@ -696,6 +696,18 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(
   }
   __syncthreads();
 
+  // q[r][d..d+3] in the layout of the Qp product (phase 10), loaded here so
+  // phase 9 and the product hide their latency
+  Quad4<T> qx[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int d = m0 + 16 * i + 4 * (l >> 4);
+      const int r = n0 + 16 * jj + (l & 15);
+      qx[i][jj].load(at_row(qc, min(r, len - 1), qk_stride, d), r < len);
+    }
+
   // ---- 9. K rows scaled by xk in slot 1, in place (both products with K
   // take diag(xk) on the same side); R into slot 0
   scale_tile<T, kTr>(s.t1, s.xk);   // bf16: rows of K; fp32: columns of K^T
@@ -709,16 +721,6 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(
     zero_acc(acc);
     if constexpr (kTr) sw_gemm64_tr<true, false>(acc, s.t1, s.t0, m0, n0);
     else sw_gemm64<T>(acc, s.t1, s.t0, m0, n0);
-    // q[r][d..d+3] in the layout of this product
-    Quad4<T> qx[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int d = m0 + 16 * i + 4 * (l >> 4);
-        const int r = n0 + 16 * jj + (l & 15);
-        qx[i][jj].load(at_row(qc, min(r, len - 1), qk_stride, d), r < len);
-      }
     Pack4<T> res[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)

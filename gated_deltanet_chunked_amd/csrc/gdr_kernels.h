@@ -16,11 +16,13 @@ hipError_t launch_intra(const Tin* q, const Tin* k, const Tin* v, const float* g
                         const int4* table, int32_t Nqk, int32_t Nv, int32_t slot0, int32_t nseg,
                         float scale, int norm, Tin* inter, float* gam, hipStream_t stream);
 
-// Chunk-serial state pass over chunk slots [slot0, slot0 + nseg).
+// Chunk-serial state pass over chunk slots [slot0, slot0 + nseg).  `discard` is
+// 256 bytes of scratch that absorbs the stores of rows past a chunk's end.
 template <typename Tin>
 void launch_inter(const Tin* inter, const int4* table, const int32_t* choff, const float* gam,
                   const float* state_in, float* carry, float* state_out, int32_t N, int32_t Nv,
-                  int32_t slot0, int32_t nseg, bool first_segment, Tin* out, hipStream_t stream);
+                  int32_t slot0, int32_t nseg, bool first_segment, Tin* out, Tin* discard,
+                  hipStream_t stream);
 
 template <typename Tin>
 void launch_decode(const Tin* q, const Tin* k, const Tin* v, const float* g, const float* beta,

@@ -41,6 +41,7 @@ Workspace plan_workspace(int64_t T, int64_t N, int64_t Nqk, int64_t Nv, gdr_dtyp
   w.inter = off;
   off = align256(off + w.seg_slots * Nv * kInterMats * kMatElems * static_cast<int64_t>(dtype_size(dtype)));
   w.carry = off; off = align256(off + N * Nv * kMatElems * 4);
+  w.discard = off; off = align256(off + 256);
   w.total = off;
   return w;
 }
