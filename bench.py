@@ -9,10 +9,13 @@ are resident in HBM before the timed region starts:
     Nv=32, D=128, bf16 q/k/v, fp32 gates and states), and
   * gdr_recurrent_step on the decode workload (256 sequences x 1 token, same
     heads, fp32 states updated in place).
-``value`` is the chunkwise forward's tokens/s from the GPU time of its kernels
-(HIP events recorded around every launch inside the timed region); the decode
-step's GB/s and both rooflines are reported beside it.  ``ms_per_step`` is
-the host wall clock of a whole step.  rank 0 prints one JSON line.
+``value`` is the chunkwise forward's tokens/s from its GPU time: the span from
+its first kernel's start to its last kernel's end, taken from HIP events that
+the runtime records at each kernel's start and end inside the timed region.
+The same events give every kernel's own duration (the figure rocprofv3's
+kernel trace reports), from which the decode step's GB/s and the rooflines
+are computed.  ``ms_per_step`` is the host wall clock of a whole step.  One
+JSON line is printed.
 """
 from __future__ import annotations
 
@@ -127,13 +130,8 @@ def main() -> int:
     def step(timings):
         gdr.chunk_fwd(P["q"], P["k"], P["v"], P["g"], P["beta"], P["cu"], P["s0"], scale=scale,
                       out=out, state_out=sout, workspace=ws, timings=timings)
-        e0.record()
         gdr.recurrent_step(Dd["q"], Dd["k"], Dd["v"], Dd["g"], Dd["beta"], dstate,
-                           state_out=dstate, out=dout, scale=scale)
-        e1.record()
-
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
+                           state_out=dstate, out=dout, scale=scale, timings=timings)
     if args.copy_probe_mib > 0:
         # a plain device-to-device copy of known size whose source is cold:
         # 1 GiB written after the source pushes it out of the 256 MB
@@ -155,11 +153,13 @@ def main() -> int:
     for _ in range(args.steps):
         tim = []
         step(tim)
-        e1.synchronize()
-        dec_ms.append(e0.elapsed_time(e1))
-        chunk_ms.append(sum(ms for _, ms in tim))
         for name, ms in tim:
-            per_kernel.setdefault(name, []).append(ms)
+            if name == "span":
+                chunk_ms.append(ms)
+            elif name == "decode":
+                dec_ms.append(ms)
+            else:
+                per_kernel.setdefault(name, []).append(ms)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
@@ -218,8 +218,14 @@ def main() -> int:
                       "alg_tflops": round(f_total / chunk_s / 1e12, 2),
                       "frac_bf16_mfma_peak": round(f_total / chunk_s / 1e12 / MFMA_PEAK_TFLOPS["bf16"], 4),
                       "alg_gflop": round(f_total / 1e9, 3),
+                      "kernel_sum_ms": round(sum(v["avg_ms"] * v["launches_per_call"]
+                                                 for v in kstats.values()), 4),
                       "kernels": {k: {"avg_ms": round(v["avg_ms"], 4),
-                                      "launches_per_call": v["launches_per_call"]}
+                                      "launches_per_call": v["launches_per_call"],
+                                      "alg_tflops": (round({"intra": f_intra, "inter": f_inter}[k]
+                                                           / (v["avg_ms"] * v["launches_per_call"] * 1e-3)
+                                                           / 1e12, 2)
+                                                     if k in ("intra", "inter") else None)}
                                   for k, v in kstats.items()}},
         "decode": {"gpu_ms": round(dec_s * 1e3, 4), "gbps": round(dec_gbps, 1),
                    "frac_hbm_peak": round(dec_gbps / HBM_PEAK_GBPS, 4),

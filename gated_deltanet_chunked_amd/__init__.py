@@ -60,8 +60,11 @@ def load(path: str = LIB_PATH):
     lib.gdr_recurrent_step.restype = ctypes.c_int
     lib.gdr_chunk_fwd_timed.argtypes = lib.gdr_chunk_fwd.argtypes + [
         ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_int32), i32,
-        ctypes.POINTER(ctypes.c_int32)]
+        ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_float)]
     lib.gdr_chunk_fwd_timed.restype = ctypes.c_int
+    lib.gdr_recurrent_step_timed.argtypes = lib.gdr_recurrent_step.argtypes + [
+        ctypes.POINTER(ctypes.c_float)]
+    lib.gdr_recurrent_step_timed.restype = ctypes.c_int
     lib.gdr_status_string.argtypes = [ctypes.c_int]
     lib.gdr_status_string.restype = ctypes.c_char_p
     lib.gdr_version.argtypes = []
@@ -120,7 +123,8 @@ def chunk_fwd(q, k, v, g, beta, cu_seqlens, state_in=None, *, scale: Optional[fl
     Returns (out [T, Nv, 128] in q's dtype, state_out or None).
     ``state_out`` may be ``state_in`` for an in-place update.
     With a list as ``timings`` the call goes through ``gdr_chunk_fwd_timed``
-    (blocking) and appends one (stage name, GPU milliseconds) per kernel.
+    (blocking) and appends one (stage name, GPU milliseconds) per kernel, then
+    ("span", milliseconds from the first kernel's start to the last one's end).
     """
     import torch
     lib = load()
@@ -163,19 +167,24 @@ def chunk_fwd(q, k, v, g, beta, cu_seqlens, state_in=None, *, scale: Optional[fl
     ms = (ctypes.c_float * cap)()
     kind = (ctypes.c_int32 * cap)()
     n = ctypes.c_int32(0)
-    st = lib.gdr_chunk_fwd_timed(*args, ms, kind, cap, ctypes.byref(n))
+    span = ctypes.c_float(0.0)
+    st = lib.gdr_chunk_fwd_timed(*args, ms, kind, cap, ctypes.byref(n), ctypes.byref(span))
     if st != 0:
         raise GdrError(st, "gdr_chunk_fwd_timed")
     timings.extend((STAGE_NAMES.get(kind[i], str(kind[i])), float(ms[i])) for i in range(n.value))
+    timings.append(("span", float(span.value)))
     return out, state_out
 
 
 def recurrent_step(q, k, v, g, beta, state_in, *, state_out=None, out=None,
-                   scale: Optional[float] = None, l2norm: bool = True):
+                   scale: Optional[float] = None, l2norm: bool = True,
+                   timings: Optional[list] = None):
     """One decode step for N sequences (``gdr_recurrent_step``).
 
     q, k [N, Nqk, 128], v [N, Nv, 128]; g, beta [N, Nv]; state_in [N, Nv, 128, 128].
     ``state_out`` defaults to ``state_in`` (in-place update).  Returns out [N, Nv, 128].
+    With a list as ``timings`` the call goes through ``gdr_recurrent_step_timed``
+    (which waits for the step) and appends ("decode", kernel milliseconds).
     """
     import torch
     lib = load()
@@ -198,9 +207,17 @@ def recurrent_step(q, k, v, g, beta, state_in, *, state_out=None, out=None,
     _check(out, "out", (N, Nv, D), dt, dev)
     if scale is None:
         scale = D ** -0.5
-    st = lib.gdr_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_in),
-                                _ptr(state_out), N, Nqk, Nv, D, code, float(scale),
-                                GDR_FLAG_QK_L2NORM if l2norm else 0, _ptr(out), _stream())
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_in), _ptr(state_out), N,
+            Nqk, Nv, D, code, float(scale), GDR_FLAG_QK_L2NORM if l2norm else 0, _ptr(out),
+            _stream())
+    if timings is None:
+        st = lib.gdr_recurrent_step(*args)
+        if st != 0:
+            raise GdrError(st, "gdr_recurrent_step")
+        return out
+    ms = ctypes.c_float(0.0)
+    st = lib.gdr_recurrent_step_timed(*args, ctypes.byref(ms))
     if st != 0:
-        raise GdrError(st, "gdr_recurrent_step")
+        raise GdrError(st, "gdr_recurrent_step_timed")
+    timings.append(("decode", float(ms.value)))
     return out

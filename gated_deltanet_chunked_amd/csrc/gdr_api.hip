@@ -11,24 +11,39 @@ using namespace gdr;
 
 namespace {
 
-// Optional per-launch timing: an event is recorded on the stream before every
-// launch and after the last one.  With no event array it does nothing.
+// Optional per-launch timing: launch i gets the event pair ev[2i], ev[2i+1],
+// which the runtime records at that kernel's start and end.  With no event
+// array every launch is untimed.
 struct Recorder {
   hipEvent_t* ev = nullptr;
   int32_t* kind = nullptr;
   int32_t cap = 0;
   int32_t n = 0;
-  hipStream_t st = nullptr;
-  void before(int32_t k) {
-    if (!ev) return;
-    if (n < cap) {
+  LaunchEvents next(int32_t k) {
+    LaunchEvents e;
+    if (ev && n < cap) {
       kind[n] = k;
-      hipEventRecord(ev[n], st);
+      e.start = ev[2 * n];
+      e.stop = ev[2 * n + 1];
     }
     ++n;
+    return e;
   }
-  void end() {
-    if (ev && n <= cap) hipEventRecord(ev[n], st);
+};
+
+// Event pairs for up to kMaxTimed timed launches, destroyed with the object.
+constexpr int32_t kMaxTimed = 64;
+struct EventPairs {
+  hipEvent_t ev[2 * kMaxTimed];
+  int32_t made = 0;
+  bool create(int32_t launches) {
+    if (launches < 0 || launches > kMaxTimed) return false;
+    for (; made < 2 * launches; ++made)
+      if (hipEventCreate(&ev[made]) != hipSuccess) return false;
+    return true;
+  }
+  ~EventPairs() {
+    for (int32_t i = 0; i < made; ++i) (void)hipEventDestroy(ev[i]);
   }
 };
 
@@ -54,18 +69,15 @@ gdr_status run_chunk(const ChunkArgs& a, hipStream_t st, Recorder& rec) {
   const int norm = (a.flags & GDR_FLAG_QK_L2NORM) ? 1 : 0;
   const int32_t nslots = static_cast<int32_t>(w.nslots);
 
-  rec.before(GDR_STAGE_TABLE);
-  launch_table(a.cu_seqlens, a.N, a.T, nslots, table, choff, st);
+  launch_table(a.cu_seqlens, a.N, a.T, nslots, table, choff, st, rec.next(GDR_STAGE_TABLE));
   for (int64_t s0 = 0; s0 < w.nslots; s0 += w.seg_slots) {
     const int32_t nseg = static_cast<int32_t>(w.nslots - s0 < w.seg_slots ? w.nslots - s0 : w.seg_slots);
-    rec.before(GDR_STAGE_INTRA);
     launch_intra<T>(q, k, v, a.g, a.beta, table, a.Nqk, a.Nv, static_cast<int32_t>(s0), nseg,
-                    a.scale, norm, inter, gam, st);
-    rec.before(GDR_STAGE_INTER);
+                    a.scale, norm, inter, gam, st, rec.next(GDR_STAGE_INTRA));
     launch_inter<T>(inter, table, choff, gam, a.state_in, carry, a.state_out, a.N, a.Nv,
-                    static_cast<int32_t>(s0), nseg, s0 == 0, out, discard, st);
+                    static_cast<int32_t>(s0), nseg, s0 == 0, out, discard, st,
+                    rec.next(GDR_STAGE_INTER));
   }
-  rec.end();
   return hipGetLastError() == hipSuccess ? GDR_OK : GDR_ERR_HIP;
 }
 
@@ -105,7 +117,8 @@ extern "C" gdr_status gdr_chunk_fwd_timed(const void* q, const void* k, const vo
                                           gdr_dtype dtype, float scale, uint32_t flags, void* out,
                                           float* state_out, void* workspace,
                                           size_t workspace_bytes, void* stream, float* kernel_ms,
-                                          int32_t* kernel_kind, int32_t max_kernels, int32_t* n) {
+                                          int32_t* kernel_kind, int32_t max_kernels, int32_t* n,
+                                          float* span_ms) {
   ChunkArgs a{q, k, v, g, beta, state_in, cu_seqlens, N, T, Nqk, Nv, D, dtype, scale, flags,
               out, state_out, workspace, workspace_bytes};
   gdr_status s = validate_chunk(a);
@@ -114,31 +127,41 @@ extern "C" gdr_status gdr_chunk_fwd_timed(const void* q, const void* k, const vo
   const int32_t need = launches_needed(plan_workspace(T, N, Nqk, Nv, dtype));
   if (need > max_kernels) return GDR_ERR_INVALID_ARGUMENT;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipEvent_t ev[64];
-  const int32_t nev = need + 1;
-  if (nev > 64) return GDR_ERR_INVALID_ARGUMENT;
-  int32_t made = 0;
-  for (; made < nev; ++made)
-    if (hipEventCreate(&ev[made]) != hipSuccess) break;
-  if (made < nev) {
-    for (int32_t i = 0; i < made; ++i) hipEventDestroy(ev[i]);
-    return GDR_ERR_HIP;
-  }
+  EventPairs pairs;
+  if (!pairs.create(need)) return need > kMaxTimed ? GDR_ERR_INVALID_ARGUMENT : GDR_ERR_HIP;
   Recorder rec;
-  rec.ev = ev;
+  rec.ev = pairs.ev;
   rec.kind = kernel_kind;
   rec.cap = need;
-  rec.st = st;
   s = dispatch_chunk(a, st, rec);
-  if (s == GDR_OK && hipEventSynchronize(ev[rec.n]) != hipSuccess) s = GDR_ERR_HIP;
+  if (s == GDR_OK && hipEventSynchronize(pairs.ev[2 * rec.n - 1]) != hipSuccess) s = GDR_ERR_HIP;
   if (s == GDR_OK) {
     for (int32_t i = 0; i < rec.n; ++i)
-      if (hipEventElapsedTime(&kernel_ms[i], ev[i], ev[i + 1]) != hipSuccess) s = GDR_ERR_HIP;
+      if (hipEventElapsedTime(&kernel_ms[i], pairs.ev[2 * i], pairs.ev[2 * i + 1]) != hipSuccess)
+        s = GDR_ERR_HIP;
+    if (span_ms && hipEventElapsedTime(span_ms, pairs.ev[0], pairs.ev[2 * rec.n - 1]) != hipSuccess)
+      s = GDR_ERR_HIP;
     *n = rec.n;
   }
-  for (int32_t i = 0; i < nev; ++i) hipEventDestroy(ev[i]);
   return s;
 }
+
+namespace {
+
+gdr_status run_step(const StepArgs& a, hipStream_t st, LaunchEvents ev) {
+  const int norm = (a.flags & GDR_FLAG_QK_L2NORM) ? 1 : 0;
+  if (a.dtype == GDR_BF16)
+    launch_decode<__bf16>(static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
+                          static_cast<const __bf16*>(a.v), a.g, a.beta, a.state_in, a.state_out,
+                          a.N, a.Nqk, a.Nv, a.scale, norm, static_cast<__bf16*>(a.out), st, ev);
+  else
+    launch_decode<float>(static_cast<const float*>(a.q), static_cast<const float*>(a.k),
+                         static_cast<const float*>(a.v), a.g, a.beta, a.state_in, a.state_out, a.N,
+                         a.Nqk, a.Nv, a.scale, norm, static_cast<float*>(a.out), st, ev);
+  return hipGetLastError() == hipSuccess ? GDR_OK : GDR_ERR_HIP;
+}
+
+}  // namespace
 
 extern "C" gdr_status gdr_recurrent_step(const void* q, const void* k, const void* v,
                                          const float* g, const float* beta, const float* state_in,
@@ -149,17 +172,28 @@ extern "C" gdr_status gdr_recurrent_step(const void* q, const void* k, const voi
   const gdr_status s = validate_step(a);
   if (s != GDR_OK) return s;
   if (N == 0) return GDR_OK;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  const int norm = (flags & GDR_FLAG_QK_L2NORM) ? 1 : 0;
-  if (dtype == GDR_BF16)
-    launch_decode<__bf16>(static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
-                          static_cast<const __bf16*>(v), g, beta, state_in, state_out, N, Nqk, Nv,
-                          scale, norm, static_cast<__bf16*>(out), st);
-  else
-    launch_decode<float>(static_cast<const float*>(q), static_cast<const float*>(k),
-                         static_cast<const float*>(v), g, beta, state_in, state_out, N, Nqk, Nv,
-                         scale, norm, static_cast<float*>(out), st);
-  return hipGetLastError() == hipSuccess ? GDR_OK : GDR_ERR_HIP;
+  return run_step(a, static_cast<hipStream_t>(stream), LaunchEvents{});
+}
+
+extern "C" gdr_status gdr_recurrent_step_timed(const void* q, const void* k, const void* v,
+                                               const float* g, const float* beta,
+                                               const float* state_in, float* state_out, int32_t N,
+                                               int32_t Nqk, int32_t Nv, int32_t D,
+                                               gdr_dtype dtype, float scale, uint32_t flags,
+                                               void* out, void* stream, float* kernel_ms) {
+  StepArgs a{q, k, v, g, beta, state_in, state_out, N, Nqk, Nv, D, dtype, scale, flags, out};
+  gdr_status s = validate_step(a);
+  if (s != GDR_OK) return s;
+  if (!kernel_ms) return GDR_ERR_INVALID_ARGUMENT;
+  *kernel_ms = 0.0f;
+  if (N == 0) return GDR_OK;
+  EventPairs pairs;
+  if (!pairs.create(1)) return GDR_ERR_HIP;
+  s = run_step(a, static_cast<hipStream_t>(stream), LaunchEvents{pairs.ev[0], pairs.ev[1]});
+  if (s == GDR_OK && (hipEventSynchronize(pairs.ev[1]) != hipSuccess ||
+                      hipEventElapsedTime(kernel_ms, pairs.ev[0], pairs.ev[1]) != hipSuccess))
+    s = GDR_ERR_HIP;
+  return s;
 }
 
 extern "C" const char* gdr_status_string(gdr_status s) {

@@ -99,16 +99,17 @@ __global__ __launch_bounds__(256) void decode_kernel(const T* __restrict__ q, co
 template <typename T>
 void launch_decode(const T* q, const T* k, const T* v, const float* g, const float* beta,
                    const float* state_in, float* state_out, int32_t N, int32_t Nqk, int32_t Nv,
-                   float scale, int norm, T* out, hipStream_t stream) {
-  hipLaunchKernelGGL(decode_kernel<T>, dim3((unsigned)N * (unsigned)Nv), dim3(256), 0, stream, q, k,
-                     v, g, beta, state_in, state_out, Nqk, Nv, scale, norm, out);
+                   float scale, int norm, T* out, hipStream_t stream, LaunchEvents ev) {
+  hipExtLaunchKernelGGL(decode_kernel<T>, dim3((unsigned)N * (unsigned)Nv), dim3(256), 0, stream,
+                        ev.start, ev.stop, 0, q, k, v, g, beta, state_in, state_out, Nqk, Nv, scale,
+                        norm, out);
 }
 
 template void launch_decode<float>(const float*, const float*, const float*, const float*,
                                    const float*, const float*, float*, int32_t, int32_t, int32_t,
-                                   float, int, float*, hipStream_t);
+                                   float, int, float*, hipStream_t, LaunchEvents);
 template void launch_decode<__bf16>(const __bf16*, const __bf16*, const __bf16*, const float*,
                                     const float*, const float*, float*, int32_t, int32_t, int32_t,
-                                    float, int, __bf16*, hipStream_t);
+                                    float, int, __bf16*, hipStream_t, LaunchEvents);
 
 }  // namespace gdr

@@ -306,18 +306,18 @@ template <typename T>
 void launch_inter(const T* inter, const int4* table, const int32_t* choff, const float* gam,
                   const float* state_in, float* carry, float* state_out, int32_t N, int32_t Nv,
                   int32_t slot0, int32_t nseg, bool first_segment, T* out, T* discard,
-                  hipStream_t stream) {
+                  hipStream_t stream, LaunchEvents ev) {
   const unsigned blocks = (unsigned)N * (unsigned)Nv * (unsigned)(kD / kBV);
-  hipLaunchKernelGGL(inter_kernel<T>, dim3(blocks), dim3(256), 0, stream, inter, table, choff, gam,
-                     state_in, carry, state_out, N, Nv, slot0, nseg, first_segment ? 1 : 0, out,
-                     discard);
+  hipExtLaunchKernelGGL(inter_kernel<T>, dim3(blocks), dim3(256), 0, stream, ev.start, ev.stop, 0,
+                        inter, table, choff, gam, state_in, carry, state_out, N, Nv, slot0, nseg,
+                        first_segment ? 1 : 0, out, discard);
 }
 
 template void launch_inter<float>(const float*, const int4*, const int32_t*, const float*,
                                   const float*, float*, float*, int32_t, int32_t, int32_t, int32_t,
-                                  bool, float*, float*, hipStream_t);
+                                  bool, float*, float*, hipStream_t, LaunchEvents);
 template void launch_inter<__bf16>(const __bf16*, const int4*, const int32_t*, const float*,
                                    const float*, float*, float*, int32_t, int32_t, int32_t, int32_t,
-                                   bool, __bf16*, __bf16*, hipStream_t);
+                                   bool, __bf16*, __bf16*, hipStream_t, LaunchEvents);
 
 }  // namespace gdr

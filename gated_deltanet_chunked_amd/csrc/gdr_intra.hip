@@ -800,17 +800,20 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(
 template <typename T>
 hipError_t launch_intra(const T* q, const T* k, const T* v, const float* g, const float* beta,
                         const int4* table, int32_t Nqk, int32_t Nv, int32_t slot0, int32_t nseg,
-                        float scale, int norm, T* inter, float* gam, hipStream_t stream) {
-  hipLaunchKernelGGL(intra_kernel<T>, dim3(nseg, Nv), dim3(256), 0, stream, q, k, v, g, beta, table,
-                     Nqk, Nv, slot0, scale, norm, inter, gam);
+                        float scale, int norm, T* inter, float* gam, hipStream_t stream,
+                        LaunchEvents ev) {
+  hipExtLaunchKernelGGL(intra_kernel<T>, dim3(nseg, Nv), dim3(256), 0, stream, ev.start, ev.stop, 0,
+                        q, k, v, g, beta, table, Nqk, Nv, slot0, scale, norm, inter, gam);
   return hipGetLastError();
 }
 
 template hipError_t launch_intra<float>(const float*, const float*, const float*, const float*,
                                         const float*, const int4*, int32_t, int32_t, int32_t,
-                                        int32_t, float, int, float*, float*, hipStream_t);
+                                        int32_t, float, int, float*, float*, hipStream_t,
+                                        LaunchEvents);
 template hipError_t launch_intra<__bf16>(const __bf16*, const __bf16*, const __bf16*, const float*,
                                          const float*, const int4*, int32_t, int32_t, int32_t,
-                                         int32_t, float, int, __bf16*, float*, hipStream_t);
+                                         int32_t, float, int, __bf16*, float*, hipStream_t,
+                                         LaunchEvents);
 
 }  // namespace gdr

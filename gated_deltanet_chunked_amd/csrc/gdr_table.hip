@@ -55,8 +55,9 @@ __global__ __launch_bounds__(1024) void table_kernel(const int32_t* __restrict__
 }
 
 void launch_table(const int32_t* cu, int32_t N, int32_t T, int32_t nslots, int4* table,
-                  int32_t* choff, hipStream_t stream) {
-  hipLaunchKernelGGL(table_kernel, dim3(1), dim3(1024), 0, stream, cu, N, T, nslots, table, choff);
+                  int32_t* choff, hipStream_t stream, LaunchEvents ev) {
+  hipExtLaunchKernelGGL(table_kernel, dim3(1), dim3(1024), 0, stream, ev.start, ev.stop, 0, cu, N, T,
+                        nslots, table, choff);
 }
 
 }  // namespace gdr

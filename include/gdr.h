@@ -127,14 +127,19 @@ gdr_status gdr_recurrent_step(const void* q, const void* k, const void* v,
 
 /*
  * Profiling variant of gdr_chunk_fwd: the same computation, plus the GPU time
- * of every kernel it launches.  The call creates one HIP event per launch
- * boundary on `stream`, waits for the last one (so, unlike gdr_chunk_fwd, it
- * blocks the host until the work is done), and writes, for launch i < *n:
- *   kernel_ms[i]   elapsed GPU time from the start of launch i to its end;
- *   kernel_kind[i] which stage it was (GDR_STAGE_*).
- * max_kernels bounds both arrays; a call needing more launches than that
- * returns GDR_ERR_INVALID_ARGUMENT before launching anything.  The number of
- * launches is 1 + 2 * ceil(slots / segment), a handful for every workload.
+ * of every kernel it launches.  Each launch gets a pair of HIP events that the
+ * runtime records at that kernel's start and end (hipExtLaunchKernelGGL), so
+ * a duration excludes the gaps between launches.  The call waits for the last
+ * event (so, unlike gdr_chunk_fwd, it blocks the host until the work is done)
+ * and writes, for launch i < *n:
+ *   kernel_ms[i]   GPU time of launch i, from the kernel's start to its end;
+ *   kernel_kind[i] which stage it was (GDR_STAGE_*);
+ * and, if span_ms is not NULL, the time from the first kernel's start to the
+ * last kernel's end (the call's GPU time, gaps between its kernels included).
+ * max_kernels bounds both arrays; a call needing more launches than that, or
+ * more than 64, returns GDR_ERR_INVALID_ARGUMENT before launching anything.
+ * The number of launches is 1 + 2 * ceil(slots / segment), a handful for the
+ * configurations of the pages.
  */
 #define GDR_STAGE_TABLE 0   /* chunk table from cu_seqlens */
 #define GDR_STAGE_INTRA 1   /* norms, gate cumsum, intra-chunk products; parallel over chunks */
@@ -147,7 +152,20 @@ gdr_status gdr_chunk_fwd_timed(const void* q, const void* k, const void* v,
                                void* out, float* state_out,
                                void* workspace, size_t workspace_bytes, void* stream,
                                float* kernel_ms, int32_t* kernel_kind, int32_t max_kernels,
-                               int32_t* n);
+                               int32_t* n, float* span_ms);
+
+/*
+ * Profiling variant of gdr_recurrent_step: the same computation, plus the GPU
+ * time of its one kernel, from the kernel's start to its end, in *kernel_ms
+ * (0 for N = 0).  Blocks the host until the step is done.  kernel_ms must not
+ * be NULL (GDR_ERR_INVALID_ARGUMENT).
+ */
+gdr_status gdr_recurrent_step_timed(const void* q, const void* k, const void* v,
+                                    const float* g, const float* beta,
+                                    const float* state_in, float* state_out,
+                                    int32_t N, int32_t Nqk, int32_t Nv, int32_t D,
+                                    gdr_dtype dtype, float scale, uint32_t flags,
+                                    void* out, void* stream, float* kernel_ms);
 
 /* A static, human-readable name for a status code. */
 const char* gdr_status_string(gdr_status s);

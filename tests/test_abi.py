@@ -158,6 +158,31 @@ def test_recurrent_step_zero_sequences_is_a_no_op():
     assert call_step(fb, N=0, q=None, k=None, v=None, state_in=None, state_out=None, out=None) == OK
 
 
+def test_timed_entry_points_validate_before_launching():
+    """The profiling variants check their extra arguments on the host."""
+    import ctypes
+    lib = gdr.load()
+    fb = FakeBuffers(T=2, N=2)
+    a = [fb.addr["q"], fb.addr["k"], fb.addr["v"], fb.addr["g"], fb.addr["beta"],
+         fb.addr["state_in"], fb.addr["state_out"], fb.N, fb.Nqk, fb.Nv, 128, gdr.GDR_BF16, 0.1,
+         gdr.GDR_FLAG_QK_L2NORM, fb.addr["out"], None]
+    assert lib.gdr_recurrent_step_timed(*a, None) == INVALID     # no kernel_ms
+    ms = ctypes.c_float(1.0)
+    a0 = list(a)
+    a0[7] = 0                                                     # N = 0: nothing to time
+    assert lib.gdr_recurrent_step_timed(*a0, ctypes.byref(ms)) == OK and ms.value == 0.0
+    fc = FakeBuffers()
+    c = [fc.addr["q"], fc.addr["k"], fc.addr["v"], fc.addr["g"], fc.addr["beta"], fc.addr["state_in"],
+         fc.addr["cu"], fc.N, fc.T, fc.Nqk, fc.Nv, 128, gdr.GDR_BF16, 0.1, gdr.GDR_FLAG_QK_L2NORM,
+         fc.addr["out"], fc.addr["state_out"], fc.addr["ws"], fc.sizes["ws"], None]
+    kms = (ctypes.c_float * 4)()
+    kind = (ctypes.c_int32 * 4)()
+    n = ctypes.c_int32(0)
+    # fewer slots than launches (the table alone is one): rejected
+    assert lib.gdr_chunk_fwd_timed(*c, kms, kind, 0, ctypes.byref(n), None) == INVALID
+    assert lib.gdr_chunk_fwd_timed(*c, None, kind, 4, ctypes.byref(n), None) == INVALID
+
+
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(RuntimeError):
         gdr.load(str(tmp_path / "missing.so"))
