@@ -165,6 +165,28 @@ __device__ __forceinline__ void sw_gemm64(f32x4 (&acc)[4][4], const T* A, const 
   const int l = lane_id();
   const int r = l & 15;
   const int kq = (l >> 4) * Mma<T>::E;
+  if constexpr (sizeof(T) == 2) {
+    // bf16: four k-steps, unrolled with two fragment sets (the reads of step
+    // k+1 go out before the products of step k)
+    constexpr int KS = kD / Mma<T>::K;
+    typename Mma<T>::frag a[2][4], b[2][4];
+    auto load = [&](int set, int k) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[set][i] = sw_frag<T>(A, m0 + 16 * i + r, k + kq);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[set][j] = sw_frag<T>(B, n0 + 16 * j + r, k + kq);
+    };
+    load(0, 0);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (ks + 1 < KS) load((ks + 1) & 1, (ks + 1) * Mma<T>::K);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = Mma<T>::mma(a[ks & 1][i], b[ks & 1][j], acc[i][j]);
+    }
+    return;
+  }
 #pragma unroll 2
   for (int k = 0; k < kD; k += Mma<T>::K) {
     typename Mma<T>::frag a[4], b[4];
@@ -258,27 +280,35 @@ __device__ __forceinline__ bf16x8 sw_frag_tr(const __bf16* tile, int o0, int k0)
 }
 
 // sw_gemm64 with either operand read from a k-major tile (ATR / BTR) through
-// transpose reads; bf16 only.
+// transpose reads; bf16 only.  The four k-steps are unrolled with two
+// fragment sets: the reads of step k+1 are issued before the products of
+// step k, so each step's LDS latency hides behind the previous step's
+// matrix instructions.
 template <bool ATR, bool BTR>
 __device__ __forceinline__ void sw_gemm64_tr(f32x4 (&acc)[4][4], const __bf16* A, const __bf16* B,
                                              int m0, int n0) {
   typedef __bf16 T;
+  constexpr int KS = kD / Mma<T>::K;
   const int l = lane_id();
   const int r = l & 15;
   const int kq = (l >> 4) * Mma<T>::E;
-#pragma unroll 1
-  for (int k = 0; k < kD; k += Mma<T>::K) {
-    typename Mma<T>::frag a[4], b[4];
+  typename Mma<T>::frag a[2][4], b[2][4];
+  auto load = [&](int set, int k) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      a[i] = ATR ? sw_frag_tr(A, m0 + 16 * i, k) : sw_frag<T>(A, m0 + 16 * i + r, k + kq);
+      a[set][i] = ATR ? sw_frag_tr(A, m0 + 16 * i, k) : sw_frag<T>(A, m0 + 16 * i + r, k + kq);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      b[j] = BTR ? sw_frag_tr(B, n0 + 16 * j, k) : sw_frag<T>(B, n0 + 16 * j + r, k + kq);
+      b[set][j] = BTR ? sw_frag_tr(B, n0 + 16 * j, k) : sw_frag<T>(B, n0 + 16 * j + r, k + kq);
+  };
+  load(0, 0);
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    if (ks + 1 < KS) load((ks + 1) & 1, (ks + 1) * Mma<T>::K);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = Mma<T>::mma(a[i], b[j], acc[i][j]);
+      for (int j = 0; j < 4; ++j) acc[i][j] = Mma<T>::mma(a[ks & 1][i], b[ks & 1][j], acc[i][j]);
   }
 }
 
