@@ -225,6 +225,15 @@ __global__ __launch_bounds__(256, 1) void inter_kernel(
                   st[i][t][2], st[i][t][3]);
     }
     __syncthreads();
+    // Output waves queue the next operands' loads before their products: the
+    // workgroup's loads go through one vector-memory path, and starting them
+    // here keeps it busy while the state waves' products (the serial chain)
+    // run.  State waves issue theirs after their products.
+    if (!STATE) {
+      load_ops(next, min(c + DEPTH, ce - 1));
+      sink ^= o.warm[0] ^ o.warm[1];
+      warm(o, min(c + kWarmAhead, ce - 1));
+    }
     f32x4 acc[4][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[i][0] = acc[i][1] = zero4();
@@ -245,10 +254,12 @@ __global__ __launch_bounds__(256, 1) void inter_kernel(
     }
     // next operands: chunk c + DEPTH (clamped: past the end it reloads the
     // last chunk, which keeps the loop free of branches)
-    load_ops(next, min(c + DEPTH, ce - 1));
-    // the warming loads held in this set were issued NSET chunks ago
-    sink ^= o.warm[0] ^ o.warm[1];
-    warm(o, min(c + kWarmAhead, ce - 1));
+    if (STATE) {
+      load_ops(next, min(c + DEPTH, ce - 1));
+      // the warming loads held in this set were issued NSET chunks ago
+      sink ^= o.warm[0] ^ o.warm[1];
+      warm(o, min(c + kWarmAhead, ce - 1));
+    }
     if (STATE) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
