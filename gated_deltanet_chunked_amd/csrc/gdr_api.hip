@@ -47,9 +47,11 @@ struct EventPairs {
   }
 };
 
-int32_t launches_needed(const Workspace& w) {
+// A single sequence needs no chunk table (Chunks derives its slots from
+// cu_seqlens directly), so its call is two launches per segment.
+int32_t launches_needed(const Workspace& w, int64_t N) {
   const int64_t segs = (w.nslots + w.seg_slots - 1) / w.seg_slots;
-  return static_cast<int32_t>(1 + 2 * segs);
+  return static_cast<int32_t>((N > 1 ? 1 : 0) + 2 * segs);
 }
 
 template <typename T>
@@ -69,12 +71,17 @@ gdr_status run_chunk(const ChunkArgs& a, hipStream_t st, Recorder& rec) {
   const int norm = (a.flags & GDR_FLAG_QK_L2NORM) ? 1 : 0;
   const int32_t nslots = static_cast<int32_t>(w.nslots);
 
-  launch_table(a.cu_seqlens, a.N, a.T, nslots, table, choff, st, rec.next(GDR_STAGE_TABLE));
+  Chunks chunks{nullptr, nullptr, a.cu_seqlens, a.T};
+  if (a.N > 1) {
+    launch_table(a.cu_seqlens, a.N, a.T, nslots, table, choff, st, rec.next(GDR_STAGE_TABLE));
+    chunks.table = table;
+    chunks.choff = choff;
+  }
   for (int64_t s0 = 0; s0 < w.nslots; s0 += w.seg_slots) {
     const int32_t nseg = static_cast<int32_t>(w.nslots - s0 < w.seg_slots ? w.nslots - s0 : w.seg_slots);
-    launch_intra<T>(q, k, v, a.g, a.beta, table, a.Nqk, a.Nv, static_cast<int32_t>(s0), nseg,
+    launch_intra<T>(q, k, v, a.g, a.beta, chunks, a.Nqk, a.Nv, static_cast<int32_t>(s0), nseg,
                     a.scale, norm, inter, gam, st, rec.next(GDR_STAGE_INTRA));
-    launch_inter<T>(inter, table, choff, gam, a.state_in, carry, a.state_out, a.N, a.Nv,
+    launch_inter<T>(inter, chunks, gam, a.state_in, carry, a.state_out, a.N, a.Nv,
                     static_cast<int32_t>(s0), nseg, s0 == 0, out, discard, st,
                     rec.next(GDR_STAGE_INTER));
   }
@@ -124,7 +131,7 @@ extern "C" gdr_status gdr_chunk_fwd_timed(const void* q, const void* k, const vo
   gdr_status s = validate_chunk(a);
   if (s != GDR_OK) return s;
   if (!kernel_ms || !kernel_kind || !n || max_kernels < 0) return GDR_ERR_INVALID_ARGUMENT;
-  const int32_t need = launches_needed(plan_workspace(T, N, Nqk, Nv, dtype));
+  const int32_t need = launches_needed(plan_workspace(T, N, Nqk, Nv, dtype), N);
   if (need > max_kernels) return GDR_ERR_INVALID_ARGUMENT;
   hipStream_t st = static_cast<hipStream_t>(stream);
   EventPairs pairs;

@@ -81,8 +81,7 @@ constexpr int kWarmAhead = 5;
 
 template <typename T>
 __global__ __launch_bounds__(256, 1) void inter_kernel(
-    const T* __restrict__ inter, const int4* __restrict__ table, const int32_t* __restrict__ choff,
-    const float* __restrict__ gam, const float* state_in, float* carry, float* state_out,
+    const T* __restrict__ inter, Chunks chunks, const float* __restrict__ gam, const float* state_in, float* carry, float* state_out,
     int32_t N, int32_t Nv, int32_t slot0, int32_t nseg, int first_segment, T* __restrict__ out,
     T* __restrict__ discard) {
   constexpr int KSTEPS = ChunkOps<T>::KSTEPS;
@@ -114,7 +113,8 @@ __global__ __launch_bounds__(256, 1) void inter_kernel(
   const int rb = 64 * (w & 1);               // first row (d or r) of this wave's block
   const int v0 = kBV * vb;                   // first state row of the workgroup
   const size_t sb = (size_t)bh * kD * kD;    // this (b, h)'s state
-  const int c0 = choff[b], c1 = choff[b + 1];
+  int c0, c1;
+  chunks.seq_slots(b, c0, c1);
 
   if (c0 == c1) {
     // empty sequence: its final state is its initial state
@@ -139,8 +139,9 @@ __global__ __launch_bounds__(256, 1) void inter_kernel(
 
   const int r16 = l & 15, q4 = l >> 4, kq = q4 * Mma<T>::E;
   for (int idx = tid; idx < ce - cb; idx += 256) {
-    const int4 e = table[cb + idx];
-    sTab[idx] = make_int2(e.y, e.z);
+    int st, ln;
+    chunks.slot(cb + idx, st, ln);
+    sTab[idx] = make_int2(st, ln);
     sGam[idx] = gam[(size_t)(cb + idx) * Nv + h];
   }
   __syncthreads();
@@ -314,21 +315,21 @@ __global__ __launch_bounds__(256, 1) void inter_kernel(
 }
 
 template <typename T>
-void launch_inter(const T* inter, const int4* table, const int32_t* choff, const float* gam,
-                  const float* state_in, float* carry, float* state_out, int32_t N, int32_t Nv,
-                  int32_t slot0, int32_t nseg, bool first_segment, T* out, T* discard,
-                  hipStream_t stream, LaunchEvents ev) {
+void launch_inter(const T* inter, Chunks chunks, const float* gam, const float* state_in,
+                  float* carry, float* state_out, int32_t N, int32_t Nv, int32_t slot0,
+                  int32_t nseg, bool first_segment, T* out, T* discard, hipStream_t stream,
+                  LaunchEvents ev) {
   const unsigned blocks = (unsigned)N * (unsigned)Nv * (unsigned)(kD / kBV);
   hipExtLaunchKernelGGL(inter_kernel<T>, dim3(blocks), dim3(256), 0, stream, ev.start, ev.stop, 0,
-                        inter, table, choff, gam, state_in, carry, state_out, N, Nv, slot0, nseg,
+                        inter, chunks, gam, state_in, carry, state_out, N, Nv, slot0, nseg,
                         first_segment ? 1 : 0, out, discard);
 }
 
-template void launch_inter<float>(const float*, const int4*, const int32_t*, const float*,
-                                  const float*, float*, float*, int32_t, int32_t, int32_t, int32_t,
-                                  bool, float*, float*, hipStream_t, LaunchEvents);
-template void launch_inter<__bf16>(const __bf16*, const int4*, const int32_t*, const float*,
-                                   const float*, float*, float*, int32_t, int32_t, int32_t, int32_t,
-                                   bool, __bf16*, __bf16*, hipStream_t, LaunchEvents);
+template void launch_inter<float>(const float*, Chunks, const float*, const float*, float*, float*,
+                                  int32_t, int32_t, int32_t, int32_t, bool, float*, float*,
+                                  hipStream_t, LaunchEvents);
+template void launch_inter<__bf16>(const __bf16*, Chunks, const float*, const float*, float*,
+                                   float*, int32_t, int32_t, int32_t, int32_t, bool, __bf16*,
+                                   __bf16*, hipStream_t, LaunchEvents);
 
 }  // namespace gdr

@@ -509,17 +509,16 @@ struct F4 {   // adapter so raw accumulators fit put_t
 template <typename T>
 __global__ __launch_bounds__(256, 2) void intra_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-    const float* __restrict__ g, const float* __restrict__ beta, const int4* __restrict__ table,
-    int32_t Nqk, int32_t Nv, int32_t slot0, float scale, int norm, T* __restrict__ inter,
+    const float* __restrict__ g, const float* __restrict__ beta, Chunks chunks, int32_t Nqk,
+    int32_t Nv, int32_t slot0, float scale, int norm, T* __restrict__ inter,
     float* __restrict__ gam_out) {
   __shared__ IntraLds<T> s;
   // bf16 reads K^T and V^T straight from the row-major K and V tiles with
   // LDS transpose reads; fp32 (no 32-bit transpose read) stages K^T and V^T
   constexpr bool kTr = sizeof(T) == 2;
   const int local_slot = blockIdx.x, h = blockIdx.y;
-  const int4 e = table[slot0 + local_slot];
-  if (e.x < 0) return;
-  const int start = e.y, len = e.z;
+  int start, len;
+  if (!chunks.slot(slot0 + local_slot, start, len)) return;
   const int j = h / (Nv / Nqk);
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int m0 = 64 * (w >> 1), n0 = 64 * (w & 1);
@@ -799,20 +798,20 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(
 
 template <typename T>
 hipError_t launch_intra(const T* q, const T* k, const T* v, const float* g, const float* beta,
-                        const int4* table, int32_t Nqk, int32_t Nv, int32_t slot0, int32_t nseg,
+                        Chunks chunks, int32_t Nqk, int32_t Nv, int32_t slot0, int32_t nseg,
                         float scale, int norm, T* inter, float* gam, hipStream_t stream,
                         LaunchEvents ev) {
   hipExtLaunchKernelGGL(intra_kernel<T>, dim3(nseg, Nv), dim3(256), 0, stream, ev.start, ev.stop, 0,
-                        q, k, v, g, beta, table, Nqk, Nv, slot0, scale, norm, inter, gam);
+                        q, k, v, g, beta, chunks, Nqk, Nv, slot0, scale, norm, inter, gam);
   return hipGetLastError();
 }
 
 template hipError_t launch_intra<float>(const float*, const float*, const float*, const float*,
-                                        const float*, const int4*, int32_t, int32_t, int32_t,
+                                        const float*, Chunks, int32_t, int32_t, int32_t,
                                         int32_t, float, int, float*, float*, hipStream_t,
                                         LaunchEvents);
 template hipError_t launch_intra<__bf16>(const __bf16*, const __bf16*, const __bf16*, const float*,
-                                         const float*, const int4*, int32_t, int32_t, int32_t,
+                                         const float*, Chunks, int32_t, int32_t, int32_t,
                                          int32_t, float, int, __bf16*, float*, hipStream_t,
                                          LaunchEvents);
 

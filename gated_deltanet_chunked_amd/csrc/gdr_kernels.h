@@ -13,6 +13,49 @@ struct LaunchEvents {
   hipEvent_t start = nullptr, stop = nullptr;
 };
 
+// Chunk slots of the packed sequences.  Chunks restart at every sequence
+// start (Qwen3-Next blog post, section 5(1)c).  With a chunk table (built
+// from cu_seqlens by table_kernel) slot s is {sequence, first token, length};
+// for a single sequence (table == nullptr) slot s covers tokens
+// [lo + 128 s, min(lo + 128 (s + 1), hi)), lo and hi being cu_seqlens[0..1]
+// clamped into [0, T]: the entries the table kernel would write.
+struct Chunks {
+  const int4* table;
+  const int32_t* choff;
+  const int32_t* cu;
+  int32_t T;
+  __device__ __forceinline__ void one_range(int& lo, int& hi) const {
+    lo = min(max(cu[0], 0), T);
+    hi = min(max(cu[1], lo), T);
+  }
+  // tokens of slot s; false for an unused slot
+  __device__ __forceinline__ bool slot(int s, int& start, int& len) const {
+    if (table) {
+      const int4 e = table[s];
+      start = e.y;
+      len = e.z;
+      return e.x >= 0;
+    }
+    int lo, hi;
+    one_range(lo, hi);
+    start = lo + 128 * s;
+    len = min(128, hi - start);
+    return start < hi;
+  }
+  // slots [c0, c1) of sequence b
+  __device__ __forceinline__ void seq_slots(int b, int& c0, int& c1) const {
+    if (table) {
+      c0 = choff[b];
+      c1 = choff[b + 1];
+      return;
+    }
+    int lo, hi;
+    one_range(lo, hi);
+    c0 = 0;
+    c1 = (hi - lo + 127) / 128;
+  }
+};
+
 void launch_table(const int32_t* cu, int32_t N, int32_t T, int32_t nslots, int4* table,
                   int32_t* choff, hipStream_t stream, LaunchEvents ev = {});
 
@@ -20,14 +63,14 @@ void launch_table(const int32_t* cu, int32_t N, int32_t T, int32_t nslots, int4*
 // also writes exp(total gate of the chunk) to gam[slot][head].
 template <typename Tin>
 hipError_t launch_intra(const Tin* q, const Tin* k, const Tin* v, const float* g, const float* beta,
-                        const int4* table, int32_t Nqk, int32_t Nv, int32_t slot0, int32_t nseg,
+                        Chunks chunks, int32_t Nqk, int32_t Nv, int32_t slot0, int32_t nseg,
                         float scale, int norm, Tin* inter, float* gam, hipStream_t stream,
                         LaunchEvents ev = {});
 
 // Chunk-serial state pass over chunk slots [slot0, slot0 + nseg).  `discard` is
 // 256 bytes of scratch that absorbs the stores of rows past a chunk's end.
 template <typename Tin>
-void launch_inter(const Tin* inter, const int4* table, const int32_t* choff, const float* gam,
+void launch_inter(const Tin* inter, Chunks chunks, const float* gam,
                   const float* state_in, float* carry, float* state_out, int32_t N, int32_t Nv,
                   int32_t slot0, int32_t nseg, bool first_segment, Tin* out, Tin* discard,
                   hipStream_t stream, LaunchEvents ev = {});

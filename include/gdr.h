@@ -138,8 +138,8 @@ gdr_status gdr_recurrent_step(const void* q, const void* k, const void* v,
  * last kernel's end (the call's GPU time, gaps between its kernels included).
  * max_kernels bounds both arrays; a call needing more launches than that, or
  * more than 64, returns GDR_ERR_INVALID_ARGUMENT before launching anything.
- * The number of launches is 1 + 2 * ceil(slots / segment), a handful for the
- * configurations of the pages.
+ * The number of launches is 2 * ceil(slots / segment), plus 1 (the chunk
+ * table) when N > 1: a handful for the configurations of the pages.
  */
 #define GDR_STAGE_TABLE 0   /* chunk table from cu_seqlens */
 #define GDR_STAGE_INTRA 1   /* norms, gate cumsum, intra-chunk products; parallel over chunks */
