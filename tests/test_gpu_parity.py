@@ -226,3 +226,39 @@ def test_chunk_equals_repeated_steps():
     steps = to_f64(torch.cat(outs))
     _assert_close("out", out, steps, 1e-4)
     _assert_close("state", st, to_f64(s), 1e-4)
+
+
+# ------------------------------------------------------- timed entry points
+
+
+@pytest.mark.parametrize("lengths", [[640], [300, 1, 129]], ids=["one-sequence", "packed"])
+def test_timed_entry_points_match_untimed(lengths):
+    """gdr_chunk_fwd_timed and gdr_recurrent_step_timed (the benchmark's
+    calls) compute exactly what the plain calls compute, and report one
+    positive duration per kernel and a span that covers them."""
+    import torch
+    inp = make_inputs(lengths, 2, 4, dtype="bf16", seed=41, state_std=0.01)
+    t = device_tensors(inp)
+    args = (t["q"], t["k"], t["v"], t["g"], t["beta"], t["cu"], t["state_in"])
+    out0, st0 = gdr.chunk_fwd(*args, scale=SCALE)
+    tim = []
+    out1, st1 = gdr.chunk_fwd(*args, scale=SCALE, timings=tim)
+    torch.cuda.synchronize()
+    assert torch.equal(out0, out1) and torch.equal(st0, st1)
+    kernels = [(n, ms) for n, ms in tim if n != "span"]
+    span = [ms for n, ms in tim if n == "span"]
+    expect = {"intra", "inter"} | ({"table"} if len(lengths) > 1 else set())
+    assert {n for n, _ in kernels} == expect
+    assert len(span) == 1 and all(ms > 0 for _, ms in kernels)
+    assert span[0] >= max(ms for _, ms in kernels)
+
+    dec = make_inputs([1] * 6, 2, 4, dtype="bf16", seed=43, state_std=0.01)
+    d = device_tensors(dec)
+    s_a, s_b = d["state_in"].clone(), d["state_in"].clone()
+    o_a = gdr.recurrent_step(d["q"], d["k"], d["v"], d["g"], d["beta"], s_a, scale=SCALE)
+    tim = []
+    o_b = gdr.recurrent_step(d["q"], d["k"], d["v"], d["g"], d["beta"], s_b, scale=SCALE,
+                             timings=tim)
+    torch.cuda.synchronize()
+    assert torch.equal(o_a, o_b) and torch.equal(s_a, s_b)
+    assert len(tim) == 1 and tim[0][0] == "decode" and tim[0][1] > 0
