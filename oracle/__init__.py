@@ -8,6 +8,9 @@ plain definition the chunkwise form must reproduce (Qwen3-Next blog post,
 section 5(2)).  ``oracle.alt`` holds two independently written codings of the
 same rule (the DeltaNet matrix form and the chunkwise form of section 5(1)),
 used only to pin ``recurrent`` in the oracle's own tests.
+``recurrent_step_bf16_state`` is one decode step whose stored state is
+rounded to bfloat16 (``round_bf16``), pinned in
+``tests/test_oracle_bf16_state.py``.
 """
 from __future__ import annotations
 
@@ -96,6 +99,45 @@ def recurrent(q, k, v, g, beta, state_in: Optional[np.ndarray], cu_seqlens,
     if rc != 0:
         raise ValueError(f"oracle rejected its arguments (code {rc})")
     return out, sout
+
+
+def round_bf16(x) -> np.ndarray:
+    """Each fp64 value rounded to the nearest bfloat16 value, ties to even.
+
+    bfloat16 keeps 8 significant bits (7 stored) and fp32's exponent range;
+    below 2**-126 its spacing stays 2**-133 (subnormals).  Written from that
+    definition: x = m * 2**e with 0.5 <= |m| < 1, so the spacing of bf16
+    values near x is 2**(e - 8); x / spacing is rounded to the nearest
+    integer, halves to even (np.rint).  Values beyond the largest finite
+    bf16 value after rounding become +-inf.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    _, e = np.frexp(x)
+    quantum = np.ldexp(1.0, np.maximum(e, -125) - 8)
+    r = np.rint(x / quantum) * quantum
+    big = np.abs(r) > 3.3895313892515355e38   # (2 - 2**-7) * 2**127
+    return np.where(big, np.copysign(np.inf, x), r)
+
+
+def recurrent_step_bf16_state(q, k, v, g, beta, state_in, scale: float, eps: float = EPS,
+                              nthreads: int = 0, l2norm: bool = True, lib=None):
+    """One decode step whose state is stored in bfloat16 between steps.
+
+    The generic "Gated DeltaNet" article (section 6.3, deployment advice)
+    names a bfloat16 state cache.  Reading taken: the stored state holds
+    bf16 values; the step itself is the exact rule of the blog post's
+    section 5(2) on those values (so the output comes from the unrounded new
+    state), and only the new state is rounded to bf16 when it is stored.
+
+    Shapes: q, k [N, Nqk, Dk]; v [N, Nv, Dv]; g, beta [N, Nv];
+    state_in [N, Nv, Dv, Dk] (bf16 values, given as floats).
+    Returns (out [N, Nv, Dv], state_out [N, Nv, Dv, Dk] rounded to bf16).
+    """
+    N = np.asarray(q).shape[0]
+    cu = np.arange(N + 1, dtype=np.int32)
+    out, sout = recurrent(q, k, v, g, beta, _f64(state_in), cu, scale, eps=eps, nthreads=nthreads,
+                          want_state=True, lib=lib, l2norm=l2norm)
+    return out, round_bf16(sout)
 
 
 def rel_l2(x, ref) -> float:
