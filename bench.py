@@ -14,8 +14,10 @@ its first kernel's start to its last kernel's end, taken from HIP events that
 the runtime records at each kernel's start and end inside the timed region.
 The same events give every kernel's own duration (the figure rocprofv3's
 kernel trace reports), from which the decode step's GB/s and the rooflines
-are computed.  ``ms_per_step`` is the host wall clock of a whole step.  One
-JSON line is printed.
+are computed.  ``ms_per_step`` is the host wall clock of a whole step.  After
+the timed steps the decode step is also measured with its state stored in
+bf16 (``gdr_recurrent_step_bf16_state``, half the state bytes), reported as
+``decode_bf16_state``; it is not part of the step.  One JSON line is printed.
 """
 from __future__ import annotations
 
@@ -49,8 +51,8 @@ def alg_flops_chunk(lengths, Nqk, Nv):
     return intra, inter
 
 
-def alg_bytes_decode(N, Nqk, Nv, es=2):
-    state = N * Nv * D * D * 4 * 2
+def alg_bytes_decode(N, Nqk, Nv, es=2, state_es=4):
+    state = N * Nv * D * D * state_es * 2
     qkv = N * (2 * Nqk + Nv) * D * es
     gb = N * Nv * 4 * 2
     out = N * Nv * D * es
@@ -198,6 +200,21 @@ def main() -> int:
                     per_launch=f"{per_launch_flops:.4g} algorithmic FLOP")
         del launches
 
+    # ---- decode with the state stored in bf16 (a bf16 state cache): measured
+    # after the timed steps, on the same decode inputs, and reported beside them
+    bstate = Dd["s0"].to(torch.bfloat16)
+    for _ in range(args.warmup):
+        gdr.recurrent_step(Dd["q"], Dd["k"], Dd["v"], Dd["g"], Dd["beta"], bstate,
+                           state_out=bstate, out=dout, scale=scale)
+    btim = []
+    for _ in range(args.steps):
+        gdr.recurrent_step(Dd["q"], Dd["k"], Dd["v"], Dd["g"], Dd["beta"], bstate,
+                           state_out=bstate, out=dout, scale=scale, timings=btim)
+    torch.cuda.synchronize()
+    bdec_s = float(np.mean([ms for _, ms in btim])) * 1e-3
+    bdec_bytes = alg_bytes_decode(dec.N, dec.Nqk, dec.Nv, state_es=2)
+    bdec_gbps = bdec_bytes / bdec_s / 1e9
+
     res = {
         "metric": "chunk GDR fwd tokens/s + % MFMA peak; decode-step GB/s (% HBM peak)",
         "value": round(tok_s, 1),
@@ -230,6 +247,9 @@ def main() -> int:
         "decode": {"gpu_ms": round(dec_s * 1e3, 4), "gbps": round(dec_gbps, 1),
                    "frac_hbm_peak": round(dec_gbps / HBM_PEAK_GBPS, 4),
                    "tokens_per_s": round(dec.N / dec_s, 1), "alg_bytes": dec_bytes},
+        "decode_bf16_state": {"gpu_ms": round(bdec_s * 1e3, 4), "gbps": round(bdec_gbps, 1),
+                              "frac_hbm_peak": round(bdec_gbps / HBM_PEAK_GBPS, 4),
+                              "tokens_per_s": round(dec.N / bdec_s, 1), "alg_bytes": bdec_bytes},
         "roofline": roof,
     }
 

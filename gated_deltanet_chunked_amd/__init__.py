@@ -65,6 +65,8 @@ def load(path: str = LIB_PATH):
     lib.gdr_recurrent_step_timed.argtypes = lib.gdr_recurrent_step.argtypes + [
         ctypes.POINTER(ctypes.c_float)]
     lib.gdr_recurrent_step_timed.restype = ctypes.c_int
+    lib.gdr_recurrent_step_bf16_state.argtypes = lib.gdr_recurrent_step_timed.argtypes
+    lib.gdr_recurrent_step_bf16_state.restype = ctypes.c_int
     lib.gdr_status_string.argtypes = [ctypes.c_int]
     lib.gdr_status_string.restype = ctypes.c_char_p
     lib.gdr_version.argtypes = []
@@ -183,8 +185,11 @@ def recurrent_step(q, k, v, g, beta, state_in, *, state_out=None, out=None,
 
     q, k [N, Nqk, 128], v [N, Nv, 128]; g, beta [N, Nv]; state_in [N, Nv, 128, 128].
     ``state_out`` defaults to ``state_in`` (in-place update).  Returns out [N, Nv, 128].
-    With a list as ``timings`` the call goes through ``gdr_recurrent_step_timed``
-    (which waits for the step) and appends ("decode", kernel milliseconds).
+    States in float32 go to ``gdr_recurrent_step``; states in bfloat16 (a bf16
+    state cache) go to ``gdr_recurrent_step_bf16_state``.
+    With a list as ``timings`` the call is timed (``gdr_recurrent_step_timed``,
+    or the bf16-state call with a time pointer; it then waits for the step)
+    and appends ("decode", kernel milliseconds).
     """
     import torch
     lib = load()
@@ -198,10 +203,13 @@ def recurrent_step(q, k, v, g, beta, state_in, *, state_out=None, out=None,
     _check(v, "v", (N, Nv, D), dt, dev)
     _check(g, "g", (N, Nv), torch.float32, dev)
     _check(beta, "beta", (N, Nv), torch.float32, dev)
-    _check(state_in, "state_in", (N, Nv, D, D), torch.float32, dev)
+    st_dt = state_in.dtype
+    if st_dt not in (torch.float32, torch.bfloat16):
+        raise TypeError(f"state_in: dtype {st_dt}, expected float32 or bfloat16")
+    _check(state_in, "state_in", (N, Nv, D, D), st_dt, dev)
     if state_out is None:
         state_out = state_in
-    _check(state_out, "state_out", (N, Nv, D, D), torch.float32, dev)
+    _check(state_out, "state_out", (N, Nv, D, D), st_dt, dev)
     if out is None:
         out = torch.empty((N, Nv, D), dtype=dt, device=dev)
     _check(out, "out", (N, Nv, D), dt, dev)
@@ -210,6 +218,14 @@ def recurrent_step(q, k, v, g, beta, state_in, *, state_out=None, out=None,
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_in), _ptr(state_out), N,
             Nqk, Nv, D, code, float(scale), GDR_FLAG_QK_L2NORM if l2norm else 0, _ptr(out),
             _stream())
+    if st_dt == torch.bfloat16:
+        ms = ctypes.c_float(0.0)
+        st = lib.gdr_recurrent_step_bf16_state(*args, ctypes.byref(ms) if timings is not None else None)
+        if st != 0:
+            raise GdrError(st, "gdr_recurrent_step_bf16_state")
+        if timings is not None:
+            timings.append(("decode", float(ms.value)))
+        return out
     if timings is None:
         st = lib.gdr_recurrent_step(*args)
         if st != 0:

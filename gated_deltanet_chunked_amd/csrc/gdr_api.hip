@@ -155,17 +155,42 @@ extern "C" gdr_status gdr_chunk_fwd_timed(const void* q, const void* k, const vo
 
 namespace {
 
+template <typename St>
+void step_as(const StepArgs& a, int norm, hipStream_t st, LaunchEvents ev) {
+  const St* sin = static_cast<const St*>(a.state_in);
+  St* sout = static_cast<St*>(a.state_out);
+  if (a.dtype == GDR_BF16)
+    launch_decode<__bf16, St>(static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
+                              static_cast<const __bf16*>(a.v), a.g, a.beta, sin, sout, a.N, a.Nqk,
+                              a.Nv, a.scale, norm, static_cast<__bf16*>(a.out), st, ev);
+  else
+    launch_decode<float, St>(static_cast<const float*>(a.q), static_cast<const float*>(a.k),
+                             static_cast<const float*>(a.v), a.g, a.beta, sin, sout, a.N, a.Nqk,
+                             a.Nv, a.scale, norm, static_cast<float*>(a.out), st, ev);
+}
+
 gdr_status run_step(const StepArgs& a, hipStream_t st, LaunchEvents ev) {
   const int norm = (a.flags & GDR_FLAG_QK_L2NORM) ? 1 : 0;
-  if (a.dtype == GDR_BF16)
-    launch_decode<__bf16>(static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
-                          static_cast<const __bf16*>(a.v), a.g, a.beta, a.state_in, a.state_out,
-                          a.N, a.Nqk, a.Nv, a.scale, norm, static_cast<__bf16*>(a.out), st, ev);
-  else
-    launch_decode<float>(static_cast<const float*>(a.q), static_cast<const float*>(a.k),
-                         static_cast<const float*>(a.v), a.g, a.beta, a.state_in, a.state_out, a.N,
-                         a.Nqk, a.Nv, a.scale, norm, static_cast<float*>(a.out), st, ev);
+  if (a.state_bf16) step_as<__bf16>(a, norm, st, ev);
+  else step_as<float>(a, norm, st, ev);
   return hipGetLastError() == hipSuccess ? GDR_OK : GDR_ERR_HIP;
+}
+
+// Validation, then the launch, timed when kernel_ms is not NULL (the call
+// then waits for the kernel's end event).
+gdr_status step_entry(const StepArgs& a, hipStream_t st, float* kernel_ms) {
+  gdr_status s = validate_step(a);
+  if (s != GDR_OK) return s;
+  if (kernel_ms) *kernel_ms = 0.0f;
+  if (a.N == 0) return GDR_OK;
+  if (!kernel_ms) return run_step(a, st, LaunchEvents{});
+  EventPairs pairs;
+  if (!pairs.create(1)) return GDR_ERR_HIP;
+  s = run_step(a, st, LaunchEvents{pairs.ev[0], pairs.ev[1]});
+  if (s == GDR_OK && (hipEventSynchronize(pairs.ev[1]) != hipSuccess ||
+                      hipEventElapsedTime(kernel_ms, pairs.ev[0], pairs.ev[1]) != hipSuccess))
+    s = GDR_ERR_HIP;
+  return s;
 }
 
 }  // namespace
@@ -175,11 +200,8 @@ extern "C" gdr_status gdr_recurrent_step(const void* q, const void* k, const voi
                                          float* state_out, int32_t N, int32_t Nqk, int32_t Nv,
                                          int32_t D, gdr_dtype dtype, float scale, uint32_t flags,
                                          void* out, void* stream) {
-  StepArgs a{q, k, v, g, beta, state_in, state_out, N, Nqk, Nv, D, dtype, scale, flags, out};
-  const gdr_status s = validate_step(a);
-  if (s != GDR_OK) return s;
-  if (N == 0) return GDR_OK;
-  return run_step(a, static_cast<hipStream_t>(stream), LaunchEvents{});
+  StepArgs a{q, k, v, g, beta, state_in, state_out, N, Nqk, Nv, D, dtype, scale, flags, out, false};
+  return step_entry(a, static_cast<hipStream_t>(stream), nullptr);
 }
 
 extern "C" gdr_status gdr_recurrent_step_timed(const void* q, const void* k, const void* v,
@@ -188,19 +210,19 @@ extern "C" gdr_status gdr_recurrent_step_timed(const void* q, const void* k, con
                                                int32_t Nqk, int32_t Nv, int32_t D,
                                                gdr_dtype dtype, float scale, uint32_t flags,
                                                void* out, void* stream, float* kernel_ms) {
-  StepArgs a{q, k, v, g, beta, state_in, state_out, N, Nqk, Nv, D, dtype, scale, flags, out};
-  gdr_status s = validate_step(a);
-  if (s != GDR_OK) return s;
   if (!kernel_ms) return GDR_ERR_INVALID_ARGUMENT;
-  *kernel_ms = 0.0f;
-  if (N == 0) return GDR_OK;
-  EventPairs pairs;
-  if (!pairs.create(1)) return GDR_ERR_HIP;
-  s = run_step(a, static_cast<hipStream_t>(stream), LaunchEvents{pairs.ev[0], pairs.ev[1]});
-  if (s == GDR_OK && (hipEventSynchronize(pairs.ev[1]) != hipSuccess ||
-                      hipEventElapsedTime(kernel_ms, pairs.ev[0], pairs.ev[1]) != hipSuccess))
-    s = GDR_ERR_HIP;
-  return s;
+  StepArgs a{q, k, v, g, beta, state_in, state_out, N, Nqk, Nv, D, dtype, scale, flags, out, false};
+  return step_entry(a, static_cast<hipStream_t>(stream), kernel_ms);
+}
+
+extern "C" gdr_status gdr_recurrent_step_bf16_state(const void* q, const void* k, const void* v,
+                                                    const float* g, const float* beta,
+                                                    const uint16_t* state_in, uint16_t* state_out,
+                                                    int32_t N, int32_t Nqk, int32_t Nv, int32_t D,
+                                                    gdr_dtype dtype, float scale, uint32_t flags,
+                                                    void* out, void* stream, float* kernel_ms) {
+  StepArgs a{q, k, v, g, beta, state_in, state_out, N, Nqk, Nv, D, dtype, scale, flags, out, true};
+  return step_entry(a, static_cast<hipStream_t>(stream), kernel_ms);
 }
 
 extern "C" const char* gdr_status_string(gdr_status s) {

@@ -4,11 +4,14 @@
 // computed in one pass over S as
 //   a = S_old kh,  b = S_old qh,  delta = beta (v - exp(g) a),
 //   o = exp(g) b + delta (kh . qh),  S_new = exp(g) S_old + delta kh^T.
-// Bandwidth bound: each (sequence, head) state (64 KiB fp32) is read once and
-// written once.  One workgroup of 256 threads per (sequence, head); thread t
-// holds columns 8 (t & 15) .. +7 of rows (t >> 4) + 16 i, i < 8, so each row
-// is 16 consecutive threads reading 512 contiguous bytes, and the two row dot
-// products reduce across those 16 lanes.
+// Bandwidth bound: each (sequence, head) state is read once and written once,
+// 64 KiB in fp32 or 32 KiB when it is stored in bf16 (a bf16 state cache, as
+// the generic "Gated DeltaNet" article's section 6.3 advises; the arithmetic
+// stays fp32 and only the stored state is rounded, to nearest even).  One
+// workgroup of 256 threads per (sequence, head); thread t holds columns
+// 8 (t & 15) .. +7 of rows (t >> 4) + 16 i, i < 8, so each row is 16
+// consecutive threads reading contiguous bytes, and the two row dot products
+// reduce across those 16 lanes.
 #include "gdr_device.h"
 #include "gdr_kernels.h"
 
@@ -30,11 +33,46 @@ __device__ __forceinline__ void load8<__bf16>(const __bf16* p, float* x) {
   for (int e = 0; e < 8; ++e) x[e] = (float)a[e];
 }
 
-template <typename T>
+// Eight consecutive state values of one row: 32 bytes of fp32 or 16 of bf16,
+// moved with non-temporal 16-byte accesses (the state is touched once).
+template <typename ST>
+struct StatePiece;
+template <>
+struct StatePiece<float> {
+  f32x4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+    b = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + 4));
+  }
+  __device__ __forceinline__ float get(int e) const { return e < 4 ? a[e] : b[e - 4]; }
+  __device__ __forceinline__ static void store(float* p, const float* x) {
+    const f32x4 y0 = {x[0], x[1], x[2], x[3]}, y1 = {x[4], x[5], x[6], x[7]};
+    __builtin_nontemporal_store(y0, reinterpret_cast<f32x4*>(p));
+    __builtin_nontemporal_store(y1, reinterpret_cast<f32x4*>(p + 4));
+  }
+};
+template <>
+struct StatePiece<__bf16> {
+  u32x4 raw;
+  __device__ __forceinline__ void load(const __bf16* p) {
+    raw = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  }
+  __device__ __forceinline__ float get(int e) const {
+    return (float)__builtin_bit_cast(bf16x8, raw)[e];
+  }
+  __device__ __forceinline__ static void store(__bf16* p, const float* x) {
+    bf16x8 y;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = (__bf16)x[e];   // round to nearest even
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x4, y), reinterpret_cast<u32x4*>(p));
+  }
+};
+
+template <typename T, typename ST>
 __global__ __launch_bounds__(256) void decode_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                      const T* __restrict__ v, const float* __restrict__ g,
                                                      const float* __restrict__ beta,
-                                                     const float* state_in, float* state_out,
+                                                     const ST* state_in, ST* state_out,
                                                      int32_t Nqk, int32_t Nv, float scale, int norm,
                                                      T* __restrict__ out) {
   const int bh = blockIdx.x;
@@ -44,14 +82,10 @@ __global__ __launch_bounds__(256) void decode_kernel(const T* __restrict__ q, co
   const int cg = tid & 15, rg = tid >> 4;
   const size_t sb = (size_t)bh * kD * kD;
 
-  // issue the state loads first: 16 x 16 bytes in flight per thread
-  f32x4 s[8][2];
+  // issue the state loads first: all of a thread's pieces in flight at once
+  StatePiece<ST> s[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float* p = state_in + sb + (size_t)(rg + 16 * i) * kD + 8 * cg;
-    s[i][0] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
-    s[i][1] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + 4));
-  }
+  for (int i = 0; i < 8; ++i) s[i].load(state_in + sb + (size_t)(rg + 16 * i) * kD + 8 * cg);
 
   const T* kp = k + ((size_t)n * Nqk + j) * kD;
   const T* qp = q + ((size_t)n * Nqk + j) * kD;
@@ -77,8 +111,9 @@ __global__ __launch_bounds__(256) void decode_kernel(const T* __restrict__ q, co
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int row = rg + 16 * i;
-    float x[8] = {s[i][0][0], s[i][0][1], s[i][0][2], s[i][0][3],
-                  s[i][1][0], s[i][1][1], s[i][1][2], s[i][1][3]};
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = s[i].get(e);
     float a = 0.f, b = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) { a += x[e] * kh[e]; b += x[e] * qh[e]; }
@@ -88,28 +123,28 @@ __global__ __launch_bounds__(256) void decode_kernel(const T* __restrict__ q, co
     if (cg == 0) op[row] = from_f32<T>(alpha * b + delta * kq);
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] = alpha * x[e] + delta * kh[e];
-    float* p = state_out + sb + (size_t)row * kD + 8 * cg;
-    const f32x4 y0 = {x[0], x[1], x[2], x[3]}, y1 = {x[4], x[5], x[6], x[7]};
-    __builtin_nontemporal_store(y0, reinterpret_cast<f32x4*>(p));
-    __builtin_nontemporal_store(y1, reinterpret_cast<f32x4*>(p + 4));
+    StatePiece<ST>::store(state_out + sb + (size_t)row * kD + 8 * cg, x);
   }
   (void)l;
 }
 
-template <typename T>
+template <typename T, typename ST>
 void launch_decode(const T* q, const T* k, const T* v, const float* g, const float* beta,
-                   const float* state_in, float* state_out, int32_t N, int32_t Nqk, int32_t Nv,
+                   const ST* state_in, ST* state_out, int32_t N, int32_t Nqk, int32_t Nv,
                    float scale, int norm, T* out, hipStream_t stream, LaunchEvents ev) {
-  hipExtLaunchKernelGGL(decode_kernel<T>, dim3((unsigned)N * (unsigned)Nv), dim3(256), 0, stream,
-                        ev.start, ev.stop, 0, q, k, v, g, beta, state_in, state_out, Nqk, Nv, scale,
-                        norm, out);
+  hipExtLaunchKernelGGL(decode_kernel<T, ST>, dim3((unsigned)N * (unsigned)Nv), dim3(256), 0,
+                        stream, ev.start, ev.stop, 0, q, k, v, g, beta, state_in, state_out, Nqk,
+                        Nv, scale, norm, out);
 }
 
-template void launch_decode<float>(const float*, const float*, const float*, const float*,
-                                   const float*, const float*, float*, int32_t, int32_t, int32_t,
-                                   float, int, float*, hipStream_t, LaunchEvents);
-template void launch_decode<__bf16>(const __bf16*, const __bf16*, const __bf16*, const float*,
-                                    const float*, const float*, float*, int32_t, int32_t, int32_t,
-                                    float, int, __bf16*, hipStream_t, LaunchEvents);
+#define GDR_DECODE_INST(T, ST)                                                                   \
+  template void launch_decode<T, ST>(const T*, const T*, const T*, const float*, const float*,  \
+                                     const ST*, ST*, int32_t, int32_t, int32_t, float, int, T*, \
+                                     hipStream_t, LaunchEvents);
+GDR_DECODE_INST(float, float)
+GDR_DECODE_INST(__bf16, float)
+GDR_DECODE_INST(float, __bf16)
+GDR_DECODE_INST(__bf16, __bf16)
+#undef GDR_DECODE_INST
 
 }  // namespace gdr

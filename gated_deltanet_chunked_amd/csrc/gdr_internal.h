@@ -74,12 +74,13 @@ struct ChunkArgs {
 struct StepArgs {
   const void* q; const void* k; const void* v;
   const float* g; const float* beta;
-  const float* state_in; float* state_out;
+  const void* state_in; void* state_out;   // float, or bf16 when state_bf16
   int32_t N, Nqk, Nv, D;
   gdr_dtype dtype;
   float scale;
   uint32_t flags;
   void* out;
+  bool state_bf16;
 };
 
 gdr_status validate_chunk(const ChunkArgs& a);

@@ -75,9 +75,11 @@ void launch_inter(const Tin* inter, Chunks chunks, const float* gam,
                   int32_t slot0, int32_t nseg, bool first_segment, Tin* out, Tin* discard,
                   hipStream_t stream, LaunchEvents ev = {});
 
-template <typename Tin>
+// One decode step; the state is stored as St (float, or __bf16 for a bf16
+// state cache), the arithmetic is fp32 either way.
+template <typename Tin, typename St>
 void launch_decode(const Tin* q, const Tin* k, const Tin* v, const float* g, const float* beta,
-                   const float* state_in, float* state_out, int32_t N, int32_t Nqk, int32_t Nv,
+                   const St* state_in, St* state_out, int32_t N, int32_t Nqk, int32_t Nv,
                    float scale, int norm, Tin* out, hipStream_t stream, LaunchEvents ev = {});
 
 }  // namespace gdr

@@ -104,7 +104,7 @@ gdr_status validate_step(const StepArgs& a) {
   const int64_t qk_bytes = static_cast<int64_t>(a.N) * a.Nqk * 128 * es;
   const int64_t v_bytes = static_cast<int64_t>(a.N) * a.Nv * 128 * es;
   const int64_t gb_bytes = static_cast<int64_t>(a.N) * a.Nv * 4;
-  const int64_t st_bytes = static_cast<int64_t>(a.N) * a.Nv * 128 * 128 * 4;
+  const int64_t st_bytes = static_cast<int64_t>(a.N) * a.Nv * 128 * 128 * (a.state_bf16 ? 2 : 4);
   struct R { const void* p; int64_t n; } in[] = {
       {a.q, qk_bytes}, {a.k, qk_bytes}, {a.v, v_bytes}, {a.g, gb_bytes}, {a.beta, gb_bytes},
       {a.state_in, st_bytes}, {a.state_out, st_bytes}};

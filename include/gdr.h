@@ -167,6 +167,31 @@ gdr_status gdr_recurrent_step_timed(const void* q, const void* k, const void* v,
                                     gdr_dtype dtype, float scale, uint32_t flags,
                                     void* out, void* stream, float* kernel_ms);
 
+/*
+ * One decode step with the state stored in bfloat16: a bf16 state cache, as
+ * the generic "Gated DeltaNet" article's deployment advice (section 6.3)
+ * names it.  The same rule as gdr_recurrent_step (blog post 5(2)) and the
+ * same arguments, except:
+ *
+ * state_in   [N, Nv, D, D] bfloat16 bit patterns (required)
+ * state_out  [N, Nv, D, D] bfloat16 bit patterns (required); may equal
+ *            state_in for an in-place update, must not overlap it otherwise
+ * kernel_ms  NULL, or where to write the kernel's GPU time (start to end);
+ *            with a pointer the call blocks until the step is done
+ *
+ * The arithmetic is fp32, on the stored bf16 values.  The output comes from
+ * the new state before it is rounded; the new state is rounded to the nearest
+ * bf16 value (ties to even) when it is stored.  Half the state bytes of
+ * gdr_recurrent_step, for the cost of that rounding at every step.  Errors
+ * as for gdr_recurrent_step.
+ */
+gdr_status gdr_recurrent_step_bf16_state(const void* q, const void* k, const void* v,
+                                         const float* g, const float* beta,
+                                         const uint16_t* state_in, uint16_t* state_out,
+                                         int32_t N, int32_t Nqk, int32_t Nv, int32_t D,
+                                         gdr_dtype dtype, float scale, uint32_t flags,
+                                         void* out, void* stream, float* kernel_ms);
+
 /* A static, human-readable name for a status code. */
 const char* gdr_status_string(gdr_status s);
 

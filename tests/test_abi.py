@@ -186,3 +186,32 @@ def test_timed_entry_points_validate_before_launching():
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(RuntimeError):
         gdr.load(str(tmp_path / "missing.so"))
+
+
+def test_bf16_state_step_validates_before_launching():
+    """gdr_recurrent_step_bf16_state: the same checks, with 2-byte states."""
+    import ctypes
+    lib = gdr.load()
+    fb = FakeBuffers(T=2, N=2)
+
+    def call(**over):
+        a = dict(q=fb.addr["q"], k=fb.addr["k"], v=fb.addr["v"], g=fb.addr["g"],
+                 beta=fb.addr["beta"], state_in=fb.addr["state_in"],
+                 state_out=fb.addr["state_out"], N=fb.N, Nqk=fb.Nqk, Nv=fb.Nv, D=128,
+                 dtype=gdr.GDR_BF16, flags=gdr.GDR_FLAG_QK_L2NORM, out=fb.addr["out"], ms=None)
+        a.update(over)
+        return lib.gdr_recurrent_step_bf16_state(
+            a["q"], a["k"], a["v"], a["g"], a["beta"], a["state_in"], a["state_out"], a["N"],
+            a["Nqk"], a["Nv"], a["D"], a["dtype"], 0.1, a["flags"], a["out"], None, a["ms"])
+
+    st_bytes = fb.N * fb.Nv * 128 * 128 * 2
+    assert call(D=64) == UNSUPPORTED
+    assert call(flags=4) == UNSUPPORTED
+    assert call(Nqk=3) == INVALID
+    assert call(state_in=None) == INVALID
+    assert call(state_out=None) == INVALID
+    assert call(state_out=fb.addr["state_in"] + 8) == INVALID                 # misaligned
+    assert call(state_out=fb.addr["state_in"] + st_bytes - 256) == INVALID    # partial overlap
+    assert call(out=fb.addr["state_in"] + st_bytes - 256) == INVALID          # out inside state_in
+    ms = ctypes.c_float(1.0)
+    assert call(N=0, ms=ctypes.byref(ms)) == OK and ms.value == 0.0

@@ -262,3 +262,89 @@ def test_timed_entry_points_match_untimed(lengths):
     torch.cuda.synchronize()
     assert torch.equal(o_a, o_b) and torch.equal(s_a, s_b)
     assert len(tim) == 1 and tim[0][0] == "decode" and tim[0][1] > 0
+
+
+# ------------------------------------------------- decode, bf16 state cache
+
+
+def _bf16_state_step(inp, s_bf16, in_place=True):
+    """One step through gdr_recurrent_step_bf16_state; returns (out, new state)
+    as fp64 arrays (the state's bf16 values exactly)."""
+    import torch
+    t = device_tensors(inp, with_state=False)
+    s_in = s_bf16.clone()
+    s_out = s_in if in_place else torch.empty_like(s_in)
+    out = gdr.recurrent_step(t["q"], t["k"], t["v"], t["g"], t["beta"], s_in, state_out=s_out,
+                             scale=SCALE)
+    torch.cuda.synchronize()
+    if not in_place:
+        assert torch.equal(s_in, s_bf16), "state_in modified by an out-of-place step"
+    return to_f64(out), to_f64(s_out)
+
+
+def _check_rounded_state(got, exact):
+    """The stored state is the new state rounded to bf16.  The kernel rounds
+    its fp32 value, the oracle the exact one, so the two may differ where fp32
+    error moves a value across a rounding boundary: near a tie, or near zero
+    where the update alpha S + delta kh^T cancels.  Rounding is monotone, so
+    every bf16 value the kernel may store lies in [round(x - e), round(x + e)],
+    e bounding the fp32 error (here 1e-5 of the head's largest |S'|, about 100
+    times fp32's error on terms of that size); and such differences must be
+    rare."""
+    import oracle
+    ref = oracle.round_bf16(exact)
+    assert np.array_equal(oracle.round_bf16(got), got), "stored state is not bf16"
+    diff = got != ref
+    frac = float(diff.mean())
+    print(f"state: {diff.sum()} of {diff.size} values round differently ({frac:.2e})")
+    assert frac <= 1e-3
+    e = 1e-5 * np.abs(exact).max(axis=(-2, -1), keepdims=True)
+    lo, hi = oracle.round_bf16(exact - e), oracle.round_bf16(exact + e)
+    bad = (got < lo) | (got > hi)
+    assert not bad.any(), f"{int(bad.sum())} values outside the fp32 error band"
+
+
+@pytest.mark.parametrize("in_place", [True, False])
+def test_decode_bf16_state_config(in_place):
+    """The decode workload (256 sequences, Nqk=16, Nv=32, bf16) with the state
+    stored in bf16 (the workload's states rounded once)."""
+    import oracle
+    import torch
+    inp = config_inputs(4)
+    s0 = torch.from_numpy(inp.state_in).to("cuda:0").to(torch.bfloat16)
+    s0_64 = to_f64(s0)
+    out, st = _bf16_state_step(inp, s0, in_place)
+    ro, exact = oracle.recurrent(inp.q, inp.k, inp.v, inp.g, inp.beta, s0_64, inp.cu_seqlens, SCALE)
+    _assert_close("out", out, ro, TOL["bf16"])
+    _assert_close("state", st, exact, TOL["bf16"])
+    _check_rounded_state(st, exact)
+
+
+def test_decode_bf16_state_fp32_inputs():
+    import oracle
+    import torch
+    inp = make_inputs([1] * 6, 2, 4, dtype="f32", seed=41, state_std=1.0)
+    s0 = torch.from_numpy(inp.state_in).to("cuda:0").to(torch.bfloat16)
+    out, st = _bf16_state_step(inp, s0)
+    ro, exact = oracle.recurrent(inp.q, inp.k, inp.v, inp.g, inp.beta, to_f64(s0), inp.cu_seqlens,
+                                 SCALE)
+    _assert_close("out", out, ro, TOL["f32"])
+    _check_rounded_state(st, exact)
+
+
+def test_decode_bf16_state_chained_steps():
+    """Ten steps in a row, each rounding the stored state, against the
+    oracle's bf16-state step chained the same way."""
+    import oracle
+    import torch
+    steps, N, Nqk, Nv = 10, 8, 2, 4
+    s = torch.from_numpy(make_inputs([1] * N, Nqk, Nv, seed=50, state_std=0.1).state_in)
+    s = s.to("cuda:0").to(torch.bfloat16)
+    ref = to_f64(s)
+    for i in range(steps):
+        inp = make_inputs([1] * N, Nqk, Nv, seed=51 + i, state_std=0.1)
+        out, st = _bf16_state_step(inp, s)
+        ro, ref = oracle.recurrent_step_bf16_state(inp.q, inp.k, inp.v, inp.g, inp.beta, ref, SCALE)
+        _assert_close(f"out step {i}", out, ro, TOL["bf16"])
+        s = torch.from_numpy(st).to("cuda:0").to(torch.bfloat16)
+    _assert_close("state after 10 steps", st, ref, TOL["bf16"])
