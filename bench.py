@@ -17,7 +17,8 @@ kernel trace reports), from which the decode step's GB/s and the rooflines
 are computed.  ``ms_per_step`` is the host wall clock of a whole step.  After
 the timed steps the decode step is also measured with its state stored in
 bf16 (``gdr_recurrent_step_bf16_state``, half the state bytes), reported as
-``decode_bf16_state``; it is not part of the step.  One JSON line is printed.
+``decode_bf16_state``, and ``gdr_recurrent_multi`` on 256 sequences x 4 tokens
+as ``multi_token``; neither is part of the step.  One JSON line is printed.
 """
 from __future__ import annotations
 
@@ -57,6 +58,18 @@ def alg_bytes_decode(N, Nqk, Nv, es=2, state_es=4):
     gb = N * Nv * 4 * 2
     out = N * Nv * D * es
     return state + qkv + gb + out
+
+
+MULTI_TOKENS = 4
+
+
+def alg_bytes_multi(N, tokens, Nqk, Nv, es=2):
+    """One read and one write of every fp32 state, plus per token the decode
+    step's bytes: q and k once per q/k head, v and out per value head, g and
+    beta."""
+    state = N * Nv * D * D * 4 * 2
+    per_tok = (2 * Nqk * D + Nv * D + Nv * D) * es + Nv * 4 * 2
+    return state + N * tokens * per_tok
 
 
 def measured_traffic(kernel: str):
@@ -215,6 +228,25 @@ def main() -> int:
     bdec_bytes = alg_bytes_decode(dec.N, dec.Nqk, dec.Nv, state_es=2)
     bdec_gbps = bdec_bytes / bdec_s / 1e9
 
+    # ---- several tokens per sequence (gdr_recurrent_multi): 256 sequences x 4
+    # tokens, the decode heads, fp32 states updated in place; measured after
+    # the timed steps and reported beside them
+    from gated_deltanet_chunked_amd.inputs import make_inputs
+    mt = make_inputs([MULTI_TOKENS] * dec.N, dec.Nqk, dec.Nv, seed=4, state_std=0.01)
+    M = to_dev(mt)
+    mout = torch.empty((mt.T, mt.Nv, D), dtype=M["q"].dtype, device=dev)
+    for _ in range(args.warmup):
+        gdr.recurrent_multi(M["q"], M["k"], M["v"], M["g"], M["beta"], M["cu"], M["s0"],
+                            scale=scale, out=mout, state_out=M["s0"])
+    mtim = []
+    for _ in range(args.steps):
+        gdr.recurrent_multi(M["q"], M["k"], M["v"], M["g"], M["beta"], M["cu"], M["s0"],
+                            scale=scale, out=mout, state_out=M["s0"], timings=mtim)
+    torch.cuda.synchronize()
+    multi_s = float(np.mean([ms for _, ms in mtim])) * 1e-3
+    multi_bytes = alg_bytes_multi(mt.N, MULTI_TOKENS, mt.Nqk, mt.Nv)
+    multi_gbps = multi_bytes / multi_s / 1e9
+
     res = {
         "metric": "chunk GDR fwd tokens/s + % MFMA peak; decode-step GB/s (% HBM peak)",
         "value": round(tok_s, 1),
@@ -250,6 +282,11 @@ def main() -> int:
         "decode_bf16_state": {"gpu_ms": round(bdec_s * 1e3, 4), "gbps": round(bdec_gbps, 1),
                               "frac_hbm_peak": round(bdec_gbps / HBM_PEAK_GBPS, 4),
                               "tokens_per_s": round(dec.N / bdec_s, 1), "alg_bytes": bdec_bytes},
+        "multi_token": {"workload": f"{mt.N} sequences x {MULTI_TOKENS} tokens, Nqk={mt.Nqk} "
+                                    f"Nv={mt.Nv} bf16, fp32 states in place",
+                        "gpu_ms": round(multi_s * 1e3, 4), "gbps": round(multi_gbps, 1),
+                        "frac_hbm_peak": round(multi_gbps / HBM_PEAK_GBPS, 4),
+                        "tokens_per_s": round(mt.T / multi_s, 1), "alg_bytes": multi_bytes},
         "roofline": roof,
     }
 

@@ -67,6 +67,10 @@ def load(path: str = LIB_PATH):
     lib.gdr_recurrent_step_timed.restype = ctypes.c_int
     lib.gdr_recurrent_step_bf16_state.argtypes = lib.gdr_recurrent_step_timed.argtypes
     lib.gdr_recurrent_step_bf16_state.restype = ctypes.c_int
+    lib.gdr_recurrent_multi.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                        ctypes.c_int, f32, u32, vp, vp, vp,
+                                        ctypes.POINTER(ctypes.c_float)]
+    lib.gdr_recurrent_multi.restype = ctypes.c_int
     lib.gdr_status_string.argtypes = [ctypes.c_int]
     lib.gdr_status_string.restype = ctypes.c_char_p
     lib.gdr_version.argtypes = []
@@ -175,6 +179,51 @@ def chunk_fwd(q, k, v, g, beta, cu_seqlens, state_in=None, *, scale: Optional[fl
         raise GdrError(st, "gdr_chunk_fwd_timed")
     timings.extend((STAGE_NAMES.get(kind[i], str(kind[i])), float(ms[i])) for i in range(n.value))
     timings.append(("span", float(span.value)))
+    return out, state_out
+
+
+def recurrent_multi(q, k, v, g, beta, cu_seqlens, state_in=None, *, scale: Optional[float] = None,
+                    out=None, state_out=None, want_state: bool = True, l2norm: bool = True,
+                    timings: Optional[list] = None):
+    """A few tokens per sequence, token by token (``gdr_recurrent_multi``).
+
+    Same arguments and results as ``chunk_fwd`` (packed q, k [T, Nqk, 128],
+    v [T, Nv, 128]; g, beta [T, Nv]; cu_seqlens [N + 1] int32 on the device;
+    state_in [N, Nv, 128, 128] f32 or None), without a workspace.  With a list
+    as ``timings`` the call waits for the kernel and appends ("multi", ms).
+    """
+    import torch
+    lib = load()
+    T, Nqk, _ = q.shape
+    Nv = v.shape[1]
+    N = cu_seqlens.shape[0] - 1
+    dev = q.device
+    dt = q.dtype
+    code = _dtype_code(q)
+    _check(q, "q", (T, Nqk, D), dt, dev)
+    _check(k, "k", (T, Nqk, D), dt, dev)
+    _check(v, "v", (T, Nv, D), dt, dev)
+    _check(g, "g", (T, Nv), torch.float32, dev)
+    _check(beta, "beta", (T, Nv), torch.float32, dev)
+    _check(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32, dev)
+    _check(state_in, "state_in", (N, Nv, D, D), torch.float32, dev)
+    if out is None:
+        out = torch.empty((T, Nv, D), dtype=dt, device=dev)
+    _check(out, "out", (T, Nv, D), dt, dev)
+    if state_out is None and want_state:
+        state_out = torch.empty((N, Nv, D, D), dtype=torch.float32, device=dev)
+    _check(state_out, "state_out", (N, Nv, D, D), torch.float32, dev)
+    if scale is None:
+        scale = D ** -0.5
+    ms = ctypes.c_float(0.0)
+    st = lib.gdr_recurrent_multi(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_in),
+                                 _ptr(cu_seqlens), N, T, Nqk, Nv, D, code, float(scale),
+                                 GDR_FLAG_QK_L2NORM if l2norm else 0, _ptr(out), _ptr(state_out),
+                                 _stream(), ctypes.byref(ms) if timings is not None else None)
+    if st != 0:
+        raise GdrError(st, "gdr_recurrent_multi")
+    if timings is not None:
+        timings.append(("multi", float(ms.value)))
     return out, state_out
 
 

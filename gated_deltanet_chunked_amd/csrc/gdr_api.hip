@@ -225,6 +225,41 @@ extern "C" gdr_status gdr_recurrent_step_bf16_state(const void* q, const void* k
   return step_entry(a, static_cast<hipStream_t>(stream), kernel_ms);
 }
 
+extern "C" gdr_status gdr_recurrent_multi(const void* q, const void* k, const void* v,
+                                          const float* g, const float* beta, const float* state_in,
+                                          const int32_t* cu_seqlens, int32_t N, int32_t T,
+                                          int32_t Nqk, int32_t Nv, int32_t D, gdr_dtype dtype,
+                                          float scale, uint32_t flags, void* out,
+                                          float* state_out, void* stream, float* kernel_ms) {
+  ChunkArgs a{q, k, v, g, beta, state_in, cu_seqlens, N, T, Nqk, Nv, D, dtype, scale, flags,
+              out, state_out, nullptr, 0, true};
+  gdr_status s = validate_chunk(a);
+  if (s != GDR_OK) return s;
+  if (kernel_ms) *kernel_ms = 0.0f;
+  if (T == 0 && !state_out) return GDR_OK;   // nothing to write
+  EventPairs pairs;
+  LaunchEvents ev{};
+  if (kernel_ms) {
+    if (!pairs.create(1)) return GDR_ERR_HIP;
+    ev = LaunchEvents{pairs.ev[0], pairs.ev[1]};
+  }
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const int norm = (flags & GDR_FLAG_QK_L2NORM) ? 1 : 0;
+  if (dtype == GDR_BF16)
+    launch_multi<__bf16>(static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
+                         static_cast<const __bf16*>(v), g, beta, state_in, cu_seqlens, N, T,
+                         state_out, Nqk, Nv, scale, norm, static_cast<__bf16*>(out), st, ev);
+  else
+    launch_multi<float>(static_cast<const float*>(q), static_cast<const float*>(k),
+                        static_cast<const float*>(v), g, beta, state_in, cu_seqlens, N, T,
+                        state_out, Nqk, Nv, scale, norm, static_cast<float*>(out), st, ev);
+  if (hipGetLastError() != hipSuccess) return GDR_ERR_HIP;
+  if (kernel_ms && (hipEventSynchronize(pairs.ev[1]) != hipSuccess ||
+                    hipEventElapsedTime(kernel_ms, pairs.ev[0], pairs.ev[1]) != hipSuccess))
+    return GDR_ERR_HIP;
+  return GDR_OK;
+}
+
 extern "C" const char* gdr_status_string(gdr_status s) {
   switch (s) {
     case GDR_OK: return "ok";

@@ -128,6 +128,123 @@ __global__ __launch_bounds__(256) void decode_kernel(const T* __restrict__ q, co
   (void)l;
 }
 
+// A few tokens per sequence (blog post section 5(2), the token loop run over
+// each sequence of a packed batch): the decode step above applied to the
+// tokens of sequence n in order, with the state kept in registers in between,
+// so S is read once and written once per call whatever the number of tokens.
+// Sequence n owns tokens [cu[n], cu[n+1]), clamped into [0, T] so a malformed
+// cu_seqlens can only give wrong numbers, never an access outside the caller's
+// buffers.  NULL state_in means zeros; NULL state_out skips the final store.
+// The next token's operands are loaded while the current one is applied.
+template <typename T>
+__global__ __launch_bounds__(256) void multi_kernel(const T* __restrict__ q, const T* __restrict__ k,
+                                                    const T* __restrict__ v, const float* __restrict__ g,
+                                                    const float* __restrict__ beta,
+                                                    const float* state_in, const int32_t* __restrict__ cu,
+                                                    int32_t T_total, float* state_out, int32_t Nqk,
+                                                    int32_t Nv, float scale, int norm, T* __restrict__ out) {
+  const int bh = blockIdx.x;
+  const int n = bh / Nv, h = bh % Nv;
+  const int j = h / (Nv / Nqk);
+  const int tid = threadIdx.x;
+  const int cg = tid & 15, rg = tid >> 4;
+  const size_t sb = (size_t)bh * kD * kD;
+  const int lo = min(max(cu[n], 0), T_total);
+  const int hi = min(max(cu[n + 1], lo), T_total);
+
+  float x[8][8];
+  if (state_in) {
+    StatePiece<float> s[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s[i].load(state_in + sb + (size_t)(rg + 16 * i) * kD + 8 * cg);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[i][e] = s[i].get(e);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[i][e] = 0.f;
+  }
+
+  // operands of one token: this lane's 8 columns of k and q, the value
+  // entries of its 8 rows, the gate and beta
+  struct Tok {
+    float kk[8], qq[8], vv[8], gg, bb;
+  };
+  auto fetch = [&](int t, Tok& o) {
+    const T* kp = k + ((size_t)t * Nqk + j) * kD + 8 * cg;
+    const T* qp = q + ((size_t)t * Nqk + j) * kD + 8 * cg;
+    load8<T>(kp, o.kk);
+    load8<T>(qp, o.qq);
+    const T* vp = v + ((size_t)t * Nv + h) * kD;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o.vv[i] = to_f32(vp[rg + 16 * i]);
+    o.gg = g[(size_t)t * Nv + h];
+    o.bb = beta[(size_t)t * Nv + h];
+  };
+
+  Tok cur;
+  if (lo < hi) fetch(lo, cur);
+#pragma unroll 1
+  for (int t = lo; t < hi; ++t) {
+    Tok nxt;
+    fetch(min(t + 1, hi - 1), nxt);   // the last token fetches itself again: in bounds
+    float ssk = 0.f, ssq = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) { ssk += cur.kk[e] * cur.kk[e]; ssq += cur.qq[e] * cur.qq[e]; }
+    ssk = group16_sum(ssk);
+    ssq = group16_sum(ssq);
+    const float rk = norm ? 1.0f / sqrtf(ssk + 1e-6f) : 1.0f;
+    const float rq = (norm ? 1.0f / sqrtf(ssq + 1e-6f) : 1.0f) * scale;
+    float kh[8], qh[8], kq = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) { kh[e] = cur.kk[e] * rk; qh[e] = cur.qq[e] * rq; kq += kh[e] * qh[e]; }
+    kq = group16_sum(kq);
+    const float alpha = expf(cur.gg);
+    T* op = out + ((size_t)t * Nv + h) * kD;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float a = 0.f, b = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) { a += x[i][e] * kh[e]; b += x[i][e] * qh[e]; }
+      a = group16_sum(a);
+      b = group16_sum(b);
+      const float delta = cur.bb * (cur.vv[i] - alpha * a);
+      if (cg == 0) op[rg + 16 * i] = from_f32<T>(alpha * b + delta * kq);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[i][e] = alpha * x[i][e] + delta * kh[e];
+    }
+    cur = nxt;
+  }
+
+  if (state_out) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      StatePiece<float>::store(state_out + sb + (size_t)(rg + 16 * i) * kD + 8 * cg, x[i]);
+  }
+}
+
+template <typename T>
+void launch_multi(const T* q, const T* k, const T* v, const float* g, const float* beta,
+                  const float* state_in, const int32_t* cu, int32_t N, int32_t T_total,
+                  float* state_out, int32_t Nqk, int32_t Nv, float scale, int norm, T* out,
+                  hipStream_t stream, LaunchEvents ev) {
+  hipExtLaunchKernelGGL(multi_kernel<T>, dim3((unsigned)N * (unsigned)Nv), dim3(256), 0, stream,
+                        ev.start, ev.stop, 0, q, k, v, g, beta, state_in, cu, T_total, state_out,
+                        Nqk, Nv, scale, norm, out);
+}
+
+template void launch_multi<float>(const float*, const float*, const float*, const float*,
+                                  const float*, const float*, const int32_t*, int32_t, int32_t,
+                                  float*, int32_t, int32_t, float, int, float*, hipStream_t,
+                                  LaunchEvents);
+template void launch_multi<__bf16>(const __bf16*, const __bf16*, const __bf16*, const float*,
+                                   const float*, const float*, const int32_t*, int32_t, int32_t,
+                                   float*, int32_t, int32_t, float, int, __bf16*, hipStream_t,
+                                   LaunchEvents);
+
 template <typename T, typename ST>
 void launch_decode(const T* q, const T* k, const T* v, const float* g, const float* beta,
                    const ST* state_in, ST* state_out, int32_t N, int32_t Nqk, int32_t Nv,

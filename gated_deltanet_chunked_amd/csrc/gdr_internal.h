@@ -69,6 +69,7 @@ struct ChunkArgs {
   uint32_t flags;
   void* out; float* state_out;
   void* workspace; size_t workspace_bytes;
+  bool no_workspace;   // gdr_recurrent_multi: the same arguments, no workspace
 };
 
 struct StepArgs {

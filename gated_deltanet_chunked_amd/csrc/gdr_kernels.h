@@ -82,4 +82,12 @@ void launch_decode(const Tin* q, const Tin* k, const Tin* v, const float* g, con
                    const St* state_in, St* state_out, int32_t N, int32_t Nqk, int32_t Nv,
                    float scale, int norm, Tin* out, hipStream_t stream, LaunchEvents ev = {});
 
+// Several tokens per sequence, token by token with the state in registers;
+// sequence n owns tokens [cu[n], cu[n+1]) of the packed batch.
+template <typename Tin>
+void launch_multi(const Tin* q, const Tin* k, const Tin* v, const float* g, const float* beta,
+                  const float* state_in, const int32_t* cu, int32_t N, int32_t T_total,
+                  float* state_out, int32_t Nqk, int32_t Nv, float scale, int norm, Tin* out,
+                  hipStream_t stream, LaunchEvents ev = {});
+
 }  // namespace gdr

@@ -53,14 +53,18 @@ gdr_status validate_chunk(const ChunkArgs& a) {
   // every element offset must fit comfortably in 63 bits; the kernels also
   // index tokens with 32-bit integers
   if (static_cast<int64_t>(a.T) * a.Nv > (int64_t(1) << 40)) return GDR_ERR_INVALID_ARGUMENT;
-  if (!a.cu_seqlens || !a.workspace) return GDR_ERR_INVALID_ARGUMENT;
+  if (a.no_workspace && static_cast<int64_t>(a.N) * a.Nv > (int64_t(1) << 31) / 4)
+    return GDR_ERR_INVALID_ARGUMENT;   // one workgroup per (sequence, head)
+  if (!a.cu_seqlens || (!a.workspace && !a.no_workspace)) return GDR_ERR_INVALID_ARGUMENT;
   if (a.T > 0 && (!a.q || !a.k || !a.v || !a.g || !a.beta || !a.out)) return GDR_ERR_INVALID_ARGUMENT;
   const void* ptrs[] = {a.q, a.k, a.v, a.g, a.beta, a.state_in, a.cu_seqlens, a.out, a.state_out};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return GDR_ERR_INVALID_ARGUMENT;
-  if ((reinterpret_cast<uintptr_t>(a.workspace) & 255u) != 0) return GDR_ERR_INVALID_ARGUMENT;
-  const Workspace w = plan_workspace(a.T, a.N, a.Nqk, a.Nv, a.dtype);
-  if (a.workspace_bytes < static_cast<size_t>(w.total)) return GDR_ERR_WORKSPACE_TOO_SMALL;
+  if (!a.no_workspace) {
+    if ((reinterpret_cast<uintptr_t>(a.workspace) & 255u) != 0) return GDR_ERR_INVALID_ARGUMENT;
+    const Workspace w = plan_workspace(a.T, a.N, a.Nqk, a.Nv, a.dtype);
+    if (a.workspace_bytes < static_cast<size_t>(w.total)) return GDR_ERR_WORKSPACE_TOO_SMALL;
+  }
 
   const int64_t es = static_cast<int64_t>(dtype_size(a.dtype));
   const int64_t qk_bytes = static_cast<int64_t>(a.T) * a.Nqk * 128 * es;

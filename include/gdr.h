@@ -16,6 +16,9 @@
  *                         chunkwise form with chunk length 128 (blog post
  *                         section 5(1); operator page "chunk_gated_delta_rule");
  *   gdr_recurrent_step -- decode: one token per sequence (blog post 5(2)).
+ * and two variants of the token loop:
+ *   gdr_recurrent_step_bf16_state -- decode with the state stored in bf16;
+ *   gdr_recurrent_multi           -- a few tokens per sequence, token by token.
  *
  * Conventions shared by all calls:
  *   - All tensor pointers are DEVICE pointers, caller-owned, contiguous,
@@ -191,6 +194,28 @@ gdr_status gdr_recurrent_step_bf16_state(const void* q, const void* k, const voi
                                          int32_t N, int32_t Nqk, int32_t Nv, int32_t D,
                                          gdr_dtype dtype, float scale, uint32_t flags,
                                          void* out, void* stream, float* kernel_ms);
+
+/*
+ * Several tokens per sequence, token by token (blog post 5(2), the token loop
+ * run over each sequence): for batches of short sequences, e.g. a few tokens
+ * per sequence when verifying speculative tokens, where chunks of 128 would
+ * be mostly padding.  Same arguments, layouts and results as gdr_chunk_fwd
+ * (packed tokens, cu_seqlens in device memory, NULL state_in = zeros, NULL
+ * state_out = final state not written, state_out may equal state_in), but no
+ * workspace.  One workgroup per (sequence, value head) keeps its state in
+ * registers across the sequence's tokens, so the state is read and written
+ * once per call.  Any sequence length works; its time grows linearly with the
+ * longest sequence, so long sequences belong to gdr_chunk_fwd.
+ * kernel_ms: NULL, or where to write the kernel's GPU time (the call then
+ * blocks until the kernel ends).  Errors as for gdr_chunk_fwd, plus
+ * GDR_ERR_INVALID_ARGUMENT when N * Nv > 2^29.
+ */
+gdr_status gdr_recurrent_multi(const void* q, const void* k, const void* v,
+                               const float* g, const float* beta,
+                               const float* state_in, const int32_t* cu_seqlens,
+                               int32_t N, int32_t T, int32_t Nqk, int32_t Nv, int32_t D,
+                               gdr_dtype dtype, float scale, uint32_t flags,
+                               void* out, float* state_out, void* stream, float* kernel_ms);
 
 /* A static, human-readable name for a status code. */
 const char* gdr_status_string(gdr_status s);

@@ -215,3 +215,38 @@ def test_bf16_state_step_validates_before_launching():
     assert call(out=fb.addr["state_in"] + st_bytes - 256) == INVALID          # out inside state_in
     ms = ctypes.c_float(1.0)
     assert call(N=0, ms=ctypes.byref(ms)) == OK and ms.value == 0.0
+
+
+def test_multi_token_validates_before_launching():
+    """gdr_recurrent_multi: the checks of gdr_chunk_fwd, without a workspace."""
+    import ctypes
+    lib = gdr.load()
+    fb = FakeBuffers()
+
+    def call(**over):
+        a = dict(q=fb.addr["q"], k=fb.addr["k"], v=fb.addr["v"], g=fb.addr["g"],
+                 beta=fb.addr["beta"], state_in=fb.addr["state_in"], cu=fb.addr["cu"], N=fb.N,
+                 T=fb.T, Nqk=fb.Nqk, Nv=fb.Nv, D=128, dtype=gdr.GDR_BF16,
+                 flags=gdr.GDR_FLAG_QK_L2NORM, out=fb.addr["out"],
+                 state_out=fb.addr["state_out"], ms=None)
+        a.update(over)
+        return lib.gdr_recurrent_multi(a["q"], a["k"], a["v"], a["g"], a["beta"], a["state_in"],
+                                       a["cu"], a["N"], a["T"], a["Nqk"], a["Nv"], a["D"],
+                                       a["dtype"], 0.1, a["flags"], a["out"], a["state_out"], None,
+                                       a["ms"])
+
+    assert call(D=64) == UNSUPPORTED
+    assert call(dtype=9) == UNSUPPORTED
+    assert call(flags=2) == UNSUPPORTED
+    assert call(Nqk=3) == INVALID
+    assert call(N=0) == INVALID
+    assert call(T=-1) == INVALID
+    assert call(cu=None) == INVALID
+    assert call(q=None) == INVALID
+    assert call(out=None) == INVALID
+    assert call(q=fb.addr["q"] + 8) == INVALID                       # misaligned
+    assert call(out=fb.addr["v"]) == INVALID                         # out aliases v
+    assert call(state_out=fb.addr["state_in"] + 4096) == INVALID     # partial overlap
+    assert call(N=1 << 20, Nqk=1, Nv=1024) == INVALID                # too many workgroups
+    ms = ctypes.c_float(1.0)
+    assert call(T=0, state_out=None, ms=ctypes.byref(ms)) == OK and ms.value == 0.0

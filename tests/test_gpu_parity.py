@@ -348,3 +348,66 @@ def test_decode_bf16_state_chained_steps():
         _assert_close(f"out step {i}", out, ro, TOL["bf16"])
         s = torch.from_numpy(st).to("cuda:0").to(torch.bfloat16)
     _assert_close("state after 10 steps", st, ref, TOL["bf16"])
+
+
+# ------------------------------------------- several tokens per sequence
+
+
+def _multi(inp, state="in", want_state=True, l2norm=True, in_place=False):
+    import torch
+    t = device_tensors(inp)
+    s_in = t["state_in"] if state == "in" else None
+    s_out = s_in if (in_place and s_in is not None) else None
+    out, st = gdr.recurrent_multi(t["q"], t["k"], t["v"], t["g"], t["beta"], t["cu"], s_in,
+                                  scale=SCALE, state_out=s_out, want_state=want_state,
+                                  l2norm=l2norm)
+    torch.cuda.synchronize()
+    return to_f64(out), (to_f64(st) if st is not None else None)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_multi_token_ragged(dtype):
+    """Short packed sequences (0 to 16 tokens), the verification shape of
+    speculative decoding, with initial states."""
+    inp = make_inputs([3, 1, 0, 16, 7, 2, 5, 4], 2, 4, dtype=dtype, seed=61, state_std=0.5)
+    out, st = _multi(inp)
+    ro, rs = oracle_full(inp)
+    _assert_close("out", out, ro, TOL[dtype])
+    _assert_close("state", st, rs, TOL[dtype])
+
+
+def test_multi_token_no_states_and_no_norm():
+    inp = make_inputs([5, 9, 1], 1, 2, dtype="f32", seed=62, state_std=0.5)
+    out, st = _multi(inp, state=None, want_state=False, l2norm=False)
+    assert st is None
+    ro, _ = oracle_full(inp, state_in=None, l2norm=False)
+    _assert_close("out", out, ro, TOL["f32"])
+
+
+def test_multi_token_in_place_and_long_sequence():
+    """The state updated in place; one sequence far longer than the loop is
+    meant for (still exact, only slower)."""
+    inp = make_inputs([300, 2], 2, 4, dtype="bf16", seed=63, state_std=0.5)
+    out, st = _multi(inp, in_place=True)
+    ro, rs = oracle_full(inp)
+    _assert_close("out", out, ro, TOL["bf16"])
+    _assert_close("state", st, rs, TOL["bf16"])
+
+
+def test_multi_token_verification_workload():
+    """256 sequences x 4 tokens, Nqk=16, Nv=32, bf16, fp32 states: the decode
+    workload with four tokens per sequence, compared in full."""
+    inp = make_inputs([4] * 256, 16, 32, dtype="bf16", seed=64, state_std=0.01)
+    out, st = _multi(inp)
+    ro, rs = oracle_full(inp)
+    _assert_close("out", out, ro, TOL["bf16"])
+    _assert_close("state", st, rs, TOL["bf16"])
+
+
+def test_multi_token_matches_chunk_fwd():
+    """The token loop and the chunkwise form agree on the same packed batch."""
+    inp = make_inputs([16, 3, 11, 8], 2, 4, dtype="f32", seed=65, state_std=0.5)
+    o_m, s_m = _multi(inp)
+    o_c, s_c = _chunk(inp)
+    _assert_close("out", o_m, o_c, TOL["f32"])
+    _assert_close("state", s_m, s_c, TOL["f32"])
