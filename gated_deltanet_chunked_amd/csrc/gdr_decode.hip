@@ -8,63 +8,83 @@
 // 64 KiB in fp32 or 32 KiB when it is stored in bf16 (a bf16 state cache, as
 // the generic "Gated DeltaNet" article's section 6.3 advises; the arithmetic
 // stays fp32 and only the stored state is rounded, to nearest even).  One
-// workgroup of 256 threads per (sequence, head); thread t holds columns
-// 8 (t & 15) .. +7 of rows (t >> 4) + 16 i, i < 8, so each row is 16
-// consecutive threads reading contiguous bytes, and the two row dot products
-// reduce across those 16 lanes.
+// workgroup of 256 threads per (sequence, head); thread t holds 8 columns of
+// rows (t >> 4) + 16 i, i < 8, so each row belongs to 16 consecutive threads
+// and the two row dot products reduce across those 16 lanes.  Which columns
+// (piece_col) is chosen so that every 16-byte access of the 16 lanes covers
+// contiguous whole lines: with bf16 states a lane's 8 columns are one 16-byte
+// piece; with fp32 states they are two 4-column pieces, one in each half of
+// the row (two separate 16-byte pieces side by side would leave every store
+// instruction covering alternate halves of 32-byte sectors).
 #include "gdr_device.h"
 #include "gdr_kernels.h"
 
 namespace gdr {
 
-template <typename T>
-__device__ __forceinline__ void load8(const T* p, float* x);
-template <>
-__device__ __forceinline__ void load8<float>(const float* p, float* x) {
-  const float4 a = *reinterpret_cast<const float4*>(p);
-  const float4 b = *reinterpret_cast<const float4*>(p + 4);
-  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
-}
-template <>
-__device__ __forceinline__ void load8<__bf16>(const __bf16* p, float* x) {
-  const bf16x8 a = *reinterpret_cast<const bf16x8*>(p);
-#pragma unroll
-  for (int e = 0; e < 8; ++e) x[e] = (float)a[e];
+// First column of half `half` (0 or 1) of the 8 columns lane cg (0..15) of a
+// row group holds: element e of the lane is column piece_col(cg, e / 4) + e % 4.
+template <typename ST>
+__device__ __forceinline__ int piece_col(int cg, int half) {
+  return sizeof(ST) == 4 ? 4 * cg + 64 * half : 8 * cg + 4 * half;
 }
 
-// Eight consecutive state values of one row: 32 bytes of fp32 or 16 of bf16,
-// moved with non-temporal 16-byte accesses (the state is touched once).
+template <typename T>
+__device__ __forceinline__ void load4(const T* p, float* x);
+template <>
+__device__ __forceinline__ void load4<float>(const float* p, float* x) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+}
+template <>
+__device__ __forceinline__ void load4<__bf16>(const __bf16* p, float* x) {
+  typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+  const bf16x4 a = *reinterpret_cast<const bf16x4*>(p);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) x[e] = (float)a[e];
+}
+
+// The 8 values of a row of q, k (D entries, type T) at the columns lane cg
+// holds for state storage ST.
+template <typename T, typename ST>
+__device__ __forceinline__ void load_cols(const T* row, int cg, float* x) {
+  load4<T>(row + piece_col<ST>(cg, 0), x);
+  load4<T>(row + piece_col<ST>(cg, 1), x + 4);
+}
+
+// The 8 state values of one row that lane cg holds (columns as piece_col):
+// two 16-byte pieces of fp32 or one of bf16, moved with non-temporal accesses
+// (the state is touched once).
 template <typename ST>
 struct StatePiece;
 template <>
 struct StatePiece<float> {
   f32x4 a, b;
-  __device__ __forceinline__ void load(const float* p) {
-    a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
-    b = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + 4));
+  __device__ __forceinline__ void load(const float* row, int cg) {
+    a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row + piece_col<float>(cg, 0)));
+    b = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row + piece_col<float>(cg, 1)));
   }
   __device__ __forceinline__ float get(int e) const { return e < 4 ? a[e] : b[e - 4]; }
-  __device__ __forceinline__ static void store(float* p, const float* x) {
+  __device__ __forceinline__ static void store(float* row, int cg, const float* x) {
     const f32x4 y0 = {x[0], x[1], x[2], x[3]}, y1 = {x[4], x[5], x[6], x[7]};
-    __builtin_nontemporal_store(y0, reinterpret_cast<f32x4*>(p));
-    __builtin_nontemporal_store(y1, reinterpret_cast<f32x4*>(p + 4));
+    __builtin_nontemporal_store(y0, reinterpret_cast<f32x4*>(row + piece_col<float>(cg, 0)));
+    __builtin_nontemporal_store(y1, reinterpret_cast<f32x4*>(row + piece_col<float>(cg, 1)));
   }
 };
 template <>
 struct StatePiece<__bf16> {
   u32x4 raw;
-  __device__ __forceinline__ void load(const __bf16* p) {
-    raw = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  __device__ __forceinline__ void load(const __bf16* row, int cg) {
+    raw = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + piece_col<__bf16>(cg, 0)));
   }
   __device__ __forceinline__ float get(int e) const {
     return (float)__builtin_bit_cast(bf16x8, raw)[e];
   }
-  __device__ __forceinline__ static void store(__bf16* p, const float* x) {
+  __device__ __forceinline__ static void store(__bf16* row, int cg, const float* x) {
     bf16x8 y;
 #pragma unroll
     for (int e = 0; e < 8; ++e) y[e] = (__bf16)x[e];   // round to nearest even
-    __builtin_nontemporal_store(__builtin_bit_cast(u32x4, y), reinterpret_cast<u32x4*>(p));
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x4, y),
+                                reinterpret_cast<u32x4*>(row + piece_col<__bf16>(cg, 0)));
   }
 };
 
@@ -85,13 +105,13 @@ __global__ __launch_bounds__(256) void decode_kernel(const T* __restrict__ q, co
   // issue the state loads first: all of a thread's pieces in flight at once
   StatePiece<ST> s[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) s[i].load(state_in + sb + (size_t)(rg + 16 * i) * kD + 8 * cg);
+  for (int i = 0; i < 8; ++i) s[i].load(state_in + sb + (size_t)(rg + 16 * i) * kD, cg);
 
   const T* kp = k + ((size_t)n * Nqk + j) * kD;
   const T* qp = q + ((size_t)n * Nqk + j) * kD;
   float kh[8], qh[8];
-  load8<T>(kp + 8 * cg, kh);
-  load8<T>(qp + 8 * cg, qh);
+  load_cols<T, ST>(kp, cg, kh);
+  load_cols<T, ST>(qp, cg, qh);
   float ssk = 0.f, ssq = 0.f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) { ssk += kh[e] * kh[e]; ssq += qh[e] * qh[e]; }
@@ -123,7 +143,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const T* __restrict__ q, co
     if (cg == 0) op[row] = from_f32<T>(alpha * b + delta * kq);
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] = alpha * x[e] + delta * kh[e];
-    StatePiece<ST>::store(state_out + sb + (size_t)row * kD + 8 * cg, x);
+    StatePiece<ST>::store(state_out + sb + (size_t)row * kD, cg, x);
   }
   (void)l;
 }
@@ -156,7 +176,7 @@ __global__ __launch_bounds__(256) void multi_kernel(const T* __restrict__ q, con
   if (state_in) {
     StatePiece<float> s[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) s[i].load(state_in + sb + (size_t)(rg + 16 * i) * kD + 8 * cg);
+    for (int i = 0; i < 8; ++i) s[i].load(state_in + sb + (size_t)(rg + 16 * i) * kD, cg);
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
@@ -174,10 +194,8 @@ __global__ __launch_bounds__(256) void multi_kernel(const T* __restrict__ q, con
     float kk[8], qq[8], vv[8], gg, bb;
   };
   auto fetch = [&](int t, Tok& o) {
-    const T* kp = k + ((size_t)t * Nqk + j) * kD + 8 * cg;
-    const T* qp = q + ((size_t)t * Nqk + j) * kD + 8 * cg;
-    load8<T>(kp, o.kk);
-    load8<T>(qp, o.qq);
+    load_cols<T, float>(k + ((size_t)t * Nqk + j) * kD, cg, o.kk);
+    load_cols<T, float>(q + ((size_t)t * Nqk + j) * kD, cg, o.qq);
     const T* vp = v + ((size_t)t * Nv + h) * kD;
 #pragma unroll
     for (int i = 0; i < 8; ++i) o.vv[i] = to_f32(vp[rg + 16 * i]);
@@ -222,7 +240,7 @@ __global__ __launch_bounds__(256) void multi_kernel(const T* __restrict__ q, con
   if (state_out) {
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      StatePiece<float>::store(state_out + sb + (size_t)(rg + 16 * i) * kD + 8 * cg, x[i]);
+      StatePiece<float>::store(state_out + sb + (size_t)(rg + 16 * i) * kD, cg, x[i]);
   }
 }
 
