@@ -10,7 +10,9 @@ same rule (the DeltaNet matrix form and the chunkwise form of section 5(1)),
 used only to pin ``recurrent`` in the oracle's own tests.
 ``recurrent_step_bf16_state`` is one decode step whose stored state is
 rounded to bfloat16 (``round_bf16``), pinned in
-``tests/test_oracle_bf16_state.py``.
+``tests/test_oracle_bf16_state.py``; ``decode_prologue`` and
+``recurrent_step_conv`` add the conv update and gates in front of a decode
+step, pinned in ``tests/test_oracle_prologue.py``.
 """
 from __future__ import annotations
 
@@ -138,6 +140,62 @@ def recurrent_step_bf16_state(q, k, v, g, beta, state_in, scale: float, eps: flo
     out, sout = recurrent(q, k, v, g, beta, _f64(state_in), cu, scale, eps=eps, nthreads=nthreads,
                           want_state=True, lib=lib, l2norm=l2norm)
     return out, round_bf16(sout)
+
+
+def decode_prologue(mixed_qkv, conv_state, conv_w, conv_b, a, b, A_log, dt_bias, Nqk: int,
+                    Nv: int, D: int = 128, activation_bf16: bool = True):
+    """The steps in front of a decode step (blog post, sections 3 and 4), in fp64.
+
+    Causal depthwise conv update (section 3, the decode branch): the cached
+    window of each channel gains the new value and drops its oldest one; the
+    channel's output is the cross-correlation of the new window with that
+    channel's kernel plus its bias, through SiLU (x / (1 + e^-x)), cast to the
+    activation dtype (bf16 when ``activation_bf16``, via ``round_bf16``).  The
+    output splits into q | k | v (Nqk*D, Nqk*D and Nv*D channels).  The gates
+    (section 4): beta = sigmoid(b), g = -exp(A_log) * softplus(a + dt_bias).
+
+    Shapes: mixed_qkv [N, C]; conv_state [N, C, K]; conv_w [C, K]; conv_b [C]
+    or None; a, b [N, Nv]; A_log, dt_bias [Nv].  Returns
+    (q [N, Nqk, D], k [N, Nqk, D], v [N, Nv, D], g [N, Nv], beta [N, Nv],
+    new conv_state [N, C, K]).
+    """
+    x = _f64(mixed_qkv)
+    cs = _f64(conv_state)
+    w = _f64(conv_w)
+    N, C = x.shape
+    if C != (2 * Nqk + Nv) * D or cs.shape[:2] != (N, C) or w.shape != (C, cs.shape[2]):
+        raise ValueError("shape mismatch")
+    new_state = np.concatenate([cs[:, :, 1:], x[:, :, None]], axis=2)
+    y = np.sum(new_state * w[None, :, :], axis=2)
+    if conv_b is not None:
+        y = y + _f64(conv_b)[None, :]
+    y = y / (1.0 + np.exp(-y))
+    if activation_bf16:
+        y = round_bf16(y)
+    q = y[:, :Nqk * D].reshape(N, Nqk, D)
+    k = y[:, Nqk * D:2 * Nqk * D].reshape(N, Nqk, D)
+    v = y[:, 2 * Nqk * D:].reshape(N, Nv, D)
+    z = _f64(a) + _f64(dt_bias)[None, :]
+    softplus = np.maximum(z, 0.0) + np.log1p(np.exp(-np.abs(z)))
+    g = -np.exp(_f64(A_log))[None, :] * softplus
+    beta = 1.0 / (1.0 + np.exp(-_f64(b)))
+    return q, k, v, g, beta, new_state
+
+
+def recurrent_step_conv(mixed_qkv, conv_state, conv_w, conv_b, a, b, A_log, dt_bias, state_in,
+                        Nqk: int, Nv: int, scale: float, activation_bf16: bool = True,
+                        l2norm: bool = True, nthreads: int = 0):
+    """``decode_prologue`` followed by one decode step of the rule.
+
+    Returns (out [N, Nv, D], state_out [N, Nv, D, D], new conv_state).
+    """
+    D = np.asarray(state_in).shape[-1]
+    q, k, v, g, beta, cs = decode_prologue(mixed_qkv, conv_state, conv_w, conv_b, a, b, A_log,
+                                           dt_bias, Nqk, Nv, D, activation_bf16=activation_bf16)
+    N = q.shape[0]
+    out, sout = recurrent(q, k, v, g, beta, state_in, np.arange(N + 1, dtype=np.int32), scale,
+                          nthreads=nthreads, l2norm=l2norm)
+    return out, sout, cs
 
 
 def rel_l2(x, ref) -> float:
