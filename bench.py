@@ -17,8 +17,9 @@ kernel trace reports), from which the decode step's GB/s and the rooflines
 are computed.  ``ms_per_step`` is the host wall clock of a whole step.  After
 the timed steps the decode step is also measured with its state stored in
 bf16 (``gdr_recurrent_step_bf16_state``, half the state bytes), reported as
-``decode_bf16_state``, and ``gdr_recurrent_multi`` on 256 sequences x 4 tokens
-as ``multi_token``; neither is part of the step.  One JSON line is printed.
+``decode_bf16_state``, ``gdr_recurrent_multi`` on 256 sequences x 4 tokens
+as ``multi_token``, and the decode step with its conv update and gates fused
+in front as ``decode_conv``; none of them is part of the step.  One JSON line is printed.
 """
 from __future__ import annotations
 
@@ -70,6 +71,16 @@ def alg_bytes_multi(N, tokens, Nqk, Nv, es=2):
     state = N * Nv * D * D * 4 * 2
     per_tok = (2 * Nqk * D + Nv * D + Nv * D) * es + Nv * 4 * 2
     return state + N * tokens * per_tok
+
+
+def alg_bytes_decode_conv(N, Nqk, Nv, K=4, es=2):
+    """The decode step's bytes with q, k, v replaced by the token's projected
+    channels, plus each channel's conv window read and written and the conv
+    kernels (read once); a, b per (sequence, head); A_log, dt_bias per head."""
+    C = (2 * Nqk + Nv) * D
+    state = N * Nv * D * D * 4 * 2
+    return (state + N * C * es + 2 * N * C * K * es + C * K * es + N * Nv * D * es
+            + N * Nv * 4 * 2 + Nv * 4 * 2)
 
 
 def measured_traffic(kernel: str):
@@ -247,6 +258,32 @@ def main() -> int:
     multi_bytes = alg_bytes_multi(mt.N, MULTI_TOKENS, mt.Nqk, mt.Nv)
     multi_gbps = multi_bytes / multi_s / 1e9
 
+    # ---- decode with the conv update and gates fused in front
+    # (gdr_recurrent_step_conv): the decode heads, 256 sequences, bf16
+    # activations, fp32 states in place; measured after the timed steps
+    from gated_deltanet_chunked_amd.inputs import prologue_inputs
+    pi = prologue_inputs(dec.N, dec.Nqk, dec.Nv, seed=4)
+    cv = {k_: torch.from_numpy(getattr(pi, k_)).to(dev, torch.bfloat16)
+          for k_ in ("mixed_qkv", "conv_state", "conv_w")}
+    cf = {k_: torch.from_numpy(getattr(pi, k_)).to(dev) for k_ in ("a", "b", "A_log", "dt_bias",
+                                                                   "state_in")}
+    cs_a, cs_b = cv["conv_state"], torch.empty_like(cv["conv_state"])
+    for _ in range(args.warmup):
+        gdr.recurrent_step_conv(cv["mixed_qkv"], cs_a, cv["conv_w"], None, cf["a"], cf["b"],
+                                cf["A_log"], cf["dt_bias"], cf["state_in"], conv_state_out=cs_b,
+                                out=dout, scale=scale)
+        cs_a, cs_b = cs_b, cs_a
+    ctim = []
+    for _ in range(args.steps):
+        gdr.recurrent_step_conv(cv["mixed_qkv"], cs_a, cv["conv_w"], None, cf["a"], cf["b"],
+                                cf["A_log"], cf["dt_bias"], cf["state_in"], conv_state_out=cs_b,
+                                out=dout, scale=scale, timings=ctim)
+        cs_a, cs_b = cs_b, cs_a
+    torch.cuda.synchronize()
+    conv_s = float(np.mean([ms for _, ms in ctim])) * 1e-3
+    conv_bytes = alg_bytes_decode_conv(dec.N, dec.Nqk, dec.Nv)
+    conv_gbps = conv_bytes / conv_s / 1e9
+
     res = {
         "metric": "chunk GDR fwd tokens/s + % MFMA peak; decode-step GB/s (% HBM peak)",
         "value": round(tok_s, 1),
@@ -287,6 +324,11 @@ def main() -> int:
                         "gpu_ms": round(multi_s * 1e3, 4), "gbps": round(multi_gbps, 1),
                         "frac_hbm_peak": round(multi_gbps / HBM_PEAK_GBPS, 4),
                         "tokens_per_s": round(mt.T / multi_s, 1), "alg_bytes": multi_bytes},
+        "decode_conv": {"workload": f"{dec.N} sequences x 1 token, Nqk={dec.Nqk} Nv={dec.Nv} bf16, "
+                                    "conv update (kernel 4) and gates fused in front, fp32 states",
+                        "gpu_ms": round(conv_s * 1e3, 4), "gbps": round(conv_gbps, 1),
+                        "frac_hbm_peak": round(conv_gbps / HBM_PEAK_GBPS, 4),
+                        "tokens_per_s": round(dec.N / conv_s, 1), "alg_bytes": conv_bytes},
         "roofline": roof,
     }
 

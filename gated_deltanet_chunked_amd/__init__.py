@@ -71,6 +71,10 @@ def load(path: str = LIB_PATH):
                                         ctypes.c_int, f32, u32, vp, vp, vp,
                                         ctypes.POINTER(ctypes.c_float)]
     lib.gdr_recurrent_multi.restype = ctypes.c_int
+    lib.gdr_recurrent_step_conv.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp,
+                                            i32, i32, i32, i32, ctypes.c_int, f32, u32, vp, vp,
+                                            ctypes.POINTER(ctypes.c_float)]
+    lib.gdr_recurrent_step_conv.restype = ctypes.c_int
     lib.gdr_status_string.argtypes = [ctypes.c_int]
     lib.gdr_status_string.restype = ctypes.c_char_p
     lib.gdr_version.argtypes = []
@@ -225,6 +229,64 @@ def recurrent_multi(q, k, v, g, beta, cu_seqlens, state_in=None, *, scale: Optio
     if timings is not None:
         timings.append(("multi", float(ms.value)))
     return out, state_out
+
+
+def recurrent_step_conv(mixed_qkv, conv_state_in, conv_weight, conv_bias, a, b, A_log, dt_bias,
+                        state_in, *, conv_state_out=None, state_out=None, out=None,
+                        scale: Optional[float] = None, l2norm: bool = True,
+                        timings: Optional[list] = None):
+    """One decode step with the conv update and gates fused in front
+    (``gdr_recurrent_step_conv``).
+
+    mixed_qkv [N, C] (q | k | v channels, C = (2 Nqk + Nv) 128) in the
+    activation dtype; conv_state_in [N, C, 4] and conv_weight [C, 4] in the same
+    dtype; conv_bias [C] or None; a, b [N, Nv] f32; A_log, dt_bias [Nv] f32;
+    state_in [N, Nv, 128, 128] f32.  ``state_out`` defaults to ``state_in`` (in
+    place); ``conv_state_out`` is a new tensor unless given (never the input).
+    Returns (out [N, Nv, 128], conv_state_out).  With a list as ``timings`` the
+    call waits for the kernel and appends ("decode_conv", ms).
+    """
+    import torch
+    lib = load()
+    N, C = mixed_qkv.shape
+    Nv = a.shape[1]
+    Nqk = (C // D - Nv) // 2
+    K = conv_state_in.shape[2]
+    dev = mixed_qkv.device
+    dt = mixed_qkv.dtype
+    code = _dtype_code(mixed_qkv)
+    if (2 * Nqk + Nv) * D != C:
+        raise ValueError(f"mixed_qkv has {C} channels, not (2 Nqk + Nv) * {D}")
+    _check(conv_state_in, "conv_state_in", (N, C, K), dt, dev)
+    _check(conv_weight, "conv_weight", (C, K), dt, dev)
+    _check(conv_bias, "conv_bias", (C,), dt, dev)
+    _check(a, "a", (N, Nv), torch.float32, dev)
+    _check(b, "b", (N, Nv), torch.float32, dev)
+    _check(A_log, "A_log", (Nv,), torch.float32, dev)
+    _check(dt_bias, "dt_bias", (Nv,), torch.float32, dev)
+    _check(state_in, "state_in", (N, Nv, D, D), torch.float32, dev)
+    if state_out is None:
+        state_out = state_in
+    _check(state_out, "state_out", (N, Nv, D, D), torch.float32, dev)
+    if conv_state_out is None:
+        conv_state_out = torch.empty_like(conv_state_in)
+    _check(conv_state_out, "conv_state_out", (N, C, K), dt, dev)
+    if out is None:
+        out = torch.empty((N, Nv, D), dtype=dt, device=dev)
+    _check(out, "out", (N, Nv, D), dt, dev)
+    if scale is None:
+        scale = D ** -0.5
+    ms = ctypes.c_float(0.0)
+    st = lib.gdr_recurrent_step_conv(
+        _ptr(mixed_qkv), _ptr(conv_state_in), _ptr(conv_state_out), _ptr(conv_weight),
+        _ptr(conv_bias), K, _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias), _ptr(state_in),
+        _ptr(state_out), N, Nqk, Nv, D, code, float(scale), GDR_FLAG_QK_L2NORM if l2norm else 0,
+        _ptr(out), _stream(), ctypes.byref(ms) if timings is not None else None)
+    if st != 0:
+        raise GdrError(st, "gdr_recurrent_step_conv")
+    if timings is not None:
+        timings.append(("decode_conv", float(ms.value)))
+    return out, conv_state_out
 
 
 def recurrent_step(q, k, v, g, beta, state_in, *, state_out=None, out=None,

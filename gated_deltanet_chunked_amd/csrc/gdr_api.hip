@@ -260,6 +260,48 @@ extern "C" gdr_status gdr_recurrent_multi(const void* q, const void* k, const vo
   return GDR_OK;
 }
 
+extern "C" gdr_status gdr_recurrent_step_conv(
+    const void* mixed_qkv, const void* conv_state_in, void* conv_state_out,
+    const void* conv_weight, const void* conv_bias, int32_t conv_k, const float* a,
+    const float* b, const float* A_log, const float* dt_bias, const float* state_in,
+    float* state_out, int32_t N, int32_t Nqk, int32_t Nv, int32_t D, gdr_dtype dtype, float scale,
+    uint32_t flags, void* out, void* stream, float* kernel_ms) {
+  ConvStepArgs c{mixed_qkv, conv_state_in, conv_state_out, conv_weight, conv_bias, conv_k, a, b,
+                 A_log, dt_bias, state_in, state_out, N, Nqk, Nv, D, dtype, scale, flags, out};
+  const gdr_status s = validate_conv_step(c);
+  if (s != GDR_OK) return s;
+  if (kernel_ms) *kernel_ms = 0.0f;
+  if (N == 0) return GDR_OK;
+  EventPairs pairs;
+  LaunchEvents ev{};
+  if (kernel_ms) {
+    if (!pairs.create(1)) return GDR_ERR_HIP;
+    ev = LaunchEvents{pairs.ev[0], pairs.ev[1]};
+  }
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const int norm = (flags & GDR_FLAG_QK_L2NORM) ? 1 : 0;
+  if (dtype == GDR_BF16)
+    launch_decode_conv<__bf16>(static_cast<const __bf16*>(mixed_qkv),
+                               static_cast<const __bf16*>(conv_state_in),
+                               static_cast<__bf16*>(conv_state_out),
+                               static_cast<const __bf16*>(conv_weight),
+                               static_cast<const __bf16*>(conv_bias), a, b, A_log, dt_bias,
+                               state_in, state_out, N, Nqk, Nv, scale, norm,
+                               static_cast<__bf16*>(out), st, ev);
+  else
+    launch_decode_conv<float>(static_cast<const float*>(mixed_qkv),
+                              static_cast<const float*>(conv_state_in),
+                              static_cast<float*>(conv_state_out),
+                              static_cast<const float*>(conv_weight),
+                              static_cast<const float*>(conv_bias), a, b, A_log, dt_bias, state_in,
+                              state_out, N, Nqk, Nv, scale, norm, static_cast<float*>(out), st, ev);
+  if (hipGetLastError() != hipSuccess) return GDR_ERR_HIP;
+  if (kernel_ms && (hipEventSynchronize(pairs.ev[1]) != hipSuccess ||
+                    hipEventElapsedTime(kernel_ms, pairs.ev[0], pairs.ev[1]) != hipSuccess))
+    return GDR_ERR_HIP;
+  return GDR_OK;
+}
+
 extern "C" const char* gdr_status_string(gdr_status s) {
   switch (s) {
     case GDR_OK: return "ok";

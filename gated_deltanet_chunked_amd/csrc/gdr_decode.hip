@@ -43,6 +43,20 @@ __device__ __forceinline__ void load4<__bf16>(const __bf16* p, float* x) {
   for (int e = 0; e < 4; ++e) x[e] = (float)a[e];
 }
 
+// Four values stored as type T (8 or 16 bytes, one access).
+template <typename T>
+__device__ __forceinline__ void put4(T* p, float a, float b, float c, float d);
+template <>
+__device__ __forceinline__ void put4<float>(float* p, float a, float b, float c, float d) {
+  *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
+}
+template <>
+__device__ __forceinline__ void put4<__bf16>(__bf16* p, float a, float b, float c, float d) {
+  typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+  const bf16x4 y = {(__bf16)a, (__bf16)b, (__bf16)c, (__bf16)d};
+  *reinterpret_cast<bf16x4*>(p) = y;
+}
+
 // The 8 values of a row of q, k (D entries, type T) at the columns lane cg
 // holds for state storage ST.
 template <typename T, typename ST>
@@ -262,6 +276,153 @@ template void launch_multi<__bf16>(const __bf16*, const __bf16*, const __bf16*, 
                                    const float*, const float*, const int32_t*, int32_t, int32_t,
                                    float*, int32_t, int32_t, float, int, __bf16*, hipStream_t,
                                    LaunchEvents);
+
+// ---- decode step with its prologue (blog post sections 3 and 4) fused in
+// front: the token's projected q|k|v passes through the causal depthwise conv
+// update (each channel's window of 4 cached values gains the new value and
+// drops its oldest; output = SiLU(kernel . window + bias), cast to the
+// activation dtype T), and the gates are formed from a and b:
+//   beta = sigmoid(b),  g = -exp(A_log) softplus(a + dt_bias).
+template <typename T>
+struct ConvArgs {
+  const T* x;          // [N, C] projected q|k|v of the token, C = (2 Nqk + Nv) 128
+  const T* cs_in;      // [N, C, 4] cached windows, oldest first
+  T* cs_out;           // [N, C, 4] updated windows; never overlaps cs_in
+  const T* w;          // [C, 4] kernels (cross-correlation order)
+  const T* bias;       // [C] or nullptr
+  const float* a;      // [N, Nv]
+  const float* b;      // [N, Nv]
+  const float* A_log;  // [Nv]
+  const float* dt_bias;   // [Nv]
+  int32_t C;
+};
+
+// The loads of one channel's conv inputs, kept raw so that issuing them does
+// not wait for them: the window, the kernel, the new value and the bias.
+template <typename T>
+struct ConvLoad {
+  typedef __attribute__((ext_vector_type(4))) T vec4;
+  vec4 win, w;
+  T x, bias;
+  __device__ __forceinline__ void issue(const ConvArgs<T>& p, int n, int c) {
+    const size_t wi = ((size_t)n * p.C + c) * 4;
+    win = *reinterpret_cast<const vec4*>(p.cs_in + wi);
+    w = *reinterpret_cast<const vec4*>(p.w + (size_t)c * 4);
+    x = p.x[(size_t)n * p.C + c];
+    bias = p.bias ? p.bias[c] : from_f32<T>(0.0f);
+  }
+  // Channel c after the conv update, as the activation dtype holds it;
+  // `write` also stores the channel's new window.
+  __device__ __forceinline__ float finish(const ConvArgs<T>& p, int n, int c, bool write) const {
+    const float s1 = to_f32(win[1]), s2 = to_f32(win[2]), s3 = to_f32(win[3]), xf = to_f32(x);
+    float y = to_f32(w[0]) * s1 + to_f32(w[1]) * s2 + to_f32(w[2]) * s3 + to_f32(w[3]) * xf;
+    y += to_f32(bias);
+    y = y / (1.0f + expf(-y));
+    if (write) put4<T>(p.cs_out + ((size_t)n * p.C + c) * 4, s1, s2, s3, xf);   // exact
+    return to_f32(from_f32<T>(y));
+  }
+};
+
+// One workgroup per (sequence, value head), the decode kernel's layout.  The
+// conv outputs are computed once per workgroup into LDS: thread t takes q/k
+// channel t of the group's q/k head (q for t < 128, k after) and, for t < 128,
+// v channel t of its value head.  Their loads are issued before the state's,
+// so the conv work overlaps the state's arrival.  The first value head of each
+// group writes the q/k windows; every head writes its v windows.
+template <typename T>
+__global__ __launch_bounds__(256) void decode_conv_kernel(ConvArgs<T> p, const float* state_in,
+                                                          float* state_out, int32_t Nqk, int32_t Nv,
+                                                          float scale, int norm,
+                                                          T* __restrict__ out) {
+  __shared__ float qk_act[2 * kD], v_act[kD];
+  const int bh = blockIdx.x;
+  const int n = bh / Nv, h = bh % Nv;
+  const int G = Nv / Nqk, j = h / G;
+  const int tid = threadIdx.x;
+  const int cg = tid & 15, rg = tid >> 4;
+  const size_t sb = (size_t)bh * kD * kD;
+
+  const int c_qk = (tid < kD ? j : Nqk + j - 1) * kD + tid;        // q: j*128 + t; k: (Nqk+j)*128 + t-128
+  const int c_v = (2 * Nqk + h) * kD + (tid & (kD - 1));            // lanes >= 128 repeat a channel
+  ConvLoad<T> lqk, lv;
+  lqk.issue(p, n, c_qk);
+  lv.issue(p, n, c_v);
+
+  StatePiece<float> s[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s[i].load(state_in + sb + (size_t)(rg + 16 * i) * kD, cg);
+
+  qk_act[tid] = lqk.finish(p, n, c_qk, h % G == 0);
+  const float vt = lv.finish(p, n, c_v, tid < kD);
+  if (tid < kD) v_act[tid] = vt;
+  const size_t gi = (size_t)n * Nv + h;
+  const float z = p.a[gi] + p.dt_bias[h];
+  const float softplus = fmaxf(z, 0.0f) + log1pf(expf(-fabsf(z)));
+  const float alpha = expf(-expf(p.A_log[h]) * softplus);
+  const float bt = 1.0f / (1.0f + expf(-p.b[gi]));
+  __syncthreads();
+
+  float kh[8], qh[8], vv[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int col = piece_col<float>(cg, e >> 2) + (e & 3);
+    qh[e] = qk_act[col];
+    kh[e] = qk_act[kD + col];
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) vv[i] = v_act[rg + 16 * i];
+
+  float ssk = 0.f, ssq = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) { ssk += kh[e] * kh[e]; ssq += qh[e] * qh[e]; }
+  ssk = group16_sum(ssk);
+  ssq = group16_sum(ssq);
+  const float rk = norm ? 1.0f / sqrtf(ssk + 1e-6f) : 1.0f;
+  const float rq = (norm ? 1.0f / sqrtf(ssq + 1e-6f) : 1.0f) * scale;
+  float kq = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) { kh[e] *= rk; qh[e] *= rq; kq += kh[e] * qh[e]; }
+  kq = group16_sum(kq);
+  T* op = out + gi * kD;
+
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int row = rg + 16 * i;
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = s[i].get(e);
+    float a = 0.f, b = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) { a += x[e] * kh[e]; b += x[e] * qh[e]; }
+    a = group16_sum(a);
+    b = group16_sum(b);
+    const float delta = bt * (vv[i] - alpha * a);
+    if (cg == 0) op[row] = from_f32<T>(alpha * b + delta * kq);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = alpha * x[e] + delta * kh[e];
+    StatePiece<float>::store(state_out + sb + (size_t)row * kD, cg, x);
+  }
+}
+
+template <typename T>
+void launch_decode_conv(const T* x, const T* cs_in, T* cs_out, const T* w, const T* bias,
+                        const float* a, const float* b, const float* A_log, const float* dt_bias,
+                        const float* state_in, float* state_out, int32_t N, int32_t Nqk, int32_t Nv,
+                        float scale, int norm, T* out, hipStream_t stream, LaunchEvents ev) {
+  ConvArgs<T> p{x, cs_in, cs_out, w, bias, a, b, A_log, dt_bias, (2 * Nqk + Nv) * kD};
+  hipExtLaunchKernelGGL(decode_conv_kernel<T>, dim3((unsigned)N * (unsigned)Nv), dim3(256), 0,
+                        stream, ev.start, ev.stop, 0, p, state_in, state_out, Nqk, Nv, scale, norm,
+                        out);
+}
+
+#define GDR_CONV_INST(T)                                                                        \
+  template void launch_decode_conv<T>(const T*, const T*, T*, const T*, const T*, const float*, \
+                                      const float*, const float*, const float*, const float*,   \
+                                      float*, int32_t, int32_t, int32_t, float, int, T*,        \
+                                      hipStream_t, LaunchEvents);
+GDR_CONV_INST(float)
+GDR_CONV_INST(__bf16)
+#undef GDR_CONV_INST
 
 template <typename T, typename ST>
 void launch_decode(const T* q, const T* k, const T* v, const float* g, const float* beta,

@@ -84,7 +84,20 @@ struct StepArgs {
   bool state_bf16;
 };
 
+struct ConvStepArgs {
+  const void* x; const void* cs_in; void* cs_out; const void* w; const void* bias;
+  int32_t conv_k;
+  const float* a; const float* b; const float* A_log; const float* dt_bias;
+  const float* state_in; float* state_out;
+  int32_t N, Nqk, Nv, D;
+  gdr_dtype dtype;
+  float scale;
+  uint32_t flags;
+  void* out;
+};
+
 gdr_status validate_chunk(const ChunkArgs& a);
+gdr_status validate_conv_step(const ConvStepArgs& a);
 gdr_status validate_step(const StepArgs& a);
 
 inline size_t dtype_size(gdr_dtype d) { return d == GDR_BF16 ? 2 : 4; }

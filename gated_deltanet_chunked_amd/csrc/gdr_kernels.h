@@ -90,4 +90,13 @@ void launch_multi(const Tin* q, const Tin* k, const Tin* v, const float* g, cons
                   float* state_out, int32_t Nqk, int32_t Nv, float scale, int norm, Tin* out,
                   hipStream_t stream, LaunchEvents ev = {});
 
+// One decode step with the conv update and gate functions fused in front
+// (conv kernel size 4).
+template <typename Tin>
+void launch_decode_conv(const Tin* x, const Tin* cs_in, Tin* cs_out, const Tin* w,
+                        const Tin* bias, const float* a, const float* b, const float* A_log,
+                        const float* dt_bias, const float* state_in, float* state_out, int32_t N,
+                        int32_t Nqk, int32_t Nv, float scale, int norm, Tin* out,
+                        hipStream_t stream, LaunchEvents ev = {});
+
 }  // namespace gdr

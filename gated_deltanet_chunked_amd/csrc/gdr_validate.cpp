@@ -122,4 +122,45 @@ gdr_status validate_step(const StepArgs& a) {
   return GDR_OK;
 }
 
+gdr_status validate_conv_step(const ConvStepArgs& a) {
+  gdr_status s = common_sizes(a.Nqk, a.Nv, a.D, a.dtype, a.flags);
+  if (s != GDR_OK) return s;
+  if (a.conv_k != 4) return GDR_ERR_UNSUPPORTED;
+  if (a.N < 0) return GDR_ERR_INVALID_ARGUMENT;
+  if (static_cast<int64_t>(a.N) * a.Nv > (int64_t(1) << 31) / 4) return GDR_ERR_INVALID_ARGUMENT;
+  if (a.N == 0) return GDR_OK;
+  const void* req[] = {a.x, a.cs_in, a.cs_out, a.w, a.a, a.b, a.A_log, a.dt_bias, a.state_in,
+                       a.state_out, a.out};
+  for (const void* p : req)
+    if (!p || !aligned16(p)) return GDR_ERR_INVALID_ARGUMENT;
+  if (a.bias && !aligned16(a.bias)) return GDR_ERR_INVALID_ARGUMENT;
+  const int64_t es = static_cast<int64_t>(dtype_size(a.dtype));
+  const int64_t C = (2 * static_cast<int64_t>(a.Nqk) + a.Nv) * 128;
+  const int64_t x_bytes = a.N * C * es, cs_bytes = a.N * C * 4 * es, w_bytes = C * 4 * es;
+  const int64_t b_bytes = C * es, nv_bytes = static_cast<int64_t>(a.N) * a.Nv * 4;
+  const int64_t h_bytes = static_cast<int64_t>(a.Nv) * 4;
+  const int64_t st_bytes = static_cast<int64_t>(a.N) * a.Nv * 128 * 128 * 4;
+  const int64_t o_bytes = static_cast<int64_t>(a.N) * a.Nv * 128 * es;
+  struct R { const void* p; int64_t n; };
+  const R in[] = {{a.x, x_bytes}, {a.cs_in, cs_bytes}, {a.w, w_bytes}, {a.bias, b_bytes},
+                  {a.a, nv_bytes}, {a.b, nv_bytes}, {a.A_log, h_bytes}, {a.dt_bias, h_bytes},
+                  {a.state_in, st_bytes}};
+  // each output overlaps no input and no other output; state_out may equal
+  // state_in exactly (in-place update of the recurrent state)
+  const R outs[] = {{a.cs_out, cs_bytes}, {a.state_out, st_bytes}, {a.out, o_bytes}};
+  constexpr int kOuts = 3, kStateOut = 1, kIns = 9, kStateIn = 8;
+  static_assert(sizeof(in) / sizeof(in[0]) == kIns && sizeof(outs) / sizeof(outs[0]) == kOuts,
+                "index constants out of date");
+  for (int i = 0; i < kOuts; ++i) {
+    for (int r = 0; r < kIns; ++r) {
+      if (i == kStateOut && r == kStateIn && a.state_out == a.state_in) continue;
+      if (overlap(outs[i].p, outs[i].n, in[r].p, in[r].n)) return GDR_ERR_INVALID_ARGUMENT;
+    }
+    for (int r = 0; r < kOuts; ++r)   // distinct outputs, even at the same address
+      if (r != i && overlap(outs[i].p, outs[i].n, outs[r].p, outs[r].n))
+        return GDR_ERR_INVALID_ARGUMENT;
+  }
+  return GDR_OK;
+}
+
 }  // namespace gdr

@@ -158,3 +158,47 @@ def orthonormal_keys(n: int, dk: int, seed: int) -> np.ndarray:
     qm, r = np.linalg.qr(m)
     qm = qm * np.sign(np.diag(r))[None, :]
     return np.ascontiguousarray(qm.T[:n])
+
+
+@dataclasses.dataclass
+class PrologueInputs:
+    """Raw inputs of a decode step with its conv/gate prologue (no arithmetic
+    of the prologue or the rule is done here)."""
+
+    mixed_qkv: np.ndarray     # [N, C] float32 (bf16-representable for "bf16"), C = (2 Nqk + Nv) D
+    conv_state: np.ndarray    # [N, C, K] same
+    conv_w: np.ndarray        # [C, K] same
+    conv_b: Optional[np.ndarray]   # [C] same, or None
+    a: np.ndarray             # [N, Nv] float32
+    b: np.ndarray             # [N, Nv] float32
+    A_log: np.ndarray         # [Nv] float32
+    dt_bias: np.ndarray       # [Nv] float32
+    state_in: np.ndarray      # [N, Nv, D, D] float32
+    Nqk: int
+    Nv: int
+    dtype: str
+
+
+def prologue_inputs(N: int, Nqk: int, Nv: int, *, dtype: str = "bf16", seed: int = 0,
+                    K: int = 4, bias: bool = False, state_std: float = 0.01) -> PrologueInputs:
+    """Seeded draw: activations and cached windows N(0, 1); conv kernels
+    U(-1/sqrt(K), 1/sqrt(K)) (PyTorch's default conv init; Qwen3-Next's conv
+    has no bias, so none unless asked); a, b N(0, 1); A ~ U(0, 16) per value
+    head stored as A_log = log(A); dt_bias = 1; states state_std * N(0, 1)."""
+    rng = np.random.default_rng(seed)
+    C = (2 * Nqk + Nv) * D
+    x = rng.standard_normal((N, C)).astype(np.float32)
+    cs = rng.standard_normal((N, C, K)).astype(np.float32)
+    lim = 1.0 / np.sqrt(K)
+    w = rng.uniform(-lim, lim, (C, K)).astype(np.float32)
+    cb = rng.uniform(-lim, lim, C).astype(np.float32) if bias else None
+    a = rng.standard_normal((N, Nv)).astype(np.float32)
+    b = rng.standard_normal((N, Nv)).astype(np.float32)
+    A_log = np.log(rng.uniform(0.0, 16.0, Nv)).astype(np.float32)
+    dt_bias = np.ones(Nv, dtype=np.float32)
+    state = (state_std * rng.standard_normal((N, Nv, D, D))).astype(np.float32)
+    if dtype == "bf16":
+        x, cs, w = round_to_bf16(x), round_to_bf16(cs), round_to_bf16(w)
+        cb = None if cb is None else round_to_bf16(cb)
+    return PrologueInputs(mixed_qkv=x, conv_state=cs, conv_w=w, conv_b=cb, a=a, b=b, A_log=A_log,
+                          dt_bias=dt_bias, state_in=state, Nqk=Nqk, Nv=Nv, dtype=dtype)

@@ -18,7 +18,9 @@
  *   gdr_recurrent_step -- decode: one token per sequence (blog post 5(2)).
  * and two variants of the token loop:
  *   gdr_recurrent_step_bf16_state -- decode with the state stored in bf16;
- *   gdr_recurrent_multi           -- a few tokens per sequence, token by token.
+ *   gdr_recurrent_multi           -- a few tokens per sequence, token by token;
+ *   gdr_recurrent_step_conv       -- decode with the conv update and gates fused
+ *                                    in front.
  *
  * Conventions shared by all calls:
  *   - All tensor pointers are DEVICE pointers, caller-owned, contiguous,
@@ -216,6 +218,40 @@ gdr_status gdr_recurrent_multi(const void* q, const void* k, const void* v,
                                int32_t N, int32_t T, int32_t Nqk, int32_t Nv, int32_t D,
                                gdr_dtype dtype, float scale, uint32_t flags,
                                void* out, float* state_out, void* stream, float* kernel_ms);
+
+/*
+ * One decode step with the steps in front of it fused (Qwen3-Next blog post,
+ * sections 3 and 4): the token's projected q|k|v goes through the causal
+ * depthwise conv update with SiLU, the gates come from a and b, then the rule
+ * runs as in gdr_recurrent_step.  Per channel c (C = (2 Nqk + Nv) D channels,
+ * q then k then v, each head's D consecutive):
+ *   window  = conv_state_in[n][c][1..K-1], then mixed_qkv[n][c]   (oldest first)
+ *   y       = SiLU(sum_i conv_weight[c][i] window[i] + conv_bias[c]), cast to dtype
+ *   conv_state_out[n][c] = window
+ * and per (sequence, value head):
+ *   beta = sigmoid(b),  g = -exp(A_log[h]) softplus(a + dt_bias[h]).
+ *
+ * mixed_qkv      [N, C]     dtype
+ * conv_state_in  [N, C, K]  dtype
+ * conv_state_out [N, C, K]  dtype; must not overlap conv_state_in or any
+ *                other buffer: the value heads of a group read the same q/k
+ *                windows, so the update cannot be made in place
+ * conv_weight    [C, K]     dtype;  conv_bias [C] dtype, or NULL for none
+ * conv_k         K; must be 4 (Qwen3-Next's kernel size; GDR_ERR_UNSUPPORTED)
+ * a, b           [N, Nv]    float32;  A_log, dt_bias [Nv] float32
+ * state_in, state_out, out, scale, flags: as for gdr_recurrent_step
+ *                (states float32; state_out may equal state_in)
+ * kernel_ms      NULL, or where to write the kernel's GPU time (the call then
+ *                blocks until the kernel ends)
+ */
+gdr_status gdr_recurrent_step_conv(const void* mixed_qkv, const void* conv_state_in,
+                                   void* conv_state_out, const void* conv_weight,
+                                   const void* conv_bias, int32_t conv_k,
+                                   const float* a, const float* b, const float* A_log,
+                                   const float* dt_bias, const float* state_in, float* state_out,
+                                   int32_t N, int32_t Nqk, int32_t Nv, int32_t D,
+                                   gdr_dtype dtype, float scale, uint32_t flags, void* out,
+                                   void* stream, float* kernel_ms);
 
 /* A static, human-readable name for a status code. */
 const char* gdr_status_string(gdr_status s);

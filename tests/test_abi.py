@@ -250,3 +250,43 @@ def test_multi_token_validates_before_launching():
     assert call(N=1 << 20, Nqk=1, Nv=1024) == INVALID                # too many workgroups
     ms = ctypes.c_float(1.0)
     assert call(T=0, state_out=None, ms=ctypes.byref(ms)) == OK and ms.value == 0.0
+
+
+def test_conv_step_validates_before_launching():
+    """gdr_recurrent_step_conv: sizes, kernel size, pointers and overlaps."""
+    import ctypes
+    lib = gdr.load()
+    N, Nqk, Nv = 2, 2, 4
+    C = (2 * Nqk + Nv) * 128
+    sizes = dict(x=N * C * 2, cs_in=N * C * 8, cs_out=N * C * 8, w=C * 8, bias=C * 2, a=N * Nv * 4,
+                 b=N * Nv * 4, A_log=Nv * 4, dt_bias=Nv * 4, s_in=N * Nv * 65536,
+                 s_out=N * Nv * 65536, out=N * Nv * 256)
+    base, addr = 1 << 40, {}
+    for k_, n in sizes.items():
+        addr[k_] = base
+        base += (n + (1 << 20)) & ~255
+
+    def call(**over):
+        a = dict(addr, K=4, N=N, Nqk=Nqk, Nv=Nv, D=128, dtype=gdr.GDR_BF16,
+                 flags=gdr.GDR_FLAG_QK_L2NORM, ms=None)
+        a.update(over)
+        return lib.gdr_recurrent_step_conv(a["x"], a["cs_in"], a["cs_out"], a["w"], a["bias"],
+                                           a["K"], a["a"], a["b"], a["A_log"], a["dt_bias"],
+                                           a["s_in"], a["s_out"], a["N"], a["Nqk"], a["Nv"], a["D"],
+                                           a["dtype"], 0.1, a["flags"], a["out"], None, a["ms"])
+
+    assert call(K=3) == UNSUPPORTED
+    assert call(D=64) == UNSUPPORTED
+    assert call(flags=8) == UNSUPPORTED
+    assert call(Nqk=3) == INVALID
+    assert call(N=-1) == INVALID
+    for name in ("x", "cs_in", "cs_out", "w", "a", "b", "A_log", "dt_bias", "s_in", "s_out", "out"):
+        assert call(**{name: None}) == INVALID, name
+    assert call(bias=addr["bias"] + 2) == INVALID                        # misaligned bias
+    assert call(cs_out=addr["cs_in"]) == INVALID                         # conv update not in place
+    assert call(cs_out=addr["cs_in"] + sizes["cs_in"] - 256) == INVALID
+    assert call(out=addr["x"]) == INVALID
+    assert call(s_out=addr["cs_out"]) == INVALID                         # outputs overlap
+    assert call(s_out=addr["s_in"] + 4096) == INVALID                    # partial state overlap
+    ms = ctypes.c_float(1.0)
+    assert call(N=0, ms=ctypes.byref(ms)) == OK and ms.value == 0.0

@@ -411,3 +411,53 @@ def test_multi_token_matches_chunk_fwd():
     o_c, s_c = _chunk(inp)
     _assert_close("out", o_m, o_c, TOL["f32"])
     _assert_close("state", s_m, s_c, TOL["f32"])
+
+
+# -------------------------------------- decode with the conv/gate prologue
+
+
+def _conv_step(p, in_place=True):
+    import torch
+    dt = torch.bfloat16 if p.dtype == "bf16" else torch.float32
+    dv = lambda x, t=None: None if x is None else torch.from_numpy(x).to("cuda:0", t or torch.float32)
+    x, cs, w = dv(p.mixed_qkv, dt), dv(p.conv_state, dt), dv(p.conv_w, dt)
+    cb = dv(p.conv_b, dt)
+    s = dv(p.state_in)
+    s_out = s if in_place else torch.empty_like(s)
+    cs_keep = cs.clone()
+    out, cs_out = gdr.recurrent_step_conv(x, cs, w, cb, dv(p.a), dv(p.b), dv(p.A_log),
+                                          dv(p.dt_bias), s, state_out=s_out, scale=SCALE)
+    torch.cuda.synchronize()
+    assert torch.equal(cs, cs_keep), "conv_state_in modified"
+    return to_f64(out), to_f64(s_out), to_f64(cs_out)
+
+
+def _conv_oracle(p):
+    import oracle
+    return oracle.recurrent_step_conv(p.mixed_qkv, p.conv_state, p.conv_w, p.conv_b, p.a, p.b,
+                                      p.A_log, p.dt_bias, p.state_in, p.Nqk, p.Nv, SCALE,
+                                      activation_bf16=(p.dtype == "bf16"))
+
+
+@pytest.mark.parametrize("in_place", [True, False])
+def test_decode_conv_workload(in_place):
+    """The decode workload (256 sequences, Nqk=16, Nv=32, bf16) with the conv
+    update and gates fused in front; the new conv windows are bit-exact."""
+    from gated_deltanet_chunked_amd.inputs import prologue_inputs
+    p = prologue_inputs(256, 16, 32, seed=71)
+    out, st, cs = _conv_step(p, in_place)
+    ro, rs, rcs = _conv_oracle(p)
+    _assert_close("out", out, ro, TOL["bf16"])
+    _assert_close("state", st, rs, TOL["bf16"])
+    assert np.array_equal(cs, rcs), "conv windows differ"
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_conv_with_bias(dtype):
+    from gated_deltanet_chunked_amd.inputs import prologue_inputs
+    p = prologue_inputs(5, 2, 4, dtype=dtype, seed=72, bias=True, state_std=0.5)
+    out, st, cs = _conv_step(p)
+    ro, rs, rcs = _conv_oracle(p)
+    _assert_close("out", out, ro, TOL[dtype])
+    _assert_close("state", st, rs, TOL[dtype])
+    assert np.array_equal(cs, rcs), "conv windows differ"
