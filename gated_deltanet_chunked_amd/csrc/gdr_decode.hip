@@ -116,16 +116,33 @@ __global__ __launch_bounds__(256) void decode_kernel(const T* __restrict__ q, co
   const int cg = tid & 15, rg = tid >> 4;
   const size_t sb = (size_t)bh * kD * kD;
 
-  // issue the state loads first: all of a thread's pieces in flight at once
+  // the token's operands first (a few small loads, kept raw so that issuing
+  // them does not wait), then all of the thread's state pieces; the small
+  // loads then arrive while the state is still in flight
+  typedef __attribute__((ext_vector_type(4))) T vec4;
+  const T* kp = k + ((size_t)n * Nqk + j) * kD;
+  const T* qp = q + ((size_t)n * Nqk + j) * kD;
+  const vec4 k0 = *reinterpret_cast<const vec4*>(kp + piece_col<ST>(cg, 0));
+  const vec4 k1 = *reinterpret_cast<const vec4*>(kp + piece_col<ST>(cg, 1));
+  const vec4 q0 = *reinterpret_cast<const vec4*>(qp + piece_col<ST>(cg, 0));
+  const vec4 q1 = *reinterpret_cast<const vec4*>(qp + piece_col<ST>(cg, 1));
+  const T* vp = v + ((size_t)n * Nv + h) * kD;
+  T vr[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) vr[i] = vp[rg + 16 * i];
+  const float gv = g[(size_t)n * Nv + h];
+  const float bt = beta[(size_t)n * Nv + h];
+
   StatePiece<ST> s[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) s[i].load(state_in + sb + (size_t)(rg + 16 * i) * kD, cg);
 
-  const T* kp = k + ((size_t)n * Nqk + j) * kD;
-  const T* qp = q + ((size_t)n * Nqk + j) * kD;
   float kh[8], qh[8];
-  load_cols<T, ST>(kp, cg, kh);
-  load_cols<T, ST>(qp, cg, qh);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    kh[e] = to_f32(k0[e]); kh[e + 4] = to_f32(k1[e]);
+    qh[e] = to_f32(q0[e]); qh[e + 4] = to_f32(q1[e]);
+  }
   float ssk = 0.f, ssq = 0.f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) { ssk += kh[e] * kh[e]; ssq += qh[e] * qh[e]; }
@@ -137,9 +154,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const T* __restrict__ q, co
 #pragma unroll
   for (int e = 0; e < 8; ++e) { kh[e] *= rk; qh[e] *= rq; kq += kh[e] * qh[e]; }
   kq = group16_sum(kq);
-  const float alpha = expf(g[(size_t)n * Nv + h]);
-  const float bt = beta[(size_t)n * Nv + h];
-  const T* vp = v + ((size_t)n * Nv + h) * kD;
+  const float alpha = expf(gv);
   T* op = out + ((size_t)n * Nv + h) * kD;
 
 #pragma unroll
@@ -153,7 +168,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const T* __restrict__ q, co
     for (int e = 0; e < 8; ++e) { a += x[e] * kh[e]; b += x[e] * qh[e]; }
     a = group16_sum(a);
     b = group16_sum(b);
-    const float delta = bt * (to_f32(vp[row]) - alpha * a);
+    const float delta = bt * (to_f32(vr[i]) - alpha * a);
     if (cg == 0) op[row] = from_f32<T>(alpha * b + delta * kq);
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] = alpha * x[e] + delta * kh[e];
