@@ -201,6 +201,34 @@ __global__ __launch_bounds__(256) void multi_kernel(const T* __restrict__ q, con
   const int lo = min(max(cu[n], 0), T_total);
   const int hi = min(max(cu[n + 1], lo), T_total);
 
+  // operands of one token, kept raw until used: this lane's two k and q
+  // pieces, the value entries of its 8 rows, the gate and beta
+  typedef __attribute__((ext_vector_type(4))) T vec4;
+  struct Raw {
+    vec4 k0, k1, q0, q1;
+    T vr[8];
+    float gg, bb;
+  };
+  auto fetch = [&](int t, Raw& o) {
+    const T* kp = k + ((size_t)t * Nqk + j) * kD;
+    const T* qp = q + ((size_t)t * Nqk + j) * kD;
+    o.k0 = *reinterpret_cast<const vec4*>(kp + piece_col<float>(cg, 0));
+    o.k1 = *reinterpret_cast<const vec4*>(kp + piece_col<float>(cg, 1));
+    o.q0 = *reinterpret_cast<const vec4*>(qp + piece_col<float>(cg, 0));
+    o.q1 = *reinterpret_cast<const vec4*>(qp + piece_col<float>(cg, 1));
+    const T* vp = v + ((size_t)t * Nv + h) * kD;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o.vr[i] = vp[rg + 16 * i];
+    o.gg = g[(size_t)t * Nv + h];
+    o.bb = beta[(size_t)t * Nv + h];
+  };
+
+  // the first token's operands, then the state: the small loads arrive while
+  // the state is in flight
+  // (token lo when the sequence has tokens, else token 0, which exists when
+  // T > 0; with T = 0 the inputs may be NULL and nothing is fetched)
+  Raw cur;
+  if (T_total > 0) fetch(lo < hi ? lo : 0, cur);
   float x[8][8];
   if (state_in) {
     StatePiece<float> s[8];
@@ -217,37 +245,26 @@ __global__ __launch_bounds__(256) void multi_kernel(const T* __restrict__ q, con
       for (int e = 0; e < 8; ++e) x[i][e] = 0.f;
   }
 
-  // operands of one token: this lane's 8 columns of k and q, the value
-  // entries of its 8 rows, the gate and beta
-  struct Tok {
-    float kk[8], qq[8], vv[8], gg, bb;
-  };
-  auto fetch = [&](int t, Tok& o) {
-    load_cols<T, float>(k + ((size_t)t * Nqk + j) * kD, cg, o.kk);
-    load_cols<T, float>(q + ((size_t)t * Nqk + j) * kD, cg, o.qq);
-    const T* vp = v + ((size_t)t * Nv + h) * kD;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) o.vv[i] = to_f32(vp[rg + 16 * i]);
-    o.gg = g[(size_t)t * Nv + h];
-    o.bb = beta[(size_t)t * Nv + h];
-  };
-
-  Tok cur;
-  if (lo < hi) fetch(lo, cur);
 #pragma unroll 1
   for (int t = lo; t < hi; ++t) {
-    Tok nxt;
+    Raw nxt;
     fetch(min(t + 1, hi - 1), nxt);   // the last token fetches itself again: in bounds
+    float kk[8], qq[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      kk[e] = to_f32(cur.k0[e]); kk[e + 4] = to_f32(cur.k1[e]);
+      qq[e] = to_f32(cur.q0[e]); qq[e + 4] = to_f32(cur.q1[e]);
+    }
     float ssk = 0.f, ssq = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) { ssk += cur.kk[e] * cur.kk[e]; ssq += cur.qq[e] * cur.qq[e]; }
+    for (int e = 0; e < 8; ++e) { ssk += kk[e] * kk[e]; ssq += qq[e] * qq[e]; }
     ssk = group16_sum(ssk);
     ssq = group16_sum(ssq);
     const float rk = norm ? 1.0f / sqrtf(ssk + 1e-6f) : 1.0f;
     const float rq = (norm ? 1.0f / sqrtf(ssq + 1e-6f) : 1.0f) * scale;
     float kh[8], qh[8], kq = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) { kh[e] = cur.kk[e] * rk; qh[e] = cur.qq[e] * rq; kq += kh[e] * qh[e]; }
+    for (int e = 0; e < 8; ++e) { kh[e] = kk[e] * rk; qh[e] = qq[e] * rq; kq += kh[e] * qh[e]; }
     kq = group16_sum(kq);
     const float alpha = expf(cur.gg);
     T* op = out + ((size_t)t * Nv + h) * kD;
@@ -258,7 +275,7 @@ __global__ __launch_bounds__(256) void multi_kernel(const T* __restrict__ q, con
       for (int e = 0; e < 8; ++e) { a += x[i][e] * kh[e]; b += x[i][e] * qh[e]; }
       a = group16_sum(a);
       b = group16_sum(b);
-      const float delta = cur.bb * (cur.vv[i] - alpha * a);
+      const float delta = cur.bb * (to_f32(cur.vr[i]) - alpha * a);
       if (cg == 0) op[rg + 16 * i] = from_f32<T>(alpha * b + delta * kq);
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[i][e] = alpha * x[i][e] + delta * kh[e];

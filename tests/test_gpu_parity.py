@@ -461,3 +461,19 @@ def test_decode_conv_with_bias(dtype):
     _assert_close("out", out, ro, TOL[dtype])
     _assert_close("state", st, rs, TOL[dtype])
     assert np.array_equal(cs, rcs), "conv windows differ"
+
+
+def test_multi_token_empty_input():
+    """T = 0 (the token buffers may be empty): every state passes through."""
+    import torch
+    dev = "cuda:0"
+    N, Nqk, Nv = 3, 2, 4
+    q = torch.empty((0, Nqk, 128), dtype=torch.bfloat16, device=dev)
+    v = torch.empty((0, Nv, 128), dtype=torch.bfloat16, device=dev)
+    g = torch.empty((0, Nv), dtype=torch.float32, device=dev)
+    cu = torch.zeros(N + 1, dtype=torch.int32, device=dev)
+    s0 = torch.randn((N, Nv, 128, 128), dtype=torch.float32, device=dev)
+    out, st = gdr.recurrent_multi(q, q, v, g, g, cu, s0, scale=SCALE)
+    torch.cuda.synchronize()
+    assert out.shape == (0, Nv, 128)
+    assert torch.equal(st, s0)
