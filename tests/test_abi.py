@@ -27,7 +27,9 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("gdr_chunk_fwd", "gdr_recurrent_step", "gdr_chunk_fwd_workspace_size",
-              "gdr_status_string", "gdr_version"):
+              "gdr_status_string", "gdr_version", "gdr_chunk_fwd_timed",
+              "gdr_recurrent_step_timed", "gdr_recurrent_step_bf16_state", "gdr_recurrent_multi",
+              "gdr_recurrent_step_conv"):
         assert n in names
 
 
