@@ -182,6 +182,53 @@ def decode_prologue(mixed_qkv, conv_state, conv_w, conv_b, a, b, A_log, dt_bias,
     return q, k, v, g, beta, new_state
 
 
+def prefill_prologue(mixed_qkv, conv_state, conv_w, conv_b, a, b, A_log, dt_bias, cu_seqlens,
+                     Nqk: int, Nv: int, D: int = 128, activation_bf16: bool = True):
+    """The steps in front of the chunkwise path for packed sequences (blog post
+    sections 3 and 4), in fp64: per sequence and channel, the causal depthwise
+    conv over the sequence's tokens, with the cached window (conv_state, or
+    zeros when None) in front of its first token; SiLU; cast to the activation
+    dtype; split into q | k | v.  The gates per token as in ``decode_prologue``.
+    The new window of a sequence is the last K values of (window, tokens).
+
+    Shapes: mixed_qkv [T, C]; conv_state [N, C, K] or None; conv_w [C, K];
+    conv_b [C] or None; a, b [T, Nv]; A_log, dt_bias [Nv]; cu_seqlens [N + 1].
+    Returns (q [T, Nqk, D], k [T, Nqk, D], v [T, Nv, D], g [T, Nv],
+    beta [T, Nv], new conv_state [N, C, K]).
+    """
+    x = _f64(mixed_qkv)
+    w = _f64(conv_w)
+    T, C = x.shape
+    K = w.shape[1]
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    N = cu.shape[0] - 1
+    if C != (2 * Nqk + Nv) * D or w.shape[0] != C:
+        raise ValueError("shape mismatch")
+    cs = np.zeros((N, C, K)) if conv_state is None else _f64(conv_state)
+    y = np.zeros((T, C))
+    new_state = np.zeros((N, C, K))
+    for n in range(N):
+        seq = x[cu[n]:cu[n + 1]].T                            # [C, len]
+        full = np.concatenate([cs[n], seq], axis=1)           # [C, K + len]
+        for t in range(seq.shape[1]):
+            # token t's window: the K values ending at it (positions t+1 .. t+K)
+            y[cu[n] + t] = np.sum(full[:, t + 1:t + 1 + K] * w, axis=1)
+        new_state[n] = full[:, -K:]
+    if conv_b is not None:
+        y = y + _f64(conv_b)[None, :]
+    y = y / (1.0 + np.exp(-y))
+    if activation_bf16:
+        y = round_bf16(y)
+    q = y[:, :Nqk * D].reshape(T, Nqk, D)
+    k = y[:, Nqk * D:2 * Nqk * D].reshape(T, Nqk, D)
+    v = y[:, 2 * Nqk * D:].reshape(T, Nv, D)
+    z = _f64(a) + _f64(dt_bias)[None, :]
+    softplus = np.maximum(z, 0.0) + np.log1p(np.exp(-np.abs(z)))
+    g = -np.exp(_f64(A_log))[None, :] * softplus
+    beta = 1.0 / (1.0 + np.exp(-_f64(b)))
+    return q, k, v, g, beta, new_state
+
+
 def recurrent_step_conv(mixed_qkv, conv_state, conv_w, conv_b, a, b, A_log, dt_bias, state_in,
                         Nqk: int, Nv: int, scale: float, activation_bf16: bool = True,
                         l2norm: bool = True, nthreads: int = 0):

@@ -114,3 +114,54 @@ def test_fused_step_from_zero_state_closed_form():
             bt = 1 / (1 + math.exp(-b[n, h]))
             assert np.allclose(out[n, h], bt * (kh @ qh) * vv, rtol=1e-12, atol=1e-15)
             assert np.allclose(st[n, h], bt * np.outer(vv, kh), rtol=1e-12, atol=1e-15)
+
+
+def test_prefill_conv_matches_torch_conv1d_with_cached_window():
+    """Per sequence: torch's grouped conv1d over (cached window, tokens), the
+    outputs at the token positions, bias, silu; the new window is the last K
+    values.  Ragged lengths, including an empty sequence and ones shorter than
+    the window."""
+    rng = np.random.default_rng(8)
+    Nqk, Nv, D, K = 1, 2, 4, 4
+    C = (2 * Nqk + Nv) * D
+    lengths = [5, 0, 2, 1, 9]
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    T = int(cu[-1])
+    x = rng.standard_normal((T, C))
+    cs = rng.standard_normal((len(lengths), C, K))
+    w = rng.standard_normal((C, K))
+    bias = rng.standard_normal(C)
+    q, k, v, _, _, new = oracle.prefill_prologue(x, cs, w, bias, np.zeros((T, Nv)),
+                                                 np.zeros((T, Nv)), np.zeros(Nv), np.zeros(Nv), cu,
+                                                 Nqk, Nv, D, activation_bf16=False)
+    got = np.concatenate([q.reshape(T, -1), k.reshape(T, -1), v.reshape(T, -1)], axis=1)
+    for n, L in enumerate(lengths):
+        seq = torch.from_numpy(np.concatenate([cs[n], x[cu[n]:cu[n + 1]].T], axis=1))[None]
+        ref = F.conv1d(seq, torch.from_numpy(w).unsqueeze(1), torch.from_numpy(bias), groups=C)
+        ref = F.silu(ref[0, :, 1:]).numpy().T                 # outputs at the L token positions
+        assert ref.shape == (L, C)
+        assert np.allclose(got[cu[n]:cu[n + 1]], ref, rtol=1e-13, atol=1e-14)
+        assert np.array_equal(new[n], seq[0, :, -K:].numpy())
+
+
+def test_prefill_equals_repeated_decode_prologue():
+    """Token by token, the decode branch gives the same outputs and windows."""
+    rng = np.random.default_rng(9)
+    Nqk, Nv, D, K, L = 1, 1, 2, 4, 6
+    C = (2 * Nqk + Nv) * D
+    x = rng.standard_normal((L, C))
+    cs = rng.standard_normal((1, C, K))
+    w = rng.standard_normal((C, K))
+    a = rng.standard_normal((L, Nv))
+    b = rng.standard_normal((L, Nv))
+    A_log, dt_bias = rng.standard_normal(Nv), rng.standard_normal(Nv)
+    pq, pk, pv, pg, pb, pnew = oracle.prefill_prologue(x, cs, w, None, a, b, A_log, dt_bias,
+                                                       [0, L], Nqk, Nv, D)
+    st = cs
+    for t in range(L):
+        dq, dk, dv, dg, db, st = oracle.decode_prologue(x[t:t + 1], st, w, None, a[t:t + 1],
+                                                        b[t:t + 1], A_log, dt_bias, Nqk, Nv, D)
+        assert np.array_equal(dq[0], pq[t]) and np.array_equal(dk[0], pk[t])
+        assert np.array_equal(dv[0], pv[t])
+        assert np.allclose(dg[0], pg[t], rtol=1e-15) and np.allclose(db[0], pb[t], rtol=1e-15)
+    assert np.array_equal(st, pnew)
