@@ -142,6 +142,27 @@ def recurrent_step_bf16_state(q, k, v, g, beta, state_in, scale: float, eps: flo
     return out, round_bf16(sout)
 
 
+def _activate(y, conv_b, activation_bf16: bool):
+    """Conv outputs [.., C] plus the bias, through SiLU (x / (1 + e^-x)), cast
+    to the activation dtype (bf16 via ``round_bf16`` when asked)."""
+    if conv_b is not None:
+        y = y + _f64(conv_b)[None, :]
+    y = y / (1.0 + np.exp(-y))
+    if activation_bf16:
+        y = round_bf16(y)
+    return y
+
+
+def _gates(a, b, A_log, dt_bias):
+    """Blog post section 4: g = -exp(A_log) softplus(a + dt_bias), beta =
+    sigmoid(b); softplus in its overflow-free form max(z, 0) + log1p(e^-|z|)."""
+    z = _f64(a) + _f64(dt_bias)[None, :]
+    softplus = np.maximum(z, 0.0) + np.log1p(np.exp(-np.abs(z)))
+    g = -np.exp(_f64(A_log))[None, :] * softplus
+    beta = 1.0 / (1.0 + np.exp(-_f64(b)))
+    return g, beta
+
+
 def decode_prologue(mixed_qkv, conv_state, conv_w, conv_b, a, b, A_log, dt_bias, Nqk: int,
                     Nv: int, D: int = 128, activation_bf16: bool = True):
     """The steps in front of a decode step (blog post, sections 3 and 4), in fp64.
@@ -167,18 +188,11 @@ def decode_prologue(mixed_qkv, conv_state, conv_w, conv_b, a, b, A_log, dt_bias,
         raise ValueError("shape mismatch")
     new_state = np.concatenate([cs[:, :, 1:], x[:, :, None]], axis=2)
     y = np.sum(new_state * w[None, :, :], axis=2)
-    if conv_b is not None:
-        y = y + _f64(conv_b)[None, :]
-    y = y / (1.0 + np.exp(-y))
-    if activation_bf16:
-        y = round_bf16(y)
+    y = _activate(y, conv_b, activation_bf16)
     q = y[:, :Nqk * D].reshape(N, Nqk, D)
     k = y[:, Nqk * D:2 * Nqk * D].reshape(N, Nqk, D)
     v = y[:, 2 * Nqk * D:].reshape(N, Nv, D)
-    z = _f64(a) + _f64(dt_bias)[None, :]
-    softplus = np.maximum(z, 0.0) + np.log1p(np.exp(-np.abs(z)))
-    g = -np.exp(_f64(A_log))[None, :] * softplus
-    beta = 1.0 / (1.0 + np.exp(-_f64(b)))
+    g, beta = _gates(a, b, A_log, dt_bias)
     return q, k, v, g, beta, new_state
 
 
@@ -214,18 +228,11 @@ def prefill_prologue(mixed_qkv, conv_state, conv_w, conv_b, a, b, A_log, dt_bias
             # token t's window: the K values ending at it (positions t+1 .. t+K)
             y[cu[n] + t] = np.sum(full[:, t + 1:t + 1 + K] * w, axis=1)
         new_state[n] = full[:, -K:]
-    if conv_b is not None:
-        y = y + _f64(conv_b)[None, :]
-    y = y / (1.0 + np.exp(-y))
-    if activation_bf16:
-        y = round_bf16(y)
+    y = _activate(y, conv_b, activation_bf16)
     q = y[:, :Nqk * D].reshape(T, Nqk, D)
     k = y[:, Nqk * D:2 * Nqk * D].reshape(T, Nqk, D)
     v = y[:, 2 * Nqk * D:].reshape(T, Nv, D)
-    z = _f64(a) + _f64(dt_bias)[None, :]
-    softplus = np.maximum(z, 0.0) + np.log1p(np.exp(-np.abs(z)))
-    g = -np.exp(_f64(A_log))[None, :] * softplus
-    beta = 1.0 / (1.0 + np.exp(-_f64(b)))
+    g, beta = _gates(a, b, A_log, dt_bias)
     return q, k, v, g, beta, new_state
 
 

@@ -32,7 +32,7 @@ MUTANTS = {
     "window_shifted_wrong_way": ("new_state = np.concatenate([cs[:, :, 1:], x[:, :, None]], axis=2)",
                                  "new_state = np.concatenate([x[:, :, None], cs[:, :, :-1]], axis=2)"),
     "silu_dropped": ("y = y / (1.0 + np.exp(-y))", "y = y"),
-    "bias_dropped": ("y = y + _f64(conv_b)[None, :]", "y = y"),
+    "bias_dropped": ("        y = y + _f64(conv_b)[None, :]", "        y = y"),
     "q_and_k_swapped": ("q = y[:, :Nqk * D].reshape(N, Nqk, D)",
                         "q = y[:, Nqk * D:2 * Nqk * D].reshape(N, Nqk, D)"),
     "softplus_dropped": ("g = -np.exp(_f64(A_log))[None, :] * softplus",
@@ -41,11 +41,14 @@ MUTANTS = {
     "beta_sign": ("beta = 1.0 / (1.0 + np.exp(-_f64(b)))", "beta = 1.0 / (1.0 + np.exp(_f64(b)))"),
     "activation_not_rounded": ("    if activation_bf16:\n        y = round_bf16(y)",
                                "    if False:\n        y = round_bf16(y)"),
+    "prefill_window_off_by_one": ("full[:, t + 1:t + 1 + K] * w", "full[:, t:t + K] * w"),
+    "prefill_new_window_from_start": ("new_state[n] = full[:, -K:]", "new_state[n] = full[:, :K]"),
     "A_log_not_exponentiated": ("g = -np.exp(_f64(A_log))[None, :] * softplus",
                                 "g = -_f64(A_log)[None, :] * softplus"),
 }
 
-REPLACED = ("round_bf16", "recurrent_step_bf16_state", "decode_prologue", "recurrent_step_conv")
+REPLACED = ("round_bf16", "recurrent_step_bf16_state", "decode_prologue", "prefill_prologue",
+            "recurrent_step_conv")
 
 
 def _mutant_module(name, old, new):
