@@ -19,7 +19,8 @@ the timed steps the decode step is also measured with its state stored in
 bf16 (``gdr_recurrent_step_bf16_state``, half the state bytes), reported as
 ``decode_bf16_state``, ``gdr_recurrent_multi`` on 256 sequences x 4 tokens
 as ``multi_token``, and the decode step with its conv update and gates fused
-in front as ``decode_conv``; none of them is part of the step.  One JSON line is printed.
+in front as ``decode_conv``, and the conv/gate prologue of the chunked path on
+the prefill workload as ``conv_prefill``; none of them is part of the step.  One JSON line is printed.
 """
 from __future__ import annotations
 
@@ -81,6 +82,13 @@ def alg_bytes_decode_conv(N, Nqk, Nv, K=4, es=2):
     state = N * Nv * D * D * 4 * 2
     return (state + N * C * es + 2 * N * C * K * es + C * K * es + N * Nv * D * es
             + N * Nv * 4 * 2 + Nv * 4 * 2)
+
+
+def alg_bytes_conv_prefill(T, N, Nqk, Nv, K=4, es=2):
+    """Projected channels read and q/k/v written once, a and b read and g and
+    beta written, kernels read once, every cached window read and written."""
+    C = (2 * Nqk + Nv) * D
+    return 2 * T * C * es + 4 * T * Nv * 4 + C * K * es + 2 * N * C * K * es + 2 * Nv * 4
 
 
 def measured_traffic(kernel: str):
@@ -284,6 +292,29 @@ def main() -> int:
     conv_bytes = alg_bytes_decode_conv(dec.N, dec.Nqk, dec.Nv)
     conv_gbps = conv_bytes / conv_s / 1e9
 
+    # ---- the conv/gate prologue of the chunked path (gdr_conv_prefill) at the
+    # prefill shape: cached windows in, new windows out; measured after the
+    # timed steps
+    from gated_deltanet_chunked_amd.inputs import prefill_prologue_inputs
+    pp = prefill_prologue_inputs(np.diff(pre.cu_seqlens).tolist(), Nqk, Nv, seed=cfg)
+    px = torch.from_numpy(pp.mixed_qkv).to(dev, torch.bfloat16)
+    pcs = torch.from_numpy(pp.conv_state).to(dev, torch.bfloat16)
+    pw = torch.from_numpy(pp.conv_w).to(dev, torch.bfloat16)
+    pf = {k_: torch.from_numpy(getattr(pp, k_)).to(dev) for k_ in ("a", "b", "A_log", "dt_bias")}
+    pcu = torch.from_numpy(pp.cu_seqlens).to(dev)
+    pcs_out = torch.empty_like(pcs)
+    for _ in range(args.warmup):
+        gdr.conv_prefill(px, pcs, pw, None, pf["a"], pf["b"], pf["A_log"], pf["dt_bias"], pcu,
+                         conv_state_out=pcs_out)
+    ptim = []
+    for _ in range(args.steps):
+        gdr.conv_prefill(px, pcs, pw, None, pf["a"], pf["b"], pf["A_log"], pf["dt_bias"], pcu,
+                         conv_state_out=pcs_out, timings=ptim)
+    torch.cuda.synchronize()
+    cp_s = float(np.mean([ms for _, ms in ptim])) * 1e-3
+    cp_bytes = alg_bytes_conv_prefill(T, N, Nqk, Nv)
+    cp_gbps = cp_bytes / cp_s / 1e9
+
     res = {
         "metric": "chunk GDR fwd tokens/s + % MFMA peak; decode-step GB/s (% HBM peak)",
         "value": round(tok_s, 1),
@@ -329,6 +360,11 @@ def main() -> int:
                         "gpu_ms": round(conv_s * 1e3, 4), "gbps": round(conv_gbps, 1),
                         "frac_hbm_peak": round(conv_gbps / HBM_PEAK_GBPS, 4),
                         "tokens_per_s": round(dec.N / conv_s, 1), "alg_bytes": conv_bytes},
+        "conv_prefill": {"workload": f"{T} tokens in {N} sequences, Nqk={Nqk} Nv={Nv} bf16, "
+                                     "conv kernel 4, cached windows in and out",
+                         "gpu_ms": round(cp_s * 1e3, 4), "gbps": round(cp_gbps, 1),
+                         "frac_hbm_peak": round(cp_gbps / HBM_PEAK_GBPS, 4),
+                         "tokens_per_s": round(T / cp_s, 1), "alg_bytes": cp_bytes},
         "roofline": roof,
     }
 

@@ -75,6 +75,10 @@ def load(path: str = LIB_PATH):
                                             i32, i32, i32, i32, ctypes.c_int, f32, u32, vp, vp,
                                             ctypes.POINTER(ctypes.c_float)]
     lib.gdr_recurrent_step_conv.restype = ctypes.c_int
+    lib.gdr_conv_prefill.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, i32, i32, i32,
+                                     i32, i32, ctypes.c_int, vp, vp, vp, vp, vp, vp,
+                                     ctypes.POINTER(ctypes.c_float)]
+    lib.gdr_conv_prefill.restype = ctypes.c_int
     lib.gdr_status_string.argtypes = [ctypes.c_int]
     lib.gdr_status_string.restype = ctypes.c_char_p
     lib.gdr_version.argtypes = []
@@ -287,6 +291,60 @@ def recurrent_step_conv(mixed_qkv, conv_state_in, conv_weight, conv_bias, a, b, 
     if timings is not None:
         timings.append(("decode_conv", float(ms.value)))
     return out, conv_state_out
+
+
+def conv_prefill(mixed_qkv, conv_state_in, conv_weight, conv_bias, a, b, A_log, dt_bias,
+                 cu_seqlens, *, conv_state_out=None, want_conv_state: bool = True,
+                 timings: Optional[list] = None):
+    """The conv/gate prologue of the chunkwise path (``gdr_conv_prefill``).
+
+    mixed_qkv [T, C] (q | k | v channels, C = (2 Nqk + Nv) 128); conv_state_in
+    [N, C, 4] or None (zeros); conv_weight [C, 4]; conv_bias [C] or None, all
+    in the activation dtype; a, b [T, Nv] f32; A_log, dt_bias [Nv] f32;
+    cu_seqlens [N + 1] int32 on the device.  Returns (q [T, Nqk, 128],
+    k, v [T, Nv, 128], g [T, Nv], beta [T, Nv], conv_state_out or None), ready
+    for ``chunk_fwd``.  With a list as ``timings`` the call waits for its
+    kernels and appends ("conv_prefill", ms).
+    """
+    import torch
+    lib = load()
+    T, C = mixed_qkv.shape
+    Nv = a.shape[1]
+    Nqk = (C // D - Nv) // 2
+    N = cu_seqlens.shape[0] - 1
+    K = conv_weight.shape[1]
+    dev = mixed_qkv.device
+    dt = mixed_qkv.dtype
+    code = _dtype_code(mixed_qkv)
+    if (2 * Nqk + Nv) * D != C:
+        raise ValueError(f"mixed_qkv has {C} channels, not (2 Nqk + Nv) * {D}")
+    _check(conv_state_in, "conv_state_in", (N, C, K), dt, dev)
+    _check(conv_weight, "conv_weight", (C, K), dt, dev)
+    _check(conv_bias, "conv_bias", (C,), dt, dev)
+    _check(a, "a", (T, Nv), torch.float32, dev)
+    _check(b, "b", (T, Nv), torch.float32, dev)
+    _check(A_log, "A_log", (Nv,), torch.float32, dev)
+    _check(dt_bias, "dt_bias", (Nv,), torch.float32, dev)
+    _check(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32, dev)
+    if conv_state_out is None and want_conv_state:
+        conv_state_out = torch.empty((N, C, K), dtype=dt, device=dev)
+    _check(conv_state_out, "conv_state_out", (N, C, K), dt, dev)
+    q = torch.empty((T, Nqk, D), dtype=dt, device=dev)
+    k = torch.empty((T, Nqk, D), dtype=dt, device=dev)
+    v = torch.empty((T, Nv, D), dtype=dt, device=dev)
+    g = torch.empty((T, Nv), dtype=torch.float32, device=dev)
+    beta = torch.empty((T, Nv), dtype=torch.float32, device=dev)
+    ms = ctypes.c_float(0.0)
+    st = lib.gdr_conv_prefill(_ptr(mixed_qkv), _ptr(conv_state_in), _ptr(conv_state_out),
+                              _ptr(conv_weight), _ptr(conv_bias), K, _ptr(a), _ptr(b), _ptr(A_log),
+                              _ptr(dt_bias), _ptr(cu_seqlens), N, T, Nqk, Nv, D, code, _ptr(q),
+                              _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _stream(),
+                              ctypes.byref(ms) if timings is not None else None)
+    if st != 0:
+        raise GdrError(st, "gdr_conv_prefill")
+    if timings is not None:
+        timings.append(("conv_prefill", float(ms.value)))
+    return q, k, v, g, beta, conv_state_out
 
 
 def recurrent_step(q, k, v, g, beta, state_in, *, state_out=None, out=None,

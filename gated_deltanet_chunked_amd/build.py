@@ -20,6 +20,7 @@ LIB = os.path.join(HERE, "libgdr.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["gdr_api.hip", "gdr_table.hip", "gdr_intra.hip", "gdr_inter.hip", "gdr_decode.hip",
+           "gdr_conv.hip",
            "gdr_validate.cpp"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -302,6 +302,58 @@ extern "C" gdr_status gdr_recurrent_step_conv(
   return GDR_OK;
 }
 
+extern "C" gdr_status gdr_conv_prefill(const void* mixed_qkv, const void* conv_state_in,
+                                       void* conv_state_out, const void* conv_weight,
+                                       const void* conv_bias, int32_t conv_k, const float* a,
+                                       const float* b, const float* A_log, const float* dt_bias,
+                                       const int32_t* cu_seqlens, int32_t N, int32_t T,
+                                       int32_t Nqk, int32_t Nv, int32_t D, gdr_dtype dtype,
+                                       void* q, void* k, void* v, float* g, float* beta,
+                                       void* stream, float* kernel_ms) {
+  ConvPrefillCheck c{mixed_qkv, conv_state_in, conv_state_out, conv_weight, conv_bias, conv_k,
+                     a, b, A_log, dt_bias, cu_seqlens, N, T, Nqk, Nv, D, dtype, q, k, v, g, beta};
+  const gdr_status s = validate_conv_prefill(c);
+  if (s != GDR_OK) return s;
+  if (kernel_ms) *kernel_ms = 0.0f;
+  if (T == 0 && !conv_state_out) return GDR_OK;
+  EventPairs pairs;
+  LaunchEvents e0{}, e1{};
+  if (kernel_ms) {
+    // one pair spans both launches: start of the first, end of the last
+    if (!pairs.create(1)) return GDR_ERR_HIP;
+    if (T > 0) e0.start = pairs.ev[0];
+    else e1.start = pairs.ev[0];
+    if (conv_state_out) e1.stop = pairs.ev[1];
+    else e0.stop = pairs.ev[1];
+  }
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const int32_t C = (2 * Nqk + Nv) * 128;
+  if (dtype == GDR_BF16) {
+    ConvPrefillArgs<__bf16> p{static_cast<const __bf16*>(mixed_qkv),
+                              static_cast<const __bf16*>(conv_state_in),
+                              static_cast<__bf16*>(conv_state_out),
+                              static_cast<const __bf16*>(conv_weight),
+                              static_cast<const __bf16*>(conv_bias), a, b, A_log, dt_bias,
+                              cu_seqlens, N, T, Nqk, Nv, C, static_cast<__bf16*>(q),
+                              static_cast<__bf16*>(k), static_cast<__bf16*>(v), g, beta};
+    launch_conv_prefill<__bf16>(p, st, e0, e1);
+  } else {
+    ConvPrefillArgs<float> p{static_cast<const float*>(mixed_qkv),
+                             static_cast<const float*>(conv_state_in),
+                             static_cast<float*>(conv_state_out),
+                             static_cast<const float*>(conv_weight),
+                             static_cast<const float*>(conv_bias), a, b, A_log, dt_bias,
+                             cu_seqlens, N, T, Nqk, Nv, C, static_cast<float*>(q),
+                             static_cast<float*>(k), static_cast<float*>(v), g, beta};
+    launch_conv_prefill<float>(p, st, e0, e1);
+  }
+  if (hipGetLastError() != hipSuccess) return GDR_ERR_HIP;
+  if (kernel_ms && (hipEventSynchronize(pairs.ev[1]) != hipSuccess ||
+                    hipEventElapsedTime(kernel_ms, pairs.ev[0], pairs.ev[1]) != hipSuccess))
+    return GDR_ERR_HIP;
+  return GDR_OK;
+}
+
 extern "C" const char* gdr_status_string(gdr_status s) {
   switch (s) {
     case GDR_OK: return "ok";

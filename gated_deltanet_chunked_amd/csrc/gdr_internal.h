@@ -96,6 +96,17 @@ struct ConvStepArgs {
   void* out;
 };
 
+struct ConvPrefillCheck {
+  const void* x; const void* cs_in; void* cs_out; const void* w; const void* bias;
+  int32_t conv_k;
+  const float* a; const float* b; const float* A_log; const float* dt_bias;
+  const int32_t* cu;
+  int32_t N, T, Nqk, Nv, D;
+  gdr_dtype dtype;
+  void* q; void* k; void* v; float* g; float* beta;
+};
+
+gdr_status validate_conv_prefill(const ConvPrefillCheck& a);
 gdr_status validate_chunk(const ChunkArgs& a);
 gdr_status validate_conv_step(const ConvStepArgs& a);
 gdr_status validate_step(const StepArgs& a);

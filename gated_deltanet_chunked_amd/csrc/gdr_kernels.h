@@ -99,4 +99,31 @@ void launch_decode_conv(const Tin* x, const Tin* cs_in, Tin* cs_out, const Tin* 
                         int32_t Nqk, int32_t Nv, float scale, int norm, Tin* out,
                         hipStream_t stream, LaunchEvents ev = {});
 
+// The conv/gate prologue of the chunkwise path over packed sequences.
+template <typename T>
+struct ConvPrefillArgs {
+  const T* x;           // [T, C] projected q|k|v, C = (2 Nqk + Nv) 128
+  const T* cs_in;       // [N, C, 4] cached windows (oldest first), or nullptr for zeros
+  T* cs_out;            // [N, C, 4] new windows, or nullptr; may equal cs_in
+  const T* w;           // [C, 4]
+  const T* bias;        // [C] or nullptr
+  const float* a;       // [T, Nv]
+  const float* b;       // [T, Nv]
+  const float* A_log;   // [Nv]
+  const float* dt_bias; // [Nv]
+  const int32_t* cu;    // [N + 1]
+  int32_t N, Ttok, Nqk, Nv, C;   // Ttok: tokens in the batch
+  T* q;                 // [T, Nqk, 128]
+  T* k;                 // [T, Nqk, 128]
+  T* v;                 // [T, Nv, 128]
+  float* g;             // [T, Nv]
+  float* beta;          // [T, Nv]
+};
+
+// Conv + gates over the tokens (skipped for T = 0), then the new windows
+// (when cs_out is set): up to two launches.
+template <typename T>
+void launch_conv_prefill(const ConvPrefillArgs<T>& p, hipStream_t stream, LaunchEvents ev_conv = {},
+                         LaunchEvents ev_window = {});
+
 }  // namespace gdr

@@ -163,4 +163,46 @@ gdr_status validate_conv_step(const ConvStepArgs& a) {
   return GDR_OK;
 }
 
+gdr_status validate_conv_prefill(const ConvPrefillCheck& a) {
+  gdr_status s = common_sizes(a.Nqk, a.Nv, a.D, a.dtype, 0u);
+  if (s != GDR_OK) return s;
+  if (a.conv_k != 4) return GDR_ERR_UNSUPPORTED;
+  if (a.N < 1 || a.T < 0) return GDR_ERR_INVALID_ARGUMENT;
+  const int64_t C = (2 * static_cast<int64_t>(a.Nqk) + a.Nv) * 128;
+  if (static_cast<int64_t>(a.T) * C > (int64_t(1) << 40)) return GDR_ERR_INVALID_ARGUMENT;
+  if (!a.w || !a.A_log || !a.dt_bias || !a.cu) return GDR_ERR_INVALID_ARGUMENT;
+  if (a.T > 0 && (!a.x || !a.a || !a.b || !a.q || !a.k || !a.v || !a.g || !a.beta))
+    return GDR_ERR_INVALID_ARGUMENT;
+  const void* ptrs[] = {a.x, a.cs_in, a.cs_out, a.w, a.bias, a.a, a.b, a.A_log, a.dt_bias,
+                        a.cu, a.q, a.k, a.v, a.g, a.beta};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return GDR_ERR_INVALID_ARGUMENT;
+  const int64_t es = static_cast<int64_t>(dtype_size(a.dtype));
+  const int64_t T = a.T, N = a.N;
+  const int64_t qk_bytes = T * a.Nqk * 128 * es, v_bytes = T * a.Nv * 128 * es;
+  const int64_t tv_bytes = T * a.Nv * 4, h_bytes = static_cast<int64_t>(a.Nv) * 4;
+  const int64_t cs_bytes = N * C * 4 * es;
+  struct R { const void* p; int64_t n; };
+  const R in[] = {{a.x, T * C * es}, {a.cs_in, cs_bytes}, {a.w, C * 4 * es}, {a.bias, C * es},
+                  {a.a, tv_bytes}, {a.b, tv_bytes}, {a.A_log, h_bytes}, {a.dt_bias, h_bytes},
+                  {a.cu, (N + 1) * 4}};
+  const R outs[] = {{a.cs_out, cs_bytes}, {a.q, qk_bytes}, {a.k, qk_bytes}, {a.v, v_bytes},
+                    {a.g, tv_bytes}, {a.beta, tv_bytes}};
+  constexpr int kIns = 9, kOuts = 6, kCsIn = 1, kCsOut = 0;
+  static_assert(sizeof(in) / sizeof(in[0]) == kIns && sizeof(outs) / sizeof(outs[0]) == kOuts,
+                "index constants out of date");
+  // each output overlaps no input and no other output; the new windows may
+  // replace the cached ones exactly (in place)
+  for (int i = 0; i < kOuts; ++i) {
+    for (int r = 0; r < kIns; ++r) {
+      if (i == kCsOut && r == kCsIn && a.cs_out == a.cs_in) continue;
+      if (overlap(outs[i].p, outs[i].n, in[r].p, in[r].n)) return GDR_ERR_INVALID_ARGUMENT;
+    }
+    for (int r = 0; r < kOuts; ++r)
+      if (r != i && overlap(outs[i].p, outs[i].n, outs[r].p, outs[r].n))
+        return GDR_ERR_INVALID_ARGUMENT;
+  }
+  return GDR_OK;
+}
+
 }  // namespace gdr

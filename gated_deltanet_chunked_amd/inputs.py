@@ -202,3 +202,50 @@ def prologue_inputs(N: int, Nqk: int, Nv: int, *, dtype: str = "bf16", seed: int
         cb = None if cb is None else round_to_bf16(cb)
     return PrologueInputs(mixed_qkv=x, conv_state=cs, conv_w=w, conv_b=cb, a=a, b=b, A_log=A_log,
                           dt_bias=dt_bias, state_in=state, Nqk=Nqk, Nv=Nv, dtype=dtype)
+
+
+@dataclasses.dataclass
+class PrefillPrologueInputs:
+    """Raw inputs of the conv/gate prologue over packed sequences."""
+
+    mixed_qkv: np.ndarray     # [T, C] float32 (bf16-representable for "bf16")
+    conv_state: Optional[np.ndarray]   # [N, C, K] same, or None
+    conv_w: np.ndarray        # [C, K]
+    conv_b: Optional[np.ndarray]       # [C] or None
+    a: np.ndarray             # [T, Nv] float32
+    b: np.ndarray             # [T, Nv] float32
+    A_log: np.ndarray         # [Nv] float32
+    dt_bias: np.ndarray       # [Nv] float32
+    cu_seqlens: np.ndarray    # [N + 1] int32
+    Nqk: int
+    Nv: int
+    dtype: str
+
+
+def prefill_prologue_inputs(lengths: Sequence[int], Nqk: int, Nv: int, *, dtype: str = "bf16",
+                            seed: int = 0, K: int = 4, bias: bool = False,
+                            cached: bool = True) -> PrefillPrologueInputs:
+    """Seeded draw with the distributions of ``prologue_inputs``, for packed
+    sequences of the given lengths; ``cached=False`` gives no cached windows."""
+    rng = np.random.default_rng(seed)
+    lengths = [int(x) for x in lengths]
+    T, N = int(sum(lengths)), len(lengths)
+    cu = np.zeros(N + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(np.asarray(lengths, dtype=np.int64)).astype(np.int32)
+    C = (2 * Nqk + Nv) * D
+    x = rng.standard_normal((T, C)).astype(np.float32)
+    cs = rng.standard_normal((N, C, K)).astype(np.float32) if cached else None
+    lim = 1.0 / np.sqrt(K)
+    w = rng.uniform(-lim, lim, (C, K)).astype(np.float32)
+    cb = rng.uniform(-lim, lim, C).astype(np.float32) if bias else None
+    a = rng.standard_normal((T, Nv)).astype(np.float32)
+    b = rng.standard_normal((T, Nv)).astype(np.float32)
+    A_log = np.log(rng.uniform(0.0, 16.0, Nv)).astype(np.float32)
+    dt_bias = np.ones(Nv, dtype=np.float32)
+    if dtype == "bf16":
+        x, w = round_to_bf16(x), round_to_bf16(w)
+        cs = None if cs is None else round_to_bf16(cs)
+        cb = None if cb is None else round_to_bf16(cb)
+    return PrefillPrologueInputs(mixed_qkv=x, conv_state=cs, conv_w=w, conv_b=cb, a=a, b=b,
+                                 A_log=A_log, dt_bias=dt_bias, cu_seqlens=cu, Nqk=Nqk, Nv=Nv,
+                                 dtype=dtype)

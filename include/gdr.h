@@ -20,7 +20,9 @@
  *   gdr_recurrent_step_bf16_state -- decode with the state stored in bf16;
  *   gdr_recurrent_multi           -- a few tokens per sequence, token by token;
  *   gdr_recurrent_step_conv       -- decode with the conv update and gates fused
- *                                    in front.
+ *                                    in front;
+ * and the conv/gate prologue of the chunkwise path:
+ *   gdr_conv_prefill              -- q, k, v, g, beta from projected channels.
  *
  * Conventions shared by all calls:
  *   - All tensor pointers are DEVICE pointers, caller-owned, contiguous,
@@ -252,6 +254,40 @@ gdr_status gdr_recurrent_step_conv(const void* mixed_qkv, const void* conv_state
                                    int32_t N, int32_t Nqk, int32_t Nv, int32_t D,
                                    gdr_dtype dtype, float scale, uint32_t flags, void* out,
                                    void* stream, float* kernel_ms);
+
+/*
+ * The steps in front of gdr_chunk_fwd for packed sequences (Qwen3-Next blog
+ * post, sections 3 and 4, the prefill branch): per sequence b and channel c
+ * (C = (2 Nqk + Nv) D channels, q then k then v, each head's D consecutive),
+ * the causal depthwise conv over the sequence's tokens with the cached window
+ * conv_state_in[b][c][0..K-1] (oldest first; NULL = zeros, the blog's
+ * prefill padding) in front of its first token:
+ *   y[t][c] = SiLU(sum_i conv_weight[c][i] x[t - K + 1 + i][c] + conv_bias[c])
+ * cast to dtype and split into q, k, v in the layouts gdr_chunk_fwd takes;
+ * the gates beta = sigmoid(b), g = -exp(A_log[h]) softplus(a + dt_bias[h]);
+ * and, if conv_state_out is not NULL, each sequence's new window, the last K
+ * values of (cached window, tokens).
+ *
+ * mixed_qkv      [T, C] dtype (the projected channels of every token)
+ * conv_state_in  [N, C, K] dtype, or NULL
+ * conv_state_out [N, C, K] dtype, or NULL; may equal conv_state_in
+ * conv_weight    [C, K] dtype;  conv_bias [C] dtype, or NULL
+ * conv_k         K; must be 4 (GDR_ERR_UNSUPPORTED otherwise)
+ * a, b           [T, Nv] float32;  A_log, dt_bias [Nv] float32
+ * cu_seqlens     [N + 1] int32, device, as for gdr_chunk_fwd
+ * q, k           [T, Nqk, D] dtype;  v [T, Nv, D] dtype;  g, beta [T, Nv] float32
+ * kernel_ms      NULL, or where to write the GPU time from the first kernel's
+ *                start to the last one's end (the call then blocks)
+ * Outputs overlap no input and no other output (except conv_state_out ==
+ * conv_state_in).  Two launches at most.
+ */
+gdr_status gdr_conv_prefill(const void* mixed_qkv, const void* conv_state_in,
+                            void* conv_state_out, const void* conv_weight, const void* conv_bias,
+                            int32_t conv_k, const float* a, const float* b, const float* A_log,
+                            const float* dt_bias, const int32_t* cu_seqlens, int32_t N,
+                            int32_t T, int32_t Nqk, int32_t Nv, int32_t D, gdr_dtype dtype,
+                            void* q, void* k, void* v, float* g, float* beta, void* stream,
+                            float* kernel_ms);
 
 /* A static, human-readable name for a status code. */
 const char* gdr_status_string(gdr_status s);

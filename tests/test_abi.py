@@ -292,3 +292,41 @@ def test_conv_step_validates_before_launching():
     assert call(s_out=addr["s_in"] + 4096) == INVALID                    # partial state overlap
     ms = ctypes.c_float(1.0)
     assert call(N=0, ms=ctypes.byref(ms)) == OK and ms.value == 0.0
+
+
+def test_conv_prefill_validates_before_launching():
+    """gdr_conv_prefill: sizes, kernel size, pointers and overlaps."""
+    import ctypes
+    lib = gdr.load()
+    T, N, Nqk, Nv = 16, 2, 2, 4
+    C = (2 * Nqk + Nv) * 128
+    sizes = dict(x=T * C * 2, cs_in=N * C * 8, cs_out=N * C * 8, w=C * 8, bias=C * 2, a=T * Nv * 4,
+                 b=T * Nv * 4, A_log=Nv * 4, dt_bias=Nv * 4, cu=(N + 1) * 4, q=T * Nqk * 256,
+                 k=T * Nqk * 256, v=T * Nv * 256, g=T * Nv * 4, beta=T * Nv * 4)
+    base, addr = 1 << 40, {}
+    for k_, n in sizes.items():
+        addr[k_] = base
+        base += (n + (1 << 20)) & ~255
+
+    def call(**over):
+        a = dict(addr, K=4, N=N, T=T, Nqk=Nqk, Nv=Nv, D=128, dtype=gdr.GDR_BF16, ms=None)
+        a.update(over)
+        return lib.gdr_conv_prefill(a["x"], a["cs_in"], a["cs_out"], a["w"], a["bias"], a["K"],
+                                    a["a"], a["b"], a["A_log"], a["dt_bias"], a["cu"], a["N"],
+                                    a["T"], a["Nqk"], a["Nv"], a["D"], a["dtype"], a["q"], a["k"],
+                                    a["v"], a["g"], a["beta"], None, a["ms"])
+
+    assert call(K=2) == UNSUPPORTED
+    assert call(D=64) == UNSUPPORTED
+    assert call(Nqk=3) == INVALID
+    assert call(N=0) == INVALID
+    assert call(T=-1) == INVALID
+    for name in ("x", "w", "a", "b", "A_log", "dt_bias", "cu", "q", "k", "v", "g", "beta"):
+        assert call(**{name: None}) == INVALID, name
+    assert call(q=addr["q"] + 4) == INVALID                        # misaligned
+    assert call(q=addr["x"]) == INVALID                            # output over an input
+    assert call(k=addr["q"]) == INVALID                            # two outputs at one address
+    assert call(cs_out=addr["cs_in"] + 256) == INVALID             # partial window overlap
+    assert call(g=addr["beta"]) == INVALID
+    ms = ctypes.c_float(1.0)
+    assert call(T=0, cs_out=None, ms=ctypes.byref(ms)) == OK and ms.value == 0.0

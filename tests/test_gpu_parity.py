@@ -477,3 +477,79 @@ def test_multi_token_empty_input():
     torch.cuda.synchronize()
     assert out.shape == (0, Nv, 128)
     assert torch.equal(st, s0)
+
+
+# ------------------------------------- conv/gate prologue of the chunked path
+
+
+def _conv_prefill(p, in_place=False, want_state=True):
+    import torch
+    dt = torch.bfloat16 if p.dtype == "bf16" else torch.float32
+    dv = lambda x, t=None: None if x is None else torch.from_numpy(x).to("cuda:0", t or torch.float32)
+    x, w, cb = dv(p.mixed_qkv, dt), dv(p.conv_w, dt), dv(p.conv_b, dt)
+    cs = dv(p.conv_state, dt)
+    cs_keep = None if cs is None else cs.clone()
+    res = gdr.conv_prefill(x, cs, w, cb, dv(p.a), dv(p.b), dv(p.A_log), dv(p.dt_bias),
+                           torch.from_numpy(p.cu_seqlens).to("cuda:0"),
+                           conv_state_out=cs if in_place else None, want_conv_state=want_state)
+    torch.cuda.synchronize()
+    if cs is not None and not in_place:
+        assert torch.equal(cs, cs_keep), "conv_state_in modified"
+    return res
+
+
+def _conv_prefill_oracle(p):
+    import oracle
+    return oracle.prefill_prologue(p.mixed_qkv, p.conv_state, p.conv_w, p.conv_b, p.a, p.b, p.A_log,
+                                   p.dt_bias, p.cu_seqlens, p.Nqk, p.Nv,
+                                   activation_bf16=(p.dtype == "bf16"))
+
+
+def _check_conv_prefill(res, ref, dtype, want_state=True):
+    q, k, v, g, beta, cs = res
+    rq, rk, rv, rg, rb, rcs = ref
+    for name, got, want in (("q", q, rq), ("k", k, rk), ("v", v, rv)):
+        _assert_close(name, to_f64(got), want, TOL[dtype])
+    # gates: fp32 exp/log1p against fp64
+    _assert_close("g", to_f64(g), rg, 1e-5)
+    _assert_close("beta", to_f64(beta), rb, 1e-5)
+    if want_state:
+        assert np.array_equal(to_f64(cs), rcs), "conv windows differ"
+    else:
+        assert cs is None
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_conv_prefill_ragged(dtype):
+    """Packed sequences shorter and longer than the window, one empty, cached
+    windows and a conv bias."""
+    from gated_deltanet_chunked_amd.inputs import prefill_prologue_inputs
+    p = prefill_prologue_inputs([5, 0, 2, 1, 9, 300], 2, 4, dtype=dtype, seed=81, bias=True)
+    _check_conv_prefill(_conv_prefill(p), _conv_prefill_oracle(p), dtype)
+
+
+def test_conv_prefill_no_cache_and_in_place():
+    from gated_deltanet_chunked_amd.inputs import prefill_prologue_inputs
+    p = prefill_prologue_inputs([7, 3], 1, 2, seed=82, cached=False)
+    _check_conv_prefill(_conv_prefill(p, want_state=False), _conv_prefill_oracle(p), "bf16",
+                        want_state=False)
+    p = prefill_prologue_inputs([7, 0, 3, 2], 1, 2, seed=83)
+    _check_conv_prefill(_conv_prefill(p, in_place=True), _conv_prefill_oracle(p), "bf16")
+
+
+def test_conv_prefill_then_chunk_fwd():
+    """The prologue feeding the chunkwise path at the prefill shape (T = 4096,
+    Nqk = 16, Nv = 32, bf16), end to end against the oracle's prologue and
+    recurrence."""
+    import oracle
+    import torch
+    from gated_deltanet_chunked_amd.inputs import prefill_prologue_inputs
+    p = prefill_prologue_inputs([4096], 16, 32, seed=84)
+    q, k, v, g, beta, _ = _conv_prefill(p, want_state=False)
+    cu = torch.from_numpy(p.cu_seqlens).to("cuda:0")
+    out, st = gdr.chunk_fwd(q, k, v, g, beta, cu, None, scale=SCALE)
+    torch.cuda.synchronize()
+    rq, rk, rv, rg, rb, _ = _conv_prefill_oracle(p)
+    ro, rs = oracle.recurrent(rq, rk, rv, rg, rb, None, p.cu_seqlens, SCALE)
+    _assert_close("out", to_f64(out), ro, TOL["bf16"])
+    _assert_close("state", to_f64(st), rs, TOL["bf16"])
