@@ -69,9 +69,17 @@ __global__ __launch_bounds__(256) void conv_prefill_kernel(ConvPrefillArgs<T> p)
     auto before = [&](int pos) -> float {
       return pos >= start ? to_f32(p.x[(size_t)pos * p.C + c]) : cached(b, min(start - pos, 3));
     };
+    // all of the block's token values at once (the tail repeats the block's
+    // last token, which exists), so the loads are in flight together
+    T xs[kTokPerBlock];
+#pragma unroll
+    for (int i = 0; i < kTokPerBlock; ++i) xs[i] = p.x[(size_t)min(t0 + i, t1 - 1) * p.C + c];
     float w1 = before(t0 - 3), w2 = before(t0 - 2), w3 = before(t0 - 1);
     const int qk = p.Nqk * kD;
-    for (int t = t0; t < t1; ++t) {
+#pragma unroll
+    for (int i = 0; i < kTokPerBlock; ++i) {
+      const int t = t0 + i;
+      if (t >= t1) break;
       if (t >= end) {   // a new sequence (after any empty ones) starts here
         b = owner(p.cu, p.N, p.Ttok, t);
         start = min(max(p.cu[b], 0), p.Ttok);
@@ -80,7 +88,7 @@ __global__ __launch_bounds__(256) void conv_prefill_kernel(ConvPrefillArgs<T> p)
         w2 = cached(b, 2);
         w3 = cached(b, 1);
       }
-      const float xt = to_f32(p.x[(size_t)t * p.C + c]);
+      const float xt = to_f32(xs[i]);
       float y = bias + w[0] * w1 + w[1] * w2 + w[2] * w3 + w[3] * xt;
       y = y / (1.0f + expf(-y));
       if (c < qk) p.q[(size_t)t * qk + c] = from_f32<T>(y);
