@@ -365,4 +365,4 @@ extern "C" const char* gdr_status_string(gdr_status s) {
   return "unknown status";
 }
 
-extern "C" const char* gdr_version(void) { return "libgdr 0.1"; }
+extern "C" const char* gdr_version(void) { return "libgdr 0.2"; }
