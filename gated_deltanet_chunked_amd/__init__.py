@@ -177,7 +177,7 @@ def chunk_fwd(q, k, v, g, beta, cu_seqlens, state_in=None, *, scale: Optional[fl
         if st != 0:
             raise GdrError(st, "gdr_chunk_fwd")
         return out, state_out
-    cap = 64
+    cap = 1024
     ms = (ctypes.c_float * cap)()
     kind = (ctypes.c_int32 * cap)()
     n = ctypes.c_int32(0)

@@ -3,6 +3,8 @@
 // on the caller's stream.  No allocation, no synchronisation.
 #include <hip/hip_runtime.h>
 
+#include <vector>
+
 #include "../../include/gdr.h"
 #include "gdr_internal.h"
 #include "gdr_kernels.h"
@@ -12,16 +14,23 @@ using namespace gdr;
 namespace {
 
 // Optional per-launch timing: launch i gets the event pair ev[2i], ev[2i+1],
-// which the runtime records at that kernel's start and end.  With no event
-// array every launch is untimed.
+// which the runtime records at that kernel's start and end.  With span_only,
+// only the first launch's start (ev[0]) and the last launch's end (ev[1]) are
+// recorded, `total` being the number of launches.  With no event array every
+// launch is untimed.
 struct Recorder {
   hipEvent_t* ev = nullptr;
   int32_t* kind = nullptr;
   int32_t cap = 0;
   int32_t n = 0;
+  bool span_only = false;
+  int32_t total = 0;
   LaunchEvents next(int32_t k) {
     LaunchEvents e;
-    if (ev && n < cap) {
+    if (ev && span_only) {
+      if (n == 0) e.start = ev[0];
+      if (n == total - 1) e.stop = ev[1];
+    } else if (ev && n < cap) {
       kind[n] = k;
       e.start = ev[2 * n];
       e.stop = ev[2 * n + 1];
@@ -31,19 +40,21 @@ struct Recorder {
   }
 };
 
-// Event pairs for up to kMaxTimed timed launches, destroyed with the object.
-constexpr int32_t kMaxTimed = 64;
+// Event pairs for timed launches, destroyed with the object.
 struct EventPairs {
-  hipEvent_t ev[2 * kMaxTimed];
-  int32_t made = 0;
+  std::vector<hipEvent_t> ev;
   bool create(int32_t launches) {
-    if (launches < 0 || launches > kMaxTimed) return false;
-    for (; made < 2 * launches; ++made)
-      if (hipEventCreate(&ev[made]) != hipSuccess) return false;
+    if (launches < 0) return false;
+    ev.reserve(2 * static_cast<size_t>(launches));
+    while (ev.size() < 2 * static_cast<size_t>(launches)) {
+      hipEvent_t e;
+      if (hipEventCreate(&e) != hipSuccess) return false;
+      ev.push_back(e);
+    }
     return true;
   }
   ~EventPairs() {
-    for (int32_t i = 0; i < made; ++i) (void)hipEventDestroy(ev[i]);
+    for (hipEvent_t e : ev) (void)hipEventDestroy(e);
   }
 };
 
@@ -71,21 +82,26 @@ gdr_status run_chunk(const ChunkArgs& a, hipStream_t st, Recorder& rec) {
   const int norm = (a.flags & GDR_FLAG_QK_L2NORM) ? 1 : 0;
   const int32_t nslots = static_cast<int32_t>(w.nslots);
 
+  // Every launch is checked at once: hipGetLastError also clears the error,
+  // so a failed launch followed by a good one would otherwise go unseen.
   Chunks chunks{nullptr, nullptr, a.cu_seqlens, a.T};
   if (a.N > 1) {
     launch_table(a.cu_seqlens, a.N, a.T, nslots, table, choff, st, rec.next(GDR_STAGE_TABLE));
+    if (hipGetLastError() != hipSuccess) return GDR_ERR_HIP;
     chunks.table = table;
     chunks.choff = choff;
   }
   for (int64_t s0 = 0; s0 < w.nslots; s0 += w.seg_slots) {
     const int32_t nseg = static_cast<int32_t>(w.nslots - s0 < w.seg_slots ? w.nslots - s0 : w.seg_slots);
-    launch_intra<T>(q, k, v, a.g, a.beta, chunks, a.Nqk, a.Nv, static_cast<int32_t>(s0), nseg,
-                    a.scale, norm, inter, gam, st, rec.next(GDR_STAGE_INTRA));
+    if (launch_intra<T>(q, k, v, a.g, a.beta, chunks, a.Nqk, a.Nv, static_cast<int32_t>(s0), nseg,
+                        a.scale, norm, inter, gam, st, rec.next(GDR_STAGE_INTRA)) != hipSuccess)
+      return GDR_ERR_HIP;
     launch_inter<T>(inter, chunks, gam, a.state_in, carry, a.state_out, a.N, a.Nv,
                     static_cast<int32_t>(s0), nseg, s0 == 0, out, discard, st,
                     rec.next(GDR_STAGE_INTER));
+    if (hipGetLastError() != hipSuccess) return GDR_ERR_HIP;
   }
-  return hipGetLastError() == hipSuccess ? GDR_OK : GDR_ERR_HIP;
+  return GDR_OK;
 }
 
 gdr_status dispatch_chunk(const ChunkArgs& a, hipStream_t st, Recorder& rec) {
@@ -132,23 +148,28 @@ extern "C" gdr_status gdr_chunk_fwd_timed(const void* q, const void* k, const vo
   if (s != GDR_OK) return s;
   if (!kernel_ms || !kernel_kind || !n || max_kernels < 0) return GDR_ERR_INVALID_ARGUMENT;
   const int32_t need = launches_needed(plan_workspace(T, N, Nqk, Nv, dtype), N);
-  if (need > max_kernels) return GDR_ERR_INVALID_ARGUMENT;
+  // more launches than the caller's arrays hold: the span alone is timed
+  const bool span_only = need > max_kernels;
   hipStream_t st = static_cast<hipStream_t>(stream);
   EventPairs pairs;
-  if (!pairs.create(need)) return need > kMaxTimed ? GDR_ERR_INVALID_ARGUMENT : GDR_ERR_HIP;
+  if (!pairs.create(span_only ? 1 : need)) return GDR_ERR_HIP;
   Recorder rec;
-  rec.ev = pairs.ev;
+  rec.ev = pairs.ev.data();
   rec.kind = kernel_kind;
   rec.cap = need;
+  rec.span_only = span_only;
+  rec.total = need;
   s = dispatch_chunk(a, st, rec);
-  if (s == GDR_OK && hipEventSynchronize(pairs.ev[2 * rec.n - 1]) != hipSuccess) s = GDR_ERR_HIP;
+  const hipEvent_t first = pairs.ev[0];
+  const hipEvent_t last = span_only ? pairs.ev[1] : pairs.ev[2 * rec.n - 1];
+  if (s == GDR_OK && hipEventSynchronize(last) != hipSuccess) s = GDR_ERR_HIP;
   if (s == GDR_OK) {
-    for (int32_t i = 0; i < rec.n; ++i)
+    const int32_t timed = span_only ? 0 : rec.n;
+    for (int32_t i = 0; i < timed; ++i)
       if (hipEventElapsedTime(&kernel_ms[i], pairs.ev[2 * i], pairs.ev[2 * i + 1]) != hipSuccess)
         s = GDR_ERR_HIP;
-    if (span_ms && hipEventElapsedTime(span_ms, pairs.ev[0], pairs.ev[2 * rec.n - 1]) != hipSuccess)
-      s = GDR_ERR_HIP;
-    *n = rec.n;
+    if (span_ms && hipEventElapsedTime(span_ms, first, last) != hipSuccess) s = GDR_ERR_HIP;
+    *n = timed;
   }
   return s;
 }

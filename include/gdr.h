@@ -143,10 +143,10 @@ gdr_status gdr_recurrent_step(const void* q, const void* k, const void* v,
  *   kernel_kind[i] which stage it was (GDR_STAGE_*);
  * and, if span_ms is not NULL, the time from the first kernel's start to the
  * last kernel's end (the call's GPU time, gaps between its kernels included).
- * max_kernels bounds both arrays; a call needing more launches than that, or
- * more than 64, returns GDR_ERR_INVALID_ARGUMENT before launching anything.
- * The number of launches is 2 * ceil(slots / segment), plus 1 (the chunk
- * table) when N > 1: a handful for the configurations of the pages.
+ * max_kernels bounds both arrays.  A call needing more launches than that
+ * still runs, but times only its span: *n is then 0 and the arrays are not
+ * written.  The number of launches is 2 * ceil(slots / segment), plus 1 (the
+ * chunk table) when N > 1: a handful for the configurations of the pages.
  */
 #define GDR_STAGE_TABLE 0   /* chunk table from cu_seqlens */
 #define GDR_STAGE_INTRA 1   /* norms, gate cumsum, intra-chunk products; parallel over chunks */

@@ -65,3 +65,53 @@ def oracle_heads(inp: GdrInputs, heads: Sequence[int], seqs: Optional[Sequence[i
 
 
 rel_l2 = oracle.rel_l2
+
+
+def per_seq_head_rel(got_out, ref_out, got_st, ref_st, cu) -> Dict[str, np.ndarray]:
+    """Relative L2 error of every (sequence, value head) separately.
+
+    Returns {"out": [N, Nv], "state": [N, Nv]} (state only when both states are
+    given).  Empty sequences have no output and get NaN there.  Where the
+    reference is all zeros the absolute L2 error stands in (as in rel_l2).
+    """
+    cu = np.asarray(cu, dtype=np.int64)
+    N = cu.shape[0] - 1
+    res = {}
+    d2 = ((np.asarray(got_out, np.float64) - ref_out) ** 2).sum(axis=-1)   # [T, Nv]
+    r2 = (np.asarray(ref_out, np.float64) ** 2).sum(axis=-1)
+    Nv = d2.shape[1] if d2.ndim == 2 else ref_out.shape[1]
+    eo = np.full((N, Nv), np.nan)
+    for b in range(N):
+        t0, t1 = cu[b], cu[b + 1]
+        if t1 > t0:
+            num = np.sqrt(d2[t0:t1].sum(axis=0))
+            den = np.sqrt(r2[t0:t1].sum(axis=0))
+            eo[b] = np.where(den > 0, num / np.where(den > 0, den, 1.0), num)
+    res["out"] = eo
+    if got_st is not None and ref_st is not None:
+        num = np.sqrt(((np.asarray(got_st, np.float64) - ref_st) ** 2).sum(axis=(-2, -1)))
+        den = np.sqrt((np.asarray(ref_st, np.float64) ** 2).sum(axis=(-2, -1)))
+        res["state"] = np.where(den > 0, num / np.where(den > 0, den, 1.0), num)
+    return res
+
+
+def assert_close_per_seq_head(got_out, ref_out, got_st, ref_st, cu, tol, name=""):
+    """Relative L2 within ``tol`` over each whole tensor AND for every
+    (sequence, value head) on its own, so an error confined to one short
+    sequence or one head is not diluted by the rest.  Prints the worst."""
+    for what, g, r in (("out", got_out, ref_out), ("state", got_st, ref_st)):
+        if g is None or r is None:
+            continue
+        assert np.isfinite(g).all(), f"{name} {what}: non-finite values"
+        err = rel_l2(g, r)
+        print(f"{name} {what}: rel L2 {err:.3e} (tolerance {tol:.0e})")
+        assert err <= tol, f"{name} {what}: rel L2 {err:.3e} > {tol:.0e}"
+    per = per_seq_head_rel(got_out, ref_out, got_st, ref_st, cu)
+    for what, e in per.items():
+        if np.all(np.isnan(e)):
+            continue
+        b, h = np.unravel_index(np.nanargmax(e), e.shape)
+        worst = float(e[b, h])
+        print(f"{name} {what}: worst (sequence, head) ({b}, {h}) rel L2 {worst:.3e}")
+        assert worst <= tol, f"{name} {what}: (sequence {b}, head {h}) rel L2 {worst:.3e} > {tol:.0e}"
+    return per

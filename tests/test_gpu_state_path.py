@@ -1,0 +1,326 @@
+"""GPU tests of the state path of the chunkwise form and the decode step,
+through the C ABI: closed forms, long slow-decay runs, wide query/key groups,
+split invariance, every way a multi-segment call carries the state, and
+guard bands around every output.
+
+Closed forms (Qwen3-Next blog post, section 5(2): the state decays, then the
+delta write; o_t = S_t qh_t):
+* beta = 0: no write, so S_T = exp(sum g) S_0 and o_t = exp(sum_{s<=t} g_s) S_0 qh_t;
+* g = 0, beta = 1 with orthonormal keys k_i: from S_0 = 0 each write adds
+  c v_i k_i^T (c = 1/sqrt(1 + eps), the normalised key's length), so reading
+  with q = k_i (beta = 0) returns scale c^2 v_i, and S = c sum_i v_i k_i^T.
+Every case is also compared with the fp64 oracle per (sequence, value head).
+"""
+import numpy as np
+import pytest
+
+import gated_deltanet_chunked_amd as gdr
+from gated_deltanet_chunked_amd.inputs import GdrInputs, make_inputs, orthonormal_keys
+from tests.gpu_util import (SCALE, TOL, assert_close_per_seq_head, device_tensors, oracle_full,
+                            rel_l2, to_f64)
+
+pytestmark = pytest.mark.gpu
+
+EPS = 1e-6
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    gdr.load()
+    yield
+    torch.cuda.synchronize()
+
+
+def _chunk(inp, state="in", want_state=True, in_place=False):
+    import torch
+    t = device_tensors(inp)
+    s_in = t["state_in"] if state == "in" else None
+    s_out = s_in if (in_place and s_in is not None) else None
+    out, st = gdr.chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], t["cu"], s_in,
+                            scale=SCALE, state_out=s_out, want_state=want_state)
+    torch.cuda.synchronize()
+    if in_place and s_in is not None:
+        assert st.data_ptr() == s_in.data_ptr()
+    return to_f64(out), (to_f64(st) if st is not None else None)
+
+
+def _normalised(x):
+    x = np.asarray(x, np.float64)
+    return x / np.sqrt((x * x).sum(axis=-1, keepdims=True) + EPS)
+
+
+# -------------------------------------------------------------- beta = 0
+
+
+def _pure_decay_closed_form(inp):
+    """o and S_out of beta = 0 written out from the closed form (fp64)."""
+    G = inp.Nv // inp.Nqk
+    cu = inp.cu_seqlens
+    qh = SCALE * _normalised(inp.q)                       # [T, Nqk, D]
+    out = np.zeros((inp.T, inp.Nv, 128))
+    st = np.zeros((inp.N, inp.Nv, 128, 128))
+    s0 = inp.state_in.astype(np.float64)
+    for b in range(inp.N):
+        t0, t1 = cu[b], cu[b + 1]
+        decay = np.exp(np.cumsum(inp.g[t0:t1].astype(np.float64), axis=0))   # [len, Nv]
+        for h in range(inp.Nv):
+            Sq = qh[t0:t1, h // G] @ s0[b, h].T                              # rows S_0 qh_t
+            out[t0:t1, h] = decay[:, h:h + 1] * Sq
+            st[b, h] = (decay[-1, h] if t1 > t0 else 1.0) * s0[b, h]
+    return out, st
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_beta_zero_chunk_is_pure_decay(dtype):
+    inp = make_inputs([300, 77, 129], 2, 4, dtype=dtype, seed=101, state_std=1.0,
+                      A_range=(0.0, 0.02))
+    inp.beta[:] = 0.0
+    out, st = _chunk(inp)
+    co, cs = _pure_decay_closed_form(inp)
+    assert_close_per_seq_head(out, co, st, cs, inp.cu_seqlens, TOL[dtype], name="closed form")
+    ro, rs = oracle_full(inp)
+    assert_close_per_seq_head(out, ro, st, rs, inp.cu_seqlens, TOL[dtype], name="oracle")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_beta_zero_decode_is_pure_decay(dtype):
+    import torch
+    inp = make_inputs([1] * 6, 2, 4, dtype=dtype, seed=102, state_std=1.0)
+    inp.beta[:] = 0.0
+    t = device_tensors(inp)
+    s = t["state_in"].clone()
+    out = gdr.recurrent_step(t["q"], t["k"], t["v"], t["g"], t["beta"], s, scale=SCALE)
+    torch.cuda.synchronize()
+    co, cs = _pure_decay_closed_form(inp)
+    assert_close_per_seq_head(to_f64(out), co, to_f64(s), cs, inp.cu_seqlens, TOL[dtype],
+                              name="closed form")
+
+
+# ------------------------------------------------------ exact retrieval
+
+
+def _retrieval_inputs(dtype, seqs, Nqk=2, Nv=4, seed=103):
+    """Per sequence of n: n writes (g = 0, beta = 1, orthonormal keys k_i,
+    random values), then n reads (beta = 0, g = 0, q = k_perm(i)).  Returns the
+    inputs and, per sequence, (first read token, permutation)."""
+    rng = np.random.default_rng(seed)
+    T = 2 * sum(seqs)
+    q = rng.standard_normal((T, Nqk, 128))
+    k = np.zeros((T, Nqk, 128))
+    v = rng.standard_normal((T, Nv, 128))
+    g = np.zeros((T, Nv))
+    beta = np.zeros((T, Nv))
+    reads = []
+    t = 0
+    for si, n in enumerate(seqs):
+        perm = rng.permutation(n)
+        for j in range(Nqk):
+            keys = orthonormal_keys(n, 128, seed=seed + 17 * si + j)
+            k[t:t + n, j] = keys
+            q[t + n:t + 2 * n, j] = keys[perm]
+            k[t + n:t + 2 * n, j] = keys[perm]
+        beta[t:t + n] = 1.0
+        reads.append((t + n, perm))
+        t += 2 * n
+    cu = np.concatenate([[0], np.cumsum([2 * n for n in seqs])]).astype(np.int32)
+    f = np.float32
+    if dtype == "bf16":
+        from gated_deltanet_chunked_amd.inputs import round_to_bf16
+        rd = lambda x: round_to_bf16(x.astype(f))
+    else:
+        rd = lambda x: x.astype(f)
+    inp = GdrInputs(q=rd(q), k=rd(k), v=rd(v), g=g.astype(f), beta=beta.astype(f), state_in=None,
+                    cu_seqlens=cu, dtype=dtype, seed=seed)
+    return inp, reads
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_exact_retrieval_chunk(dtype):
+    """Writes and reads inside one chunk (64 + 64), across a chunk boundary
+    (100 + 100) and a full basis (128 + 128)."""
+    seqs = [64, 100, 128]
+    inp, reads = _retrieval_inputs(dtype, seqs)
+    out, st = _chunk(inp, state=None)
+    ro, rs = oracle_full(inp, state_in=None)
+    assert_close_per_seq_head(out, ro, st, rs, inp.cu_seqlens, TOL[dtype], name="oracle")
+    c2 = 1.0 / (1.0 + EPS)
+    G = inp.Nv // inp.Nqk
+    for (r0, perm), n, b in zip(reads, seqs, range(len(seqs))):
+        w0 = r0 - n
+        want = SCALE * c2 * inp.v[w0:r0][perm].astype(np.float64)          # [n, Nv, D]
+        got = out[r0:r0 + n]
+        # fp32 keys are orthonormal to ~1e-7; bf16-rounded keys only to ~4e-3
+        tol = 1e-4 if dtype == "f32" else 2e-2
+        err = rel_l2(got, want)
+        print(f"sequence {b}: retrieved values rel L2 {err:.3e}")
+        assert err <= tol
+        if dtype == "f32":
+            for h in range(inp.Nv):
+                keys = inp.k[w0:r0, h // G].astype(np.float64)
+                S = np.sqrt(c2) * inp.v[w0:r0, h].astype(np.float64).T @ keys
+                assert rel_l2(st[b, h], S) <= 1e-4
+
+
+# ------------------------------------------------ long slow-decay runs
+
+
+def test_long_slow_decay_bf16():
+    """T = 32768 (256 serial chunks), Nqk = 16, Nv = 32, bf16, gates near 1
+    (A ~ U(0, 0.05)) and a unit-scale initial state: the state carries across
+    the whole sequence, so rounding in the state pass would accumulate."""
+    inp = make_inputs([32768], 16, 32, dtype="bf16", seed=104, state_std=1.0,
+                      A_range=(0.0, 0.05))
+    out, st = _chunk(inp)
+    ro, rs = oracle_full(inp)
+    assert_close_per_seq_head(out, ro, st, rs, inp.cu_seqlens, TOL["bf16"], name="T=32768")
+
+
+# ------------------------------------------------- wide query/key groups
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("Nqk", [4, 2], ids=["G8", "G16"])
+def test_wide_groups(dtype, Nqk):
+    """Nv = 32 value heads on 4 (G = 8) or 2 (G = 16) query/key heads."""
+    inp = make_inputs([700, 1, 333], Nqk, 32, dtype=dtype, seed=105 + Nqk, state_std=0.1,
+                      A_range=(0.0, 1.0))
+    out, st = _chunk(inp)
+    ro, rs = oracle_full(inp)
+    assert_close_per_seq_head(out, ro, st, rs, inp.cu_seqlens, TOL[dtype])
+
+
+# ----------------------------------------------------- split invariance
+
+
+def _slice(inp, t0, t1, state):
+    return GdrInputs(q=inp.q[t0:t1], k=inp.k[t0:t1], v=inp.v[t0:t1], g=inp.g[t0:t1],
+                     beta=inp.beta[t0:t1], state_in=state,
+                     cu_seqlens=np.array([0, t1 - t0], np.int32), dtype=inp.dtype, seed=inp.seed)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_split_sequence_equals_whole(dtype):
+    """chunk_fwd on tokens [0, 1000), then on [1000, 2100) from its final
+    state, equals chunk_fwd on [0, 2100): the state carries a sequence across
+    calls (the operator page's state reuse)."""
+    inp = make_inputs([2100], 2, 4, dtype=dtype, seed=107, state_std=0.5, A_range=(0.0, 0.5))
+    whole_o, whole_s = _chunk(inp)
+    o1, s1 = _chunk(_slice(inp, 0, 1000, inp.state_in))
+    o2, s2 = _chunk(_slice(inp, 1000, 2100, s1.astype(np.float32)))
+    split_o = np.concatenate([o1, o2])
+    ro, rs = oracle_full(inp)
+    assert_close_per_seq_head(split_o, ro, s2, rs, inp.cu_seqlens, TOL[dtype], name="split")
+    assert_close_per_seq_head(whole_o, ro, whole_s, rs, inp.cu_seqlens, TOL[dtype], name="whole")
+    assert_close_per_seq_head(split_o, whole_o, s2, whole_s, inp.cu_seqlens, TOL[dtype],
+                              name="split vs whole")
+
+
+# ------------------------------------------- multi-segment state carry
+
+
+@pytest.mark.parametrize("mode", ["in_place", "no_state_out", "no_state_in", "fp32"])
+def test_multi_segment_carry(mode):
+    """Calls long enough to take several segments (the intra-chunk products
+    of one segment are consumed before the next segment's are made), with
+    sequences spanning segment boundaries, and every way the state is
+    carried between segments: in place, through the workspace (no state_out),
+    from zeros (no state_in), and in fp32 (smaller segments)."""
+    if mode == "fp32":
+        inp = make_inputs([2500, 1700, 900], 8, 32, dtype="f32", seed=108, state_std=0.5,
+                          A_range=(0.0, 0.5))
+    else:
+        inp = make_inputs([3000, 5000, 2100], 16, 32, dtype="bf16", seed=109, state_std=0.5,
+                          A_range=(0.0, 0.5))
+    state = None if mode == "no_state_in" else "in"
+    out, st = _chunk(inp, state=state, want_state=(mode != "no_state_out"),
+                     in_place=(mode == "in_place"))
+    ro, rs = oracle_full(inp, state_in=None) if state is None else oracle_full(inp)
+    if mode == "no_state_out":
+        assert st is None
+        rs = None
+    assert_close_per_seq_head(out, ro, st, rs, inp.cu_seqlens, TOL[inp.dtype], name=mode)
+
+
+def test_single_sequence_multi_segment_in_place():
+    inp = make_inputs([9000], 16, 32, dtype="bf16", seed=110, state_std=0.5, A_range=(0.0, 0.5))
+    out, st = _chunk(inp, in_place=True)
+    ro, rs = oracle_full(inp)
+    assert_close_per_seq_head(out, ro, st, rs, inp.cu_seqlens, TOL["bf16"])
+
+
+# ------------------------------------------------------- guard bands
+
+
+PAD = 4096   # elements of guard band on each side (16-byte multiples for both dtypes)
+
+
+def _guarded(shape, dtype, fill):
+    """A tensor of `shape` inside a larger buffer whose guard bands hold `fill`."""
+    import torch
+    n = int(np.prod(shape))
+    buf = torch.full((PAD + n + PAD,), fill, dtype=dtype, device="cuda:0")
+    return buf, buf[PAD:PAD + n].view(*shape)
+
+
+def _check_guards(buf, fill, name):
+    import torch
+    lo, hi = buf[:PAD], buf[-PAD:]
+    assert torch.all(lo == fill).item() and torch.all(hi == fill).item(), \
+        f"{name}: a kernel wrote outside its buffer"
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_guard_bands_chunk(dtype):
+    """out, state_out and the workspace sit between guard bands; no kernel
+    writes outside them (ragged tails, one-token and empty sequences, several
+    segments)."""
+    import torch
+    lengths = [300, 1, 0, 129, 77, 5000]
+    inp = make_inputs(lengths, 16, 32, dtype=dtype, seed=111, state_std=0.1)
+    t = device_tensors(inp)
+    tdt = t["q"].dtype
+    ob, out = _guarded((inp.T, inp.Nv, 128), tdt, -7.0)
+    sb, st = _guarded((inp.N, inp.Nv, 128, 128), torch.float32, -9.0)
+    need = gdr.workspace_size(inp.T, inp.N, inp.Nqk, inp.Nv,
+                              gdr.GDR_BF16 if dtype == "bf16" else gdr.GDR_F32)
+    wb = torch.full((need + 2 * PAD,), 0xA5, dtype=torch.uint8, device="cuda:0")
+    ws = wb[PAD:PAD + need]
+    gdr.chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], t["cu"], t["state_in"],
+                  scale=SCALE, out=out, state_out=st, workspace=ws)
+    torch.cuda.synchronize()
+    _check_guards(ob, -7.0, "out")
+    _check_guards(sb, -9.0, "state_out")
+    assert torch.all(wb[:PAD] == 0xA5).item() and torch.all(wb[-PAD:] == 0xA5).item(), \
+        "workspace: a kernel wrote outside it"
+    ro, rs = oracle_full(inp)
+    assert_close_per_seq_head(to_f64(out), ro, to_f64(st), rs, inp.cu_seqlens, TOL[dtype])
+
+
+def test_guard_bands_decode_and_multi():
+    import torch
+    inp = make_inputs([1] * 7, 2, 4, dtype="bf16", seed=112, state_std=0.1)
+    t = device_tensors(inp)
+    ob, out = _guarded((inp.N, inp.Nv, 128), torch.bfloat16, -7.0)
+    sb, st = _guarded((inp.N, inp.Nv, 128, 128), torch.float32, -9.0)
+    gdr.recurrent_step(t["q"], t["k"], t["v"], t["g"], t["beta"], t["state_in"], state_out=st,
+                       out=out, scale=SCALE)
+    torch.cuda.synchronize()
+    _check_guards(ob, -7.0, "decode out")
+    _check_guards(sb, -9.0, "decode state_out")
+    ro, rs = oracle_full(inp)
+    assert_close_per_seq_head(to_f64(out), ro, to_f64(st), rs, inp.cu_seqlens, TOL["bf16"])
+
+    inp = make_inputs([3, 0, 16, 5], 2, 4, dtype="bf16", seed=113, state_std=0.1)
+    t = device_tensors(inp)
+    ob, out = _guarded((inp.T, inp.Nv, 128), torch.bfloat16, -7.0)
+    sb, st = _guarded((inp.N, inp.Nv, 128, 128), torch.float32, -9.0)
+    gdr.recurrent_multi(t["q"], t["k"], t["v"], t["g"], t["beta"], t["cu"], t["state_in"],
+                        out=out, state_out=st, scale=SCALE)
+    torch.cuda.synchronize()
+    _check_guards(ob, -7.0, "multi out")
+    _check_guards(sb, -9.0, "multi state_out")
+    ro, rs = oracle_full(inp)
+    assert_close_per_seq_head(to_f64(out), ro, to_f64(st), rs, inp.cu_seqlens, TOL["bf16"])

@@ -140,3 +140,15 @@ def test_without_normalisation_matches_prenormalised():
     assert pins._rel(o1, o2) < 1e-14 and pins._rel(s1, s2) < 1e-14
     o3, _ = oracle.recurrent(q, k, v, g, beta, s0, cu, 0.4, l2norm=False)
     assert pins._rel(o3, o1) > 1e-2
+
+
+def test_rel_l2_hand_values():
+    """The checker every parity test relies on, on values worked by hand:
+    |(1,2,2) - (1,2,4)| = 2 and |(1,2,4)| = sqrt(21); a zero reference gives
+    the absolute error; equal arrays give 0; the error is symmetric in sign."""
+    import math
+    assert oracle.rel_l2([1.0, 2.0, 2.0], [1.0, 2.0, 4.0]) == pytest.approx(2 / math.sqrt(21), rel=1e-15)
+    assert oracle.rel_l2([[3.0], [4.0]], [[0.0], [0.0]]) == pytest.approx(5.0, rel=1e-15)
+    assert oracle.rel_l2(np.ones((3, 4)), np.ones((3, 4))) == 0.0
+    assert oracle.rel_l2([0.0, 0.0], [3.0, 4.0]) == pytest.approx(1.0, rel=1e-15)
+    assert oracle.rel_l2([-1.0, 2.0], [1.0, 2.0]) == pytest.approx(2 / math.sqrt(5), rel=1e-15)
