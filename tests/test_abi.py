@@ -180,9 +180,12 @@ def test_timed_entry_points_validate_before_launching():
     kms = (ctypes.c_float * 4)()
     kind = (ctypes.c_int32 * 4)()
     n = ctypes.c_int32(0)
-    # fewer slots than launches (the table alone is one): rejected
-    assert lib.gdr_chunk_fwd_timed(*c, kms, kind, 0, ctypes.byref(n), None) == INVALID
+    # missing result arrays or a negative capacity: rejected (fewer slots than
+    # launches is allowed: only the span is then timed, a GPU test checks it)
     assert lib.gdr_chunk_fwd_timed(*c, None, kind, 4, ctypes.byref(n), None) == INVALID
+    assert lib.gdr_chunk_fwd_timed(*c, kms, None, 4, ctypes.byref(n), None) == INVALID
+    assert lib.gdr_chunk_fwd_timed(*c, kms, kind, -1, ctypes.byref(n), None) == INVALID
+    assert lib.gdr_chunk_fwd_timed(*c, kms, kind, 4, None, None) == INVALID
 
 
 def test_binding_fails_loudly_without_library(tmp_path):

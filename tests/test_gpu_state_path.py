@@ -324,3 +324,31 @@ def test_guard_bands_decode_and_multi():
     _check_guards(sb, -9.0, "multi state_out")
     ro, rs = oracle_full(inp)
     assert_close_per_seq_head(to_f64(out), ro, to_f64(st), rs, inp.cu_seqlens, TOL["bf16"])
+
+
+def test_timed_call_with_fewer_slots_than_launches_times_the_span():
+    """gdr_chunk_fwd_timed with room for fewer kernel times than launches still
+    computes the same result and reports only the span (n = 0)."""
+    import ctypes
+    import torch
+    inp = make_inputs([300, 1, 129], 2, 4, dtype="bf16", seed=114, state_std=0.1)
+    t = device_tensors(inp)
+    ref_o, ref_s = gdr.chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], t["cu"], t["state_in"],
+                                 scale=SCALE)
+    out, st = torch.empty_like(ref_o), torch.empty_like(ref_s)
+    need = gdr.workspace_size(inp.T, inp.N, inp.Nqk, inp.Nv, gdr.GDR_BF16)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda:0")
+    lib = gdr.load()
+    kms = (ctypes.c_float * 1)()
+    kind = (ctypes.c_int32 * 1)()
+    n = ctypes.c_int32(-1)
+    span = ctypes.c_float(0.0)
+    p = lambda x: x.data_ptr()
+    rc = lib.gdr_chunk_fwd_timed(p(t["q"]), p(t["k"]), p(t["v"]), p(t["g"]), p(t["beta"]),
+                                 p(t["state_in"]), p(t["cu"]), inp.N, inp.T, inp.Nqk, inp.Nv, 128,
+                                 gdr.GDR_BF16, SCALE, gdr.GDR_FLAG_QK_L2NORM, p(out), p(st), p(ws),
+                                 need, torch.cuda.current_stream().cuda_stream, kms, kind, 1,
+                                 ctypes.byref(n), ctypes.byref(span))
+    torch.cuda.synchronize()
+    assert rc == 0 and n.value == 0 and span.value > 0
+    assert torch.equal(out, ref_o) and torch.equal(st, ref_s)
