@@ -79,6 +79,11 @@ def load(path: str = LIB_PATH):
                                      i32, i32, ctypes.c_int, vp, vp, vp, vp, vp, vp,
                                      ctypes.POINTER(ctypes.c_float)]
     lib.gdr_conv_prefill.restype = ctypes.c_int
+    lib.gdr_chunk_fwd_no_alloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                           ctypes.c_int, f32, u32, vp, vp, vp]
+    lib.gdr_chunk_fwd_no_alloc.restype = ctypes.c_int
+    lib.gdr_chunk_fwd_no_alloc_scratch_bytes.argtypes = []
+    lib.gdr_chunk_fwd_no_alloc_scratch_bytes.restype = sz
     lib.gdr_status_string.argtypes = [ctypes.c_int]
     lib.gdr_status_string.restype = ctypes.c_char_p
     lib.gdr_version.argtypes = []
@@ -187,6 +192,40 @@ def chunk_fwd(q, k, v, g, beta, cu_seqlens, state_in=None, *, scale: Optional[fl
         raise GdrError(st, "gdr_chunk_fwd_timed")
     timings.extend((STAGE_NAMES.get(kind[i], str(kind[i])), float(ms[i])) for i in range(n.value))
     timings.append(("span", float(span.value)))
+    return out, state_out
+
+
+def chunk_fwd_no_alloc(q, k, v, g, beta, cu_seqlens, state_in, out, state_out, *,
+                       scale: Optional[float] = None, l2norm: bool = True):
+    """``gdr_chunk_fwd_no_alloc``: the chunkwise forward with the library's
+    fixed scratch as workspace.  The caller passes every buffer (``state_in``
+    and ``state_out`` may be None), so this function allocates nothing either.
+    Returns (out, state_out)."""
+    import torch
+    lib = load()
+    T, Nqk, _ = q.shape
+    Nv = v.shape[1]
+    N = cu_seqlens.shape[0] - 1
+    dev = q.device
+    dt = q.dtype
+    code = _dtype_code(q)
+    _check(q, "q", (T, Nqk, D), dt, dev)
+    _check(k, "k", (T, Nqk, D), dt, dev)
+    _check(v, "v", (T, Nv, D), dt, dev)
+    _check(g, "g", (T, Nv), torch.float32, dev)
+    _check(beta, "beta", (T, Nv), torch.float32, dev)
+    _check(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32, dev)
+    _check(state_in, "state_in", (N, Nv, D, D), torch.float32, dev)
+    _check(out, "out", (T, Nv, D), dt, dev)
+    _check(state_out, "state_out", (N, Nv, D, D), torch.float32, dev)
+    if scale is None:
+        scale = D ** -0.5
+    st = lib.gdr_chunk_fwd_no_alloc(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                    _ptr(state_in), _ptr(cu_seqlens), N, T, Nqk, Nv, D, code,
+                                    float(scale), GDR_FLAG_QK_L2NORM if l2norm else 0, _ptr(out),
+                                    _ptr(state_out), _stream())
+    if st != 0:
+        raise GdrError(st, "gdr_chunk_fwd_no_alloc")
     return out, state_out
 
 

@@ -3,6 +3,7 @@
 // on the caller's stream.  No allocation, no synchronisation.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
 #include <vector>
 
 #include "../../include/gdr.h"
@@ -67,7 +68,7 @@ int32_t launches_needed(const Workspace& w, int64_t N) {
 
 template <typename T>
 gdr_status run_chunk(const ChunkArgs& a, hipStream_t st, Recorder& rec) {
-  const Workspace w = plan_workspace(a.T, a.N, a.Nqk, a.Nv, a.dtype);
+  const Workspace w = plan_workspace(a.T, a.N, a.Nqk, a.Nv, a.dtype, a.budget);
   char* ws = static_cast<char*>(a.workspace);
   int4* table = reinterpret_cast<int4*>(ws + w.table);
   int32_t* choff = reinterpret_cast<int32_t*>(ws + w.choff);
@@ -172,6 +173,70 @@ extern "C" gdr_status gdr_chunk_fwd_timed(const void* q, const void* k, const vo
     *n = timed;
   }
   return s;
+}
+
+// ---------------------------------------------------------------------------
+// gdr_chunk_fwd_no_alloc: gdr_chunk_fwd with its workspace in a fixed
+// device-resident array instead of a caller buffer, for callers that cannot
+// allocate.  Each GPU the library runs on holds its own copy of the array
+// until the process ends.  Its address on a device is looked up once, with
+// that device current (hipGetSymbolAddress; the array's name in host code is
+// only a stand-in, never a device address), and kept per device.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr int64_t kScratchBytes = int64_t(64) << 20;
+constexpr int kMaxDevices = 64;
+
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex scratch_mu;
+void* scratch_dev[kMaxDevices] = {};
+
+gdr_status scratch_ptr(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return GDR_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return GDR_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_dev[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return GDR_ERR_HIP;
+    scratch_dev[dev] = p;
+  }
+  *out = scratch_dev[dev];
+  return GDR_OK;
+}
+
+}  // namespace
+
+extern "C" size_t gdr_chunk_fwd_no_alloc_scratch_bytes(void) {
+  return static_cast<size_t>(kScratchBytes);
+}
+
+extern "C" gdr_status gdr_chunk_fwd_no_alloc(const void* q, const void* k, const void* v,
+                                             const float* g, const float* beta,
+                                             const float* state_in, const int32_t* cu_seqlens,
+                                             int32_t N, int32_t T, int32_t Nqk, int32_t Nv,
+                                             int32_t D, gdr_dtype dtype, float scale,
+                                             uint32_t flags, void* out, float* state_out,
+                                             void* stream) {
+  // every check that needs no workspace first, then the sizes against the
+  // fixed scratch: a call that cannot fit is refused before any HIP call
+  const ChunkArgs pre{q, k, v, g, beta, state_in, cu_seqlens, N, T, Nqk, Nv, D, dtype, scale,
+                      flags, out, state_out, nullptr, 0, true, 0};
+  gdr_status s = validate_chunk(pre);
+  if (s != GDR_OK) return s;
+  if (plan_workspace(T, N, Nqk, Nv, dtype, kScratchBytes).total < 0)
+    return GDR_ERR_WORKSPACE_TOO_SMALL;
+  void* ws = nullptr;
+  const gdr_status p = scratch_ptr(&ws);
+  if (p != GDR_OK) return p;
+  ChunkArgs a{q, k, v, g, beta, state_in, cu_seqlens, N, T, Nqk, Nv, D, dtype, scale, flags,
+              out, state_out, ws, static_cast<size_t>(kScratchBytes), false, kScratchBytes};
+  s = validate_chunk(a);
+  if (s != GDR_OK) return s;
+  Recorder none;
+  return dispatch_chunk(a, static_cast<hipStream_t>(stream), none);
 }
 
 namespace {

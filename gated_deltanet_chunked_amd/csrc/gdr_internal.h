@@ -57,7 +57,11 @@ struct Workspace {
   int64_t seg_slots;
 };
 
-Workspace plan_workspace(int64_t T, int64_t N, int64_t Nqk, int64_t Nv, gdr_dtype dtype);
+// Layout of the workspace.  budget = 0: segments of about 128 MiB of matrices
+// (segment_slots).  budget > 0: the largest even split whose whole layout
+// fits in `budget` bytes; total = -1 when not even one chunk slot fits.
+Workspace plan_workspace(int64_t T, int64_t N, int64_t Nqk, int64_t Nv, gdr_dtype dtype,
+                         int64_t budget = 0);
 
 struct ChunkArgs {
   const void* q; const void* k; const void* v;
@@ -70,6 +74,7 @@ struct ChunkArgs {
   void* out; float* state_out;
   void* workspace; size_t workspace_bytes;
   bool no_workspace;   // gdr_recurrent_multi: the same arguments, no workspace
+  int64_t budget;      // > 0: the workspace is a fixed buffer of this many bytes (plan_workspace)
 };
 
 struct StepArgs {

@@ -30,16 +30,34 @@ gdr_status common_sizes(int32_t Nqk, int32_t Nv, int32_t D, gdr_dtype dtype, uin
 
 }  // namespace
 
-Workspace plan_workspace(int64_t T, int64_t N, int64_t Nqk, int64_t Nv, gdr_dtype dtype) {
+Workspace plan_workspace(int64_t T, int64_t N, int64_t Nqk, int64_t Nv, gdr_dtype dtype,
+                         int64_t budget) {
   Workspace w{};
+  const int64_t es = static_cast<int64_t>(dtype_size(dtype));
+  const int64_t per_slot = Nv * kInterMats * kMatElems * es;
   w.nslots = max_slots(T, N);
-  w.seg_slots = segment_slots(w.nslots, Nv, static_cast<int64_t>(dtype_size(dtype)));
+  // everything but the segment's matrices
+  const int64_t fixed = align256(w.nslots * 4 * 4) + align256((N + 1) * 4) +
+                        align256(w.nslots * Nv * 4) + align256(N * Nv * kMatElems * 4) + 256;
+  if (budget > 0) {
+    // the largest segment that fits the budget, then the slots split evenly
+    int64_t cap = (budget - fixed) / per_slot;
+    if (cap > kMaxSegSlots) cap = kMaxSegSlots;
+    if (cap < 1) {
+      w.total = -1;   // does not fit
+      return w;
+    }
+    const int64_t nsegs = (w.nslots + cap - 1) / cap;
+    w.seg_slots = (w.nslots + nsegs - 1) / nsegs;
+  } else {
+    w.seg_slots = segment_slots(w.nslots, Nv, es);
+  }
   int64_t off = 0;
   w.table = off; off = align256(off + w.nslots * 4 * 4);
   w.choff = off; off = align256(off + (N + 1) * 4);
   w.gam = off; off = align256(off + w.nslots * Nv * 4);
   w.inter = off;
-  off = align256(off + w.seg_slots * Nv * kInterMats * kMatElems * static_cast<int64_t>(dtype_size(dtype)));
+  off = align256(off + w.seg_slots * per_slot);
   w.carry = off; off = align256(off + N * Nv * kMatElems * 4);
   w.discard = off; off = align256(off + 256);
   w.total = off;
@@ -62,8 +80,9 @@ gdr_status validate_chunk(const ChunkArgs& a) {
     if (p && !aligned16(p)) return GDR_ERR_INVALID_ARGUMENT;
   if (!a.no_workspace) {
     if ((reinterpret_cast<uintptr_t>(a.workspace) & 255u) != 0) return GDR_ERR_INVALID_ARGUMENT;
-    const Workspace w = plan_workspace(a.T, a.N, a.Nqk, a.Nv, a.dtype);
-    if (a.workspace_bytes < static_cast<size_t>(w.total)) return GDR_ERR_WORKSPACE_TOO_SMALL;
+    const Workspace w = plan_workspace(a.T, a.N, a.Nqk, a.Nv, a.dtype, a.budget);
+    if (w.total < 0 || a.workspace_bytes < static_cast<size_t>(w.total))
+      return GDR_ERR_WORKSPACE_TOO_SMALL;
   }
 
   const int64_t es = static_cast<int64_t>(dtype_size(a.dtype));

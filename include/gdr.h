@@ -133,6 +133,34 @@ gdr_status gdr_recurrent_step(const void* q, const void* k, const void* v,
                               void* out, void* stream);
 
 /*
+ * gdr_chunk_fwd without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The same computation, arguments and
+ * results as gdr_chunk_fwd, except that the scratch lives in a fixed array of
+ * gdr_chunk_fwd_no_alloc_scratch_bytes() bytes (64 MiB) inside the library:
+ * every GPU the library runs on holds one copy of it until the process ends,
+ * located on the first call made with that device current.  The call
+ * allocates nothing; it only enqueues kernels on `stream`.
+ *
+ * Sizes whose scratch does not fit return GDR_ERR_WORKSPACE_TOO_SMALL before
+ * any HIP call.  The fit depends on N * Nv (a 64 KiB carried state per
+ * sequence and head when state_out is NULL) and on Nv (one chunk of
+ * intra-chunk matrices per head); long sequences are split into more
+ * segments, never refused.  All calls on one GPU share its array, so calls
+ * that may overlap on one GPU (different streams, threads) race: serialise
+ * them.  No part of the array needs to start at zero.
+ */
+gdr_status gdr_chunk_fwd_no_alloc(const void* q, const void* k, const void* v,
+                                  const float* g, const float* beta,
+                                  const float* state_in, const int32_t* cu_seqlens,
+                                  int32_t N, int32_t T, int32_t Nqk, int32_t Nv, int32_t D,
+                                  gdr_dtype dtype, float scale, uint32_t flags,
+                                  void* out, float* state_out, void* stream);
+
+/* Size in bytes of the fixed scratch array gdr_chunk_fwd_no_alloc uses. */
+size_t gdr_chunk_fwd_no_alloc_scratch_bytes(void);
+
+/*
  * Profiling variant of gdr_chunk_fwd: the same computation, plus the GPU time
  * of every kernel it launches.  Each launch gets a pair of HIP events that the
  * runtime records at that kernel's start and end (hipExtLaunchKernelGGL), so
