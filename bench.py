@@ -1,26 +1,33 @@
 """Throughput of libgdr on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill|long|varlen]
-                    [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long|prefill|varlen]
+                    [--no-cpu-baseline] [--chunk-only]
 
 One step is one pass of the whole hot path on synthetic, seeded inputs that
 are resident in HBM before the timed region starts:
-  * gdr_chunk_fwd on the prefill workload (default: B=1, T=4096, Nqk=16,
-    Nv=32, D=128, bf16 q/k/v, fp32 gates and states), and
+  * gdr_chunk_fwd on the chunk workload (default ``long``: B=1, T=32768,
+    Nqk=16, Nv=32, D=128, bf16 q/k/v, fp32 gates and states, the largest
+    single-GPU workload), and
   * gdr_recurrent_step on the decode workload (256 sequences x 1 token, same
     heads, fp32 states updated in place).
 ``value`` is the chunkwise forward's tokens/s from its GPU time: the span from
 its first kernel's start to its last kernel's end, taken from HIP events that
 the runtime records at each kernel's start and end inside the timed region.
 The same events give every kernel's own duration (the figure rocprofv3's
-kernel trace reports), from which the decode step's GB/s and the rooflines
-are computed.  ``ms_per_step`` is the host wall clock of a whole step.  After
-the timed steps the decode step is also measured with its state stored in
-bf16 (``gdr_recurrent_step_bf16_state``, half the state bytes), reported as
-``decode_bf16_state``, ``gdr_recurrent_multi`` on 256 sequences x 4 tokens
-as ``multi_token``, and the decode step with its conv update and gates fused
-in front as ``decode_conv``, and the conv/gate prologue of the chunked path on
-the prefill workload as ``conv_prefill``; none of them is part of the step.  One JSON line is printed.
+kernel trace reports), from which the rooflines are computed: ``roofline`` is
+the chunk path's dominant kernel against the bf16 matrix-core peak,
+``roofline_decode`` the decode step against HBM bandwidth.  ``ms_per_step``
+is the host wall clock of a whole step.
+
+After the timed steps, outside the step: the prefill workload (T=4096) is
+timed the same way beside the chunk workload (``chunk_fwd_prefill``); both
+are also timed cold (``cold``), with a 512 MiB buffer written between calls
+so that no input is left in the 256 MB Infinity Cache.  Unless
+``--chunk-only``: the decode step with its state stored in bf16
+(``decode_bf16_state``), ``gdr_recurrent_multi`` on 256 sequences x 4
+tokens (``multi_token``), the decode step with its conv update and gates
+fused in front (``decode_conv``) and the conv/gate prologue of the chunked
+path on the chunk workload (``conv_prefill``).  One JSON line is printed.
 """
 from __future__ import annotations
 
@@ -112,13 +119,89 @@ def measured_traffic(kernel: str):
         return None
 
 
+class ChunkLeg:
+    """One chunk workload resident on the device, with its outputs and
+    workspace, called through the timed entry point."""
+
+    def __init__(self, gdr, inp, dev, scale):
+        import torch
+        self.gdr, self.inp, self.scale = gdr, inp, scale
+        dt = torch.bfloat16 if inp.dtype == "bf16" else torch.float32
+        self.t = dict(q=torch.from_numpy(inp.q).to(dev, dt), k=torch.from_numpy(inp.k).to(dev, dt),
+                      v=torch.from_numpy(inp.v).to(dev, dt), g=torch.from_numpy(inp.g).to(dev),
+                      beta=torch.from_numpy(inp.beta).to(dev),
+                      cu=torch.from_numpy(inp.cu_seqlens).to(dev),
+                      s0=torch.from_numpy(inp.state_in).to(dev))
+        self.out = torch.empty((inp.T, inp.Nv, D), dtype=dt, device=dev)
+        self.sout = torch.empty_like(self.t["s0"])
+        code = gdr.GDR_BF16 if inp.dtype == "bf16" else gdr.GDR_F32
+        self.ws = torch.empty(gdr.workspace_size(inp.T, inp.N, inp.Nqk, inp.Nv, code),
+                              dtype=torch.uint8, device=dev)
+
+    def __call__(self, timings=None):
+        t = self.t
+        self.gdr.chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], t["cu"], t["s0"],
+                           scale=self.scale, out=self.out, state_out=self.sout, workspace=self.ws,
+                           timings=timings)
+
+    def flops(self):
+        return alg_flops_chunk(np.diff(self.inp.cu_seqlens).tolist(), self.inp.Nqk, self.inp.Nv)
+
+    def summarise(self, tims, steps):
+        """Span and per-kernel figures from the timed calls' event records."""
+        spans = [ms for tim in tims for n, ms in tim if n == "span"]
+        per_kernel = {}
+        for tim in tims:
+            for n, ms in tim:
+                if n != "span":
+                    per_kernel.setdefault(n, []).append(ms)
+        f_intra, f_inter = self.flops()
+        span_s = float(np.mean(spans)) * 1e-3
+        kst = {}
+        for n, lst in per_kernel.items():
+            per_call = len(lst) / steps
+            avg = float(np.mean(lst))
+            f = {"intra": f_intra, "inter": f_inter}.get(n)
+            kst[n] = {"avg_ms": round(avg, 4), "launches_per_call": per_call,
+                      "alg_tflops": round(f / (avg * per_call * 1e-3) / 1e12, 2) if f else None}
+        f_tot = f_intra + f_inter
+        return {"workload": self.inp.name, "tokens": self.inp.T, "sequences": self.inp.N,
+                "gpu_ms": round(span_s * 1e3, 4), "tokens_per_s": round(self.inp.T / span_s, 1),
+                "alg_gflop": round(f_tot / 1e9, 3),
+                "alg_tflops": round(f_tot / span_s / 1e12, 2),
+                "frac_bf16_mfma_peak": round(f_tot / span_s / 1e12 / MFMA_PEAK_TFLOPS["bf16"], 4),
+                "kernel_sum_ms": round(sum(v["avg_ms"] * v["launches_per_call"] for v in kst.values()), 4),
+                "kernels": kst}
+
+
+def time_chunk(leg, steps, warmup, flush=None):
+    """`steps` timed calls after `warmup` untimed ones; with `flush` (a 512 MiB
+    device buffer) the buffer is rewritten before every call, so the call
+    starts with no input left in the Infinity Cache (cold)."""
+    import torch
+    for _ in range(warmup):
+        leg()
+    torch.cuda.synchronize()
+    tims = []
+    for _ in range(steps):
+        if flush is not None:
+            flush.add_(1.0)
+        tim = []
+        leg(tim)
+        tims.append(tim)
+    torch.cuda.synchronize()
+    return leg.summarise(tims, steps)
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", choices=["prefill", "long", "varlen"], default="prefill")
+    ap.add_argument("--workload", choices=["prefill", "long", "varlen"], default="long")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--chunk-only", action="store_true",
+                    help="time the step and the chunk figures only (for profiling runs)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="before the steps, copy a buffer of this many MiB device to device once; "
                          "a profiler's byte counters on that plain copy calibrate the ones on the "
@@ -144,26 +227,15 @@ def main() -> int:
     cfg = {"prefill": 1, "varlen": 2, "long": 3}[args.workload]
     pre = config_inputs(cfg)
     dec = config_inputs(4)
-
-    def to_dev(inp):
-        dt = torch.bfloat16 if inp.dtype == "bf16" else torch.float32
-        return dict(q=torch.from_numpy(inp.q).to(dev, dt), k=torch.from_numpy(inp.k).to(dev, dt),
-                    v=torch.from_numpy(inp.v).to(dev, dt), g=torch.from_numpy(inp.g).to(dev),
-                    beta=torch.from_numpy(inp.beta).to(dev),
-                    cu=torch.from_numpy(inp.cu_seqlens).to(dev),
-                    s0=torch.from_numpy(inp.state_in).to(dev))
-
-    P, Dd = to_dev(pre), to_dev(dec)
+    leg = ChunkLeg(gdr, pre, dev, scale)
     T, N, Nqk, Nv = pre.T, pre.N, pre.Nqk, pre.Nv
-    out = torch.empty((T, Nv, D), dtype=P["q"].dtype, device=dev)
-    sout = torch.empty_like(P["s0"])
-    ws = torch.empty(gdr.workspace_size(T, N, Nqk, Nv, gdr.GDR_BF16), dtype=torch.uint8, device=dev)
+
+    Dd = ChunkLeg(gdr, dec, dev, scale).t     # the decode step's inputs on the device
     dstate = Dd["s0"].clone()
     dout = torch.empty((dec.N, dec.Nv, D), dtype=Dd["q"].dtype, device=dev)
 
     def step(timings):
-        gdr.chunk_fwd(P["q"], P["k"], P["v"], P["g"], P["beta"], P["cu"], P["s0"], scale=scale,
-                      out=out, state_out=sout, workspace=ws, timings=timings)
+        leg(timings)
         gdr.recurrent_step(Dd["q"], Dd["k"], Dd["v"], Dd["g"], Dd["beta"], dstate,
                            state_out=dstate, out=dout, scale=scale, timings=timings)
     if args.copy_probe_mib > 0:
@@ -181,59 +253,94 @@ def main() -> int:
         step([])
     torch.cuda.synchronize()
 
-    chunk_ms, dec_ms = [], []
-    per_kernel = {}
+    chunk_tims, dec_ms = [], []
     t0 = time.perf_counter()
     for _ in range(args.steps):
         tim = []
         step(tim)
-        for name, ms in tim:
-            if name == "span":
-                chunk_ms.append(ms)
-            elif name == "decode":
-                dec_ms.append(ms)
-            else:
-                per_kernel.setdefault(name, []).append(ms)
+        dec_ms.extend(ms for n, ms in tim if n == "decode")
+        chunk_tims.append([(n, ms) for n, ms in tim if n != "decode"])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    # ---- prefill figures
-    lengths = np.diff(pre.cu_seqlens).tolist()
-    f_intra, f_inter = alg_flops_chunk(lengths, Nqk, Nv)
-    f_total = f_intra + f_inter
-    chunk_s = float(np.mean(chunk_ms)) * 1e-3
-    tok_s = T / chunk_s
-    # average duration of one launch of each kernel, and launches per call
-    kstats = {}
-    for name, lst in per_kernel.items():
-        kstats[name] = dict(avg_ms=float(np.mean(lst)), launches_per_call=len(lst) / args.steps)
-    # ---- decode figures
+    chunk = leg.summarise(chunk_tims, args.steps)
+    tok_s = chunk["tokens_per_s"]
     dec_s = float(np.mean(dec_ms)) * 1e-3
     dec_bytes = alg_bytes_decode(dec.N, dec.Nqk, dec.Nv)
     dec_gbps = dec_bytes / dec_s / 1e9
-
-    # the dominant kernel: the one with the most GPU time per step
-    per_step = {name: s["avg_ms"] * s["launches_per_call"] for name, s in kstats.items()}
-    per_step["decode"] = dec_s * 1e3
-    dom = max(per_step, key=per_step.get)
-    if dom == "decode":
-        roof = dict(kernel="decode", bound="hbm", achieved=round(dec_gbps, 1), peak=HBM_PEAK_GBPS,
+    roof_dec = dict(kernel="decode", bound="hbm", achieved=round(dec_gbps, 1), peak=HBM_PEAK_GBPS,
                     unit="GB/s", frac=round(dec_gbps / HBM_PEAK_GBPS, 4),
                     traffic=measured_traffic("decode"),
                     per_launch=f"{dec_bytes} algorithmic bytes")
-    else:
-        f_dom = {"intra": f_intra, "inter": f_inter}.get(dom, 0.0)
-        launches = per_kernel[dom]
-        per_launch_flops = f_dom / kstats[dom]["launches_per_call"]
-        ach = per_launch_flops / (kstats[dom]["avg_ms"] * 1e-3) / 1e12
-        roof = dict(kernel=dom, bound="mfma", achieved=round(ach, 2), peak=MFMA_PEAK_TFLOPS["bf16"],
-                    unit="TFLOP/s", frac=round(ach / MFMA_PEAK_TFLOPS["bf16"], 4),
-                    traffic=measured_traffic(dom) if args.workload == "prefill" else None,
-                    per_launch=f"{per_launch_flops:.4g} algorithmic FLOP")
-        del launches
 
-    # ---- decode with the state stored in bf16 (a bf16 state cache): measured
-    # after the timed steps, on the same decode inputs, and reported beside them
+    # the chunk path's dominant kernel: the most GPU time per call
+    f_intra, f_inter = leg.flops()
+    kst = chunk["kernels"]
+    dom = max((k for k in kst if k in ("intra", "inter")),
+              key=lambda k: kst[k]["avg_ms"] * kst[k]["launches_per_call"])
+    per_launch_flops = {"intra": f_intra, "inter": f_inter}[dom] / kst[dom]["launches_per_call"]
+    ach = per_launch_flops / (kst[dom]["avg_ms"] * 1e-3) / 1e12
+    roof = dict(kernel=dom, bound="mfma", achieved=round(ach, 2), peak=MFMA_PEAK_TFLOPS["bf16"],
+                unit="TFLOP/s", frac=round(ach / MFMA_PEAK_TFLOPS["bf16"], 4),
+                traffic=measured_traffic(f"{dom}_{args.workload}"),
+                per_launch=f"{per_launch_flops:.6g} algorithmic FLOP per launch, "
+                           f"{kst[dom]['launches_per_call']:g} launches per call")
+
+    res = {
+        "metric": "chunk GDR fwd tokens/s + % MFMA peak; decode-step GB/s (% HBM peak)",
+        "value": round(tok_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; distributions of the Qwen3-Next gate initialisation)",
+        "config": {"workload": CONFIG_NAMES[cfg] + " + " + CONFIG_NAMES[4],
+                   "tokens": T, "sequences": N, "Nqk": Nqk, "Nv": Nv, "D": D, "chunk": L,
+                   "decode_sequences": dec.N},
+        "chunk_fwd": chunk,
+        "decode": {"gpu_ms": round(dec_s * 1e3, 4), "gbps": round(dec_gbps, 1),
+                   "frac_hbm_peak": round(dec_gbps / HBM_PEAK_GBPS, 4),
+                   "tokens_per_s": round(dec.N / dec_s, 1), "alg_bytes": dec_bytes},
+        "roofline": roof,
+        "roofline_decode": roof_dec,
+    }
+
+    # ---- beside the step: the prefill workload, and cold (Infinity Cache
+    # flushed) figures of both chunk workloads
+    flush = torch.zeros(1 << 27, dtype=torch.float32, device=dev)   # 512 MiB
+    if cfg != 1:
+        leg1 = ChunkLeg(gdr, config_inputs(1), dev, scale)
+        res["chunk_fwd_prefill"] = time_chunk(leg1, args.steps, args.warmup)
+    else:
+        leg1 = leg
+    cold = {"what": "512 MiB buffer written before every call; same calls otherwise"}
+    cold[args.workload] = time_chunk(leg, args.steps, 1, flush)
+    if cfg != 1:
+        cold["prefill"] = time_chunk(leg1, args.steps, 1, flush)
+    res["cold"] = cold
+    del flush, leg1
+
+    if not args.chunk_only:
+        res.update(extras(gdr, dec, Dd, dout, pre, cfg, args, dev, scale))
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(pre, scale)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+def extras(gdr, dec, Dd, dout, pre, cfg, args, dev, scale):
+    """The decode variants and the prefill prologue, measured after the timed
+    steps and reported beside them (not part of the step)."""
+    import torch
+    res = {}
+    T, N, Nqk, Nv = pre.T, pre.N, pre.Nqk, pre.Nv
+
+    # decode with the state stored in bf16 (a bf16 state cache)
     bstate = Dd["s0"].to(torch.bfloat16)
     for _ in range(args.warmup):
         gdr.recurrent_step(Dd["q"], Dd["k"], Dd["v"], Dd["g"], Dd["beta"], bstate,
@@ -246,13 +353,16 @@ def main() -> int:
     bdec_s = float(np.mean([ms for _, ms in btim])) * 1e-3
     bdec_bytes = alg_bytes_decode(dec.N, dec.Nqk, dec.Nv, state_es=2)
     bdec_gbps = bdec_bytes / bdec_s / 1e9
+    res["decode_bf16_state"] = {"gpu_ms": round(bdec_s * 1e3, 4), "gbps": round(bdec_gbps, 1),
+                                "frac_hbm_peak": round(bdec_gbps / HBM_PEAK_GBPS, 4),
+                                "tokens_per_s": round(dec.N / bdec_s, 1), "alg_bytes": bdec_bytes}
+    del bstate
 
-    # ---- several tokens per sequence (gdr_recurrent_multi): 256 sequences x 4
-    # tokens, the decode heads, fp32 states updated in place; measured after
-    # the timed steps and reported beside them
+    # several tokens per sequence (gdr_recurrent_multi): 256 sequences x 4
+    # tokens, the decode heads, fp32 states updated in place
     from gated_deltanet_chunked_amd.inputs import make_inputs
     mt = make_inputs([MULTI_TOKENS] * dec.N, dec.Nqk, dec.Nv, seed=4, state_std=0.01)
-    M = to_dev(mt)
+    M = ChunkLeg(gdr, mt, dev, scale).t
     mout = torch.empty((mt.T, mt.Nv, D), dtype=M["q"].dtype, device=dev)
     for _ in range(args.warmup):
         gdr.recurrent_multi(M["q"], M["k"], M["v"], M["g"], M["beta"], M["cu"], M["s0"],
@@ -265,10 +375,15 @@ def main() -> int:
     multi_s = float(np.mean([ms for _, ms in mtim])) * 1e-3
     multi_bytes = alg_bytes_multi(mt.N, MULTI_TOKENS, mt.Nqk, mt.Nv)
     multi_gbps = multi_bytes / multi_s / 1e9
+    res["multi_token"] = {"workload": f"{mt.N} sequences x {MULTI_TOKENS} tokens, Nqk={mt.Nqk} "
+                                      f"Nv={mt.Nv} bf16, fp32 states in place",
+                          "gpu_ms": round(multi_s * 1e3, 4), "gbps": round(multi_gbps, 1),
+                          "frac_hbm_peak": round(multi_gbps / HBM_PEAK_GBPS, 4),
+                          "tokens_per_s": round(mt.T / multi_s, 1), "alg_bytes": multi_bytes}
+    del M, mout
 
-    # ---- decode with the conv update and gates fused in front
-    # (gdr_recurrent_step_conv): the decode heads, 256 sequences, bf16
-    # activations, fp32 states in place; measured after the timed steps
+    # decode with the conv update and gates fused in front
+    # (gdr_recurrent_step_conv): 256 sequences, bf16 activations, fp32 states
     from gated_deltanet_chunked_amd.inputs import prologue_inputs
     pi = prologue_inputs(dec.N, dec.Nqk, dec.Nv, seed=4)
     cv = {k_: torch.from_numpy(getattr(pi, k_)).to(dev, torch.bfloat16)
@@ -291,10 +406,16 @@ def main() -> int:
     conv_s = float(np.mean([ms for _, ms in ctim])) * 1e-3
     conv_bytes = alg_bytes_decode_conv(dec.N, dec.Nqk, dec.Nv)
     conv_gbps = conv_bytes / conv_s / 1e9
+    res["decode_conv"] = {"workload": f"{dec.N} sequences x 1 token, Nqk={dec.Nqk} Nv={dec.Nv} "
+                                      "bf16, conv update (kernel 4) and gates fused in front, "
+                                      "fp32 states",
+                          "gpu_ms": round(conv_s * 1e3, 4), "gbps": round(conv_gbps, 1),
+                          "frac_hbm_peak": round(conv_gbps / HBM_PEAK_GBPS, 4),
+                          "tokens_per_s": round(dec.N / conv_s, 1), "alg_bytes": conv_bytes}
+    del cv, cf, cs_a, cs_b
 
-    # ---- the conv/gate prologue of the chunked path (gdr_conv_prefill) at the
-    # prefill shape: cached windows in, new windows out; measured after the
-    # timed steps
+    # the conv/gate prologue of the chunked path (gdr_conv_prefill) on the
+    # chunk workload's tokens: cached windows in, new windows out
     from gated_deltanet_chunked_amd.inputs import prefill_prologue_inputs
     pp = prefill_prologue_inputs(np.diff(pre.cu_seqlens).tolist(), Nqk, Nv, seed=cfg)
     px = torch.from_numpy(pp.mixed_qkv).to(dev, torch.bfloat16)
@@ -314,64 +435,12 @@ def main() -> int:
     cp_s = float(np.mean([ms for _, ms in ptim])) * 1e-3
     cp_bytes = alg_bytes_conv_prefill(T, N, Nqk, Nv)
     cp_gbps = cp_bytes / cp_s / 1e9
-
-    res = {
-        "metric": "chunk GDR fwd tokens/s + % MFMA peak; decode-step GB/s (% HBM peak)",
-        "value": round(tok_s, 1),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(wall / args.steps * 1e3, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded; distributions of the Qwen3-Next gate initialisation)",
-        "config": {"workload": CONFIG_NAMES[cfg] + " + " + CONFIG_NAMES[4],
-                   "tokens": T, "sequences": N, "Nqk": Nqk, "Nv": Nv, "D": D, "chunk": L,
-                   "decode_sequences": dec.N},
-        "chunk_fwd": {"gpu_ms": round(chunk_s * 1e3, 4), "tokens_per_s": round(tok_s, 1),
-                      "alg_tflops": round(f_total / chunk_s / 1e12, 2),
-                      "frac_bf16_mfma_peak": round(f_total / chunk_s / 1e12 / MFMA_PEAK_TFLOPS["bf16"], 4),
-                      "alg_gflop": round(f_total / 1e9, 3),
-                      "kernel_sum_ms": round(sum(v["avg_ms"] * v["launches_per_call"]
-                                                 for v in kstats.values()), 4),
-                      "kernels": {k: {"avg_ms": round(v["avg_ms"], 4),
-                                      "launches_per_call": v["launches_per_call"],
-                                      "alg_tflops": (round({"intra": f_intra, "inter": f_inter}[k]
-                                                           / (v["avg_ms"] * v["launches_per_call"] * 1e-3)
-                                                           / 1e12, 2)
-                                                     if k in ("intra", "inter") else None)}
-                                  for k, v in kstats.items()}},
-        "decode": {"gpu_ms": round(dec_s * 1e3, 4), "gbps": round(dec_gbps, 1),
-                   "frac_hbm_peak": round(dec_gbps / HBM_PEAK_GBPS, 4),
-                   "tokens_per_s": round(dec.N / dec_s, 1), "alg_bytes": dec_bytes},
-        "decode_bf16_state": {"gpu_ms": round(bdec_s * 1e3, 4), "gbps": round(bdec_gbps, 1),
-                              "frac_hbm_peak": round(bdec_gbps / HBM_PEAK_GBPS, 4),
-                              "tokens_per_s": round(dec.N / bdec_s, 1), "alg_bytes": bdec_bytes},
-        "multi_token": {"workload": f"{mt.N} sequences x {MULTI_TOKENS} tokens, Nqk={mt.Nqk} "
-                                    f"Nv={mt.Nv} bf16, fp32 states in place",
-                        "gpu_ms": round(multi_s * 1e3, 4), "gbps": round(multi_gbps, 1),
-                        "frac_hbm_peak": round(multi_gbps / HBM_PEAK_GBPS, 4),
-                        "tokens_per_s": round(mt.T / multi_s, 1), "alg_bytes": multi_bytes},
-        "decode_conv": {"workload": f"{dec.N} sequences x 1 token, Nqk={dec.Nqk} Nv={dec.Nv} bf16, "
-                                    "conv update (kernel 4) and gates fused in front, fp32 states",
-                        "gpu_ms": round(conv_s * 1e3, 4), "gbps": round(conv_gbps, 1),
-                        "frac_hbm_peak": round(conv_gbps / HBM_PEAK_GBPS, 4),
-                        "tokens_per_s": round(dec.N / conv_s, 1), "alg_bytes": conv_bytes},
-        "conv_prefill": {"workload": f"{T} tokens in {N} sequences, Nqk={Nqk} Nv={Nv} bf16, "
-                                     "conv kernel 4, cached windows in and out",
-                         "gpu_ms": round(cp_s * 1e3, 4), "gbps": round(cp_gbps, 1),
-                         "frac_hbm_peak": round(cp_gbps / HBM_PEAK_GBPS, 4),
-                         "tokens_per_s": round(T / cp_s, 1), "alg_bytes": cp_bytes},
-        "roofline": roof,
-    }
-
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(pre, scale)
-    print(json.dumps(res), flush=True)
-    return 0
+    res["conv_prefill"] = {"workload": f"{T} tokens in {N} sequences, Nqk={Nqk} Nv={Nv} bf16, "
+                                       "conv kernel 4, cached windows in and out",
+                           "gpu_ms": round(cp_s * 1e3, 4), "gbps": round(cp_gbps, 1),
+                           "frac_hbm_peak": round(cp_gbps / HBM_PEAK_GBPS, 4),
+                           "tokens_per_s": round(T / cp_s, 1), "alg_bytes": cp_bytes}
+    return res
 
 
 def cpu_baseline(pre, scale):

@@ -801,9 +801,15 @@ hipError_t launch_intra(const T* q, const T* k, const T* v, const float* g, cons
                         Chunks chunks, int32_t Nqk, int32_t Nv, int32_t slot0, int32_t nseg,
                         float scale, int norm, T* inter, float* gam, hipStream_t stream,
                         LaunchEvents ev) {
-  hipExtLaunchKernelGGL(intra_kernel<T>, dim3(nseg, Nv), dim3(256), 0, stream, ev.start, ev.stop, 0,
-                        q, k, v, g, beta, chunks, Nqk, Nv, slot0, scale, norm, inter, gam);
-  return hipGetLastError();
+  if constexpr (sizeof(T) == 2) {
+    // bf16 inputs have their own kernel (gdr_intra_bf16.hip)
+    return launch_intra_bf16(q, k, v, g, beta, chunks, Nqk, Nv, slot0, nseg, scale, norm, inter,
+                             gam, stream, ev);
+  } else {
+    hipExtLaunchKernelGGL(intra_kernel<T>, dim3(nseg, Nv), dim3(256), 0, stream, ev.start, ev.stop,
+                          0, q, k, v, g, beta, chunks, Nqk, Nv, slot0, scale, norm, inter, gam);
+    return hipGetLastError();
+  }
 }
 
 template hipError_t launch_intra<float>(const float*, const float*, const float*, const float*,

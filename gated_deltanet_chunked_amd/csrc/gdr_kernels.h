@@ -67,6 +67,12 @@ hipError_t launch_intra(const Tin* q, const Tin* k, const Tin* v, const float* g
                         float scale, int norm, Tin* inter, float* gam, hipStream_t stream,
                         LaunchEvents ev = {});
 
+// The bf16 kernel behind launch_intra<__bf16> (gdr_intra_bf16.hip).
+hipError_t launch_intra_bf16(const __bf16* q, const __bf16* k, const __bf16* v, const float* g,
+                             const float* beta, Chunks chunks, int32_t Nqk, int32_t Nv,
+                             int32_t slot0, int32_t nseg, float scale, int norm, __bf16* inter,
+                             float* gam, hipStream_t stream, LaunchEvents ev = {});
+
 // Chunk-serial state pass over chunk slots [slot0, slot0 + nseg).  `discard` is
 // 256 bytes of scratch that absorbs the stores of rows past a chunk's end.
 template <typename Tin>
