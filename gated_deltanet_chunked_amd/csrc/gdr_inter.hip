@@ -319,10 +319,16 @@ void launch_inter(const T* inter, Chunks chunks, const float* gam, const float* 
                   float* carry, float* state_out, int32_t N, int32_t Nv, int32_t slot0,
                   int32_t nseg, bool first_segment, T* out, T* discard, hipStream_t stream,
                   LaunchEvents ev) {
-  const unsigned blocks = (unsigned)N * (unsigned)Nv * (unsigned)(kD / kBV);
-  hipExtLaunchKernelGGL(inter_kernel<T>, dim3(blocks), dim3(256), 0, stream, ev.start, ev.stop, 0,
-                        inter, chunks, gam, state_in, carry, state_out, N, Nv, slot0, nseg,
-                        first_segment ? 1 : 0, out, discard);
+  if constexpr (sizeof(T) == 2) {
+    // bf16 has its own kernel (gdr_inter_bf16.hip)
+    launch_inter_bf16(inter, chunks, gam, state_in, carry, state_out, N, Nv, slot0, nseg,
+                      first_segment, out, discard, stream, ev);
+  } else {
+    const unsigned blocks = (unsigned)N * (unsigned)Nv * (unsigned)(kD / kBV);
+    hipExtLaunchKernelGGL(inter_kernel<T>, dim3(blocks), dim3(256), 0, stream, ev.start, ev.stop,
+                          0, inter, chunks, gam, state_in, carry, state_out, N, Nv, slot0, nseg,
+                          first_segment ? 1 : 0, out, discard);
+  }
 }
 
 template void launch_inter<float>(const float*, Chunks, const float*, const float*, float*, float*,

@@ -1,0 +1,312 @@
+// gdr_inter_bf16.hip -- the chunk-serial half of the chunkwise gated delta
+// rule for bf16 inputs.
+//
+// The same pass as the fp32 kernel in gdr_inter.hip (Qwen3-Next blog post,
+// section 5(1)f, in the affine form prepared by the intra-chunk kernel): for
+// each chunk of a sequence, in order,
+//   O      = Qp S^T + Ou                        (the chunk's output rows)
+//   S_next = exp(gc_last) S + S M' + Bm         (the state after the chunk)
+// with S in R^{Dv x Dk}; a workgroup owns BV = 32 rows of S of one (sequence,
+// value head), four workgroups per (sequence, head) on one XCD.
+//
+// What bounds a chunk step is the compute unit's vector-memory path: per
+// chunk a workgroup needs about 80 KB of operands (all of Mt and Qp, its
+// slices of Bm and Ou).  A wave issues its instructions in order, so a wave
+// that issues loads stalls while the path is busy.  Here the waves on the
+// serial chain never issue one:
+//   waves 0, 1 (state):   (S M')^T for 64 key rows each, and the update of S
+//                         they keep in fp32 registers; operands from LDS only;
+//   waves 2-5 (output):   (Qp S^T) for 32 chunk rows each, + Ou, the output
+//                         stores; Qp and Ou prefetched two chunks ahead into a
+//                         ring of register sets;
+//   waves 6, 7 (loaders): copy each chunk's Mt and the workgroup's slice of
+//                         Bm into a three-deep LDS ring, two chunks ahead,
+//                         with direct global-to-LDS loads, then wait for the
+//                         chunk the next step needs.
+// One barrier per chunk step hands over the ring slot and the bf16 copy of S
+// (double-buffered).
+#include "gdr_device.h"
+#include "gdr_internal.h"
+#include "gdr_kernels.h"
+
+namespace gdr {
+namespace {
+
+typedef __bf16 bf;
+constexpr int kBV = 32;                       // state rows per workgroup
+constexpr int kMtBytes = 128 * 128 * 2;       // one chunk's Mt (32 KiB)
+constexpr int kBmBytes = kBV * 128 * 2;       // the workgroup's Bm slice (8 KiB)
+constexpr int kRing = 3;
+
+struct InterLds {
+  char mt[kRing][kMtBytes];   // Mt of chunks c, c + 1, c + 2 (workspace fragment order)
+  char bm[kRing][kBmBytes];   // the workgroup's Bm blocks (workspace order)
+  bf s[2][kBV * 128];         // bf16 copy of the workgroup's rows of S, swizzled
+  int2 tab[kMaxSegSlots];     // {first token, length} of the segment's chunks
+  float gam[kMaxSegSlots];    // exp(gc_last) of the segment's chunks
+};
+
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// One 16-byte piece per lane, global to LDS: the 64 lanes of the wave fill
+// the 1 KiB at dst (lane l at dst + 16 l).
+__device__ __forceinline__ void dma16(const char* src_wave, char* dst_wave, int lane) {
+  __builtin_amdgcn_global_load_lds(src_wave + 16 * lane,
+                                   (__attribute__((address_space(3))) void*)dst_wave, 16, 0, 0);
+}
+
+__global__ __launch_bounds__(512, 1) void inter_bf16_kernel(
+    const bf* __restrict__ inter, Chunks chunks, const float* __restrict__ gam,
+    const float* state_in, float* carry, float* state_out, int32_t N, int32_t Nv, int32_t slot0,
+    int32_t nseg, int first_segment, bf* __restrict__ out, bf* __restrict__ discard) {
+  constexpr int VB = 128 / kBV;
+  __shared__ InterLds s;
+
+  const int id = blockIdx.x;
+  const int pairs = N * Nv;
+  int bh, vb;
+  if ((pairs & 7) == 0) {
+    // the VB row blocks of one (b, h) read the same Mt and Qp: deal them to
+    // the same XCD (workgroups go to the 8 XCDs round-robin)
+    bh = (id & 7) + 8 * (id / (8 * VB));
+    vb = (id >> 3) % VB;
+  } else {
+    bh = id / VB;
+    vb = id % VB;
+  }
+  const int b = bh / Nv, h = bh % Nv;
+  const int tid = threadIdx.x, l = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int v0 = kBV * vb;
+  const size_t sb = (size_t)bh * 128 * 128;
+  int c0, c1;
+  chunks.seq_slots(b, c0, c1);
+
+  if (c0 == c1) {
+    // empty sequence: its final state is its initial state
+    if (first_segment && state_out && state_out != state_in) {
+      for (int idx = tid; idx < kBV * 128 / 4; idx += 512) {
+        const int r = idx / 32, c = (idx % 32) * 4;
+        const size_t off = sb + (size_t)(v0 + r) * 128 + c;
+        float4 val = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (state_in) val = *reinterpret_cast<const float4*>(state_in + off);
+        *reinterpret_cast<float4*>(state_out + off) = val;
+      }
+    }
+    return;
+  }
+  const int cb = max(c0, slot0), ce = min(c1, slot0 + nseg);
+  if (cb >= ce) return;
+  const float* src = (cb == c0) ? state_in : carry;
+  float* dstS = (ce == c1) ? state_out : carry;
+  const size_t mstride = (size_t)Nv * 4 * 128 * 128;
+  // matrices of (slot c, head h): Mt, Qp, Bm, Ou
+  const bf* mats0 = inter + (size_t)h * 4 * 128 * 128 - (size_t)slot0 * mstride;
+  auto mats = [&](int c) { return mats0 + (size_t)c * mstride; };
+
+  for (int idx = tid; idx < ce - cb; idx += 512) {
+    int st, ln;
+    chunks.slot(cb + idx, st, ln);
+    s.tab[idx] = make_int2(st, ln);
+    s.gam[idx] = gam[(size_t)(cb + idx) * Nv + h];
+  }
+
+  const int r16 = l & 15, q4 = l >> 4;
+
+  if (w >= 6) {
+    // ---------------- loaders: Mt blocks 16 lw .. 16 lw + 15 and Bm blocks
+    // 4 lw .. 4 lw + 3 of each chunk, two chunks ahead
+    const int lw = w - 6;
+    auto issue = [&](int c, int slot) {
+      const char* m = reinterpret_cast<const char*>(mats(c));
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const int bi = 16 * lw + k;
+        dma16(m + bi * 1024, s.mt[slot] + bi * 1024, l);
+      }
+      const char* bmv = reinterpret_cast<const char*>(mats(c) + 2 * 128 * 128) + vb * kBmBytes;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int bj = 4 * lw + k;
+        dma16(bmv + bj * 1024, s.bm[slot] + bj * 1024, l);
+      }
+    };
+    issue(cb, 0);
+    issue(min(cb + 1, ce - 1), 1);
+    asm volatile("s_waitcnt vmcnt(20)" ::: "memory");   // chunk cb in LDS
+    lds_barrier();                                         // tables, ring slot 0, S(cb)
+    int slot = 2;
+    for (int c = cb; c < ce; ++c) {
+      // ring slot (c + 2) % 3 was read in step c - 1, which ended at the
+      // last barrier; past the end the last chunk is loaded again, so every
+      // step issues the same loads and the wait below stays exact
+      issue(min(c + 2, ce - 1), slot);
+      slot = slot == kRing - 1 ? 0 : slot + 1;
+      asm volatile("s_waitcnt vmcnt(20)" ::: "memory");   // chunk c + 1 in LDS
+      lds_barrier();
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    return;
+  }
+
+  if (w < 2) {
+    // ---------------- state waves: rows v0 .. v0 + 31 of S, key rows
+    // rb .. rb + 63 of the product (S M')^T
+    const int rb = 64 * w;
+    f32x4 st[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        st[i][t] = zero4();
+        if (src)
+          st[i][t] = *reinterpret_cast<const f32x4*>(
+              src + sb + (size_t)(v0 + 16 * t + r16) * 128 + rb + 16 * i + 4 * q4);
+      }
+    auto put_s = [&](int buf) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          bf16x4 v;
+          v[0] = (bf)st[i][t][0]; v[1] = (bf)st[i][t][1]; v[2] = (bf)st[i][t][2]; v[3] = (bf)st[i][t][3];
+          *reinterpret_cast<bf16x4*>(s.s[buf] + Sw<bf>::at(16 * t + r16, rb + 16 * i + 4 * q4)) = v;
+        }
+    };
+    put_s(0);
+    lds_barrier();
+    int slot = 0, buf = 0;
+    for (int c = cb; c < ce; ++c) {
+      const float gC = s.gam[c - cb];
+      f32x4 acc[4][2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i][0] = acc[i][1] = zero4();
+      const char* mt = s.mt[slot];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 s0 = sw_frag<bf>(s.s[buf], r16, ks * 32 + 8 * q4);
+        const bf16x8 s1 = sw_frag<bf>(s.s[buf], 16 + r16, ks * 32 + 8 * q4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          // block (key row block rb / 16 + i, k-step ks) of Mt: lane l's 8 values
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+              mt + (((rb >> 4) + i) * 4 + ks) * 1024 + l * 16);
+          acc[i][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, s0, acc[i][0], 0, 0, 0);
+          acc[i][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, s1, acc[i][1], 0, 0, 0);
+        }
+      }
+      // S = exp(gc_last) S + S M' + Bm; this wave's Bm blocks are (wh = w, i, t)
+      const char* bmw = s.bm[slot] + w * 4096;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const bf16x4 x = *reinterpret_cast<const bf16x4*>(bmw + (i * 2 + t) * 512 + l * 8);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) st[i][t][e] = gC * st[i][t][e] + acc[i][t][e] + (float)x[e];
+        }
+      buf ^= 1;
+      put_s(buf);
+      slot = slot == kRing - 1 ? 0 : slot + 1;
+      lds_barrier();
+    }
+    if (dstS) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          *reinterpret_cast<f32x4*>(dstS + sb + (size_t)(v0 + 16 * t + r16) * 128 + rb + 16 * i +
+                                    4 * q4) = st[i][t];
+    }
+    return;
+  }
+
+  // ---------------- output waves: chunk rows rr0 .. rr0 + 31, all 32 state rows
+  const int ow = w - 2, rr0 = 32 * ow;
+  struct Ops {
+    bf16x8 a[2][4];     // rows rr0 + 16 i of Qp, k-step ks
+    bf16x4 x[2][2];     // Ou[r][v0 + 16 t + 4 q ..]
+  };
+  auto load_ops = [&](Ops& o, int c) {
+    const bf* m = mats(c);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        o.a[i][ks] = *reinterpret_cast<const bf16x8*>(
+            m + 128 * 128 + ((((rr0 >> 4) + i) * 4 + ks) * 512) + l * 8);
+    // Ou blocks pass_blk(vb, r / 64, (r % 64) / 16, t) of 256 values, 4 per lane
+    const bf* ou = m + 3 * 128 * 128;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+        o.x[i][t] = *reinterpret_cast<const bf16x4*>(
+            ou + pass_blk(vb, rr0 >> 6, ((rr0 & 63) >> 4) + i, t) + l * 4);
+  };
+  Ops ops[3];
+  load_ops(ops[0], cb);
+  load_ops(ops[1], min(cb + 1, ce - 1));
+  lds_barrier();
+  int buf = 0;
+  auto step = [&](Ops& o, Ops& next, int c) {
+    // the chunk two ahead (past the end, the last chunk again)
+    load_ops(next, min(c + 2, ce - 1));
+    const int2 e = s.tab[c - cb];
+    f32x4 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) acc[i][0] = acc[i][1] = zero4();
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const bf16x8 s0 = sw_frag<bf>(s.s[buf], r16, ks * 32 + 8 * q4);
+      const bf16x8 s1 = sw_frag<bf>(s.s[buf], 16 + r16, ks * 32 + 8 * q4);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        acc[i][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(s0, o.a[i][ks], acc[i][0], 0, 0, 0);
+        acc[i][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(s1, o.a[i][ks], acc[i][1], 0, 0, 0);
+      }
+    }
+    // acc[i][t] = (Qp S^T)[r][v .. v + 3], r = rr0 + 16 i + r16, v = 16 t + 4 q4;
+    // rows past the chunk's end go to the discard line (the store count
+    // stays fixed, so the memory waits of later steps stay exact)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = rr0 + 16 * i + r16;
+      bf* orow = r < e.y ? out + ((size_t)(e.x + r) * Nv + h) * 128 + v0 : discard;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        bf16x4 v;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) v[x] = (bf)(acc[i][t][x] + (float)o.x[i][t][x]);
+        *reinterpret_cast<bf16x4*>(orow + 16 * t + 4 * q4) = v;
+      }
+    }
+    buf ^= 1;
+    lds_barrier();
+  };
+  int c = cb;
+#pragma unroll 1
+  for (; c + 3 <= ce; c += 3) {
+    step(ops[0], ops[2], c);
+    step(ops[1], ops[0], c + 1);
+    step(ops[2], ops[1], c + 2);
+  }
+  if (c < ce) step(ops[0], ops[2], c);
+  if (c + 1 < ce) step(ops[1], ops[0], c + 1);
+}
+
+}  // namespace
+
+void launch_inter_bf16(const __bf16* inter, Chunks chunks, const float* gam, const float* state_in,
+                       float* carry, float* state_out, int32_t N, int32_t Nv, int32_t slot0,
+                       int32_t nseg, bool first_segment, __bf16* out, __bf16* discard,
+                       hipStream_t stream, LaunchEvents ev) {
+  const unsigned blocks = (unsigned)N * (unsigned)Nv * (unsigned)(128 / kBV);
+  hipExtLaunchKernelGGL(inter_bf16_kernel, dim3(blocks), dim3(512), 0, stream, ev.start, ev.stop, 0,
+                        inter, chunks, gam, state_in, carry, state_out, N, Nv, slot0, nseg,
+                        first_segment ? 1 : 0, out, discard);
+}
+
+}  // namespace gdr

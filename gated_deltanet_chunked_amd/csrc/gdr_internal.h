@@ -17,7 +17,7 @@ inline int64_t max_slots(int64_t T, int64_t N) { return T / 128 + N; }
 
 // Upper bound on the chunk slots of one segment (the state pass stages a
 // segment's chunk table in LDS).
-constexpr int kMaxSegSlots = 2048;
+constexpr int kMaxSegSlots = 512;
 
 // Largest number of value heads.  It keeps the 128 rows of a chunk of v (row
 // stride Nv * 128 elements of at most 4 bytes) within 2 GiB, so the kernels

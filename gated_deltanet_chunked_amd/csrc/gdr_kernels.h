@@ -81,6 +81,12 @@ void launch_inter(const Tin* inter, Chunks chunks, const float* gam,
                   int32_t slot0, int32_t nseg, bool first_segment, Tin* out, Tin* discard,
                   hipStream_t stream, LaunchEvents ev = {});
 
+// The bf16 kernel behind launch_inter<__bf16> (gdr_inter_bf16.hip).
+void launch_inter_bf16(const __bf16* inter, Chunks chunks, const float* gam, const float* state_in,
+                       float* carry, float* state_out, int32_t N, int32_t Nv, int32_t slot0,
+                       int32_t nseg, bool first_segment, __bf16* out, __bf16* discard,
+                       hipStream_t stream, LaunchEvents ev = {});
+
 // One decode step; the state is stored as St (float, or __bf16 for a bf16
 // state cache), the arithmetic is fp32 either way.
 template <typename Tin, typename St>
