@@ -12,7 +12,9 @@ used only to pin ``recurrent`` in the oracle's own tests.
 rounded to bfloat16 (``round_bf16``), pinned in
 ``tests/test_oracle_bf16_state.py``; ``decode_prologue`` and
 ``recurrent_step_conv`` add the conv update and gates in front of a decode
-step, pinned in ``tests/test_oracle_prologue.py``.
+step, pinned in ``tests/test_oracle_prologue.py``; ``gated_rmsnorm`` and
+``recurrent_step_gated`` are the gated RMSNorm after the rule, pinned in
+``tests/test_oracle_gated_norm.py``.
 """
 from __future__ import annotations
 
@@ -250,6 +252,51 @@ def recurrent_step_conv(mixed_qkv, conv_state, conv_w, conv_b, a, b, A_log, dt_b
     out, sout = recurrent(q, k, v, g, beta, state_in, np.arange(N + 1, dtype=np.int32), scale,
                           nthreads=nthreads, l2norm=l2norm)
     return out, sout, cs
+
+
+NORM_EPS = 1e-6
+
+
+def gated_rmsnorm(x, z, weight=None, eps: float = NORM_EPS, out_bf16: bool = False) -> np.ndarray:
+    """The gated RMSNorm in front of the output projection (Qwen3-Next blog
+    post: RMSNormGated in section 1, ``self.norm(core_attn_out, z)`` in section
+    6; the norm is the ``_norm`` of the Zero-Centered RMSNorm section,
+    x * rsqrt(mean(x^2) + eps), over each head's last dimension).
+
+    Reading taken where the pages are silent: the output gate z enters through
+    SiLU, z * sigmoid(z) (the activation the pages use for this block's conv and
+    for gating in the MLP), multiplied element-wise with the normalised output
+    and the per-channel weight w (None: ones, the initial value of the plain
+    RMSNorm the blog says RMSNormGated uses; the zero-centred form passes 1 + g):
+
+        y = x / sqrt(mean(x^2) + eps) * w * z * sigmoid(z)
+
+    Shapes: x, z [..., D]; weight [D].  fp64; ``out_bf16`` rounds y to bf16
+    (the result is cast back to the activation dtype).
+    """
+    x = _f64(x)
+    z = _f64(z)
+    w = np.ones(x.shape[-1]) if weight is None else _f64(weight)
+    inv = 1.0 / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+    y = x * inv * w * (z / (1.0 + np.exp(-z)))
+    return round_bf16(y) if out_bf16 else y
+
+
+def recurrent_step_gated(q, k, v, g, beta, state_in, z, weight, scale: float, eps: float = EPS,
+                         norm_eps: float = NORM_EPS, out_bf16: bool = False, nthreads: int = 0,
+                         l2norm: bool = True):
+    """One decode step followed by the gated RMSNorm of its output (blog post
+    sections 5(2) and 6).  The step's output is cast to the activation dtype
+    before the norm, as the blog's recurrence returns it (``out_bf16``: bf16).
+
+    Returns (y [N, Nv, Dv], state_out [N, Nv, Dv, Dk]).
+    """
+    N = np.asarray(q).shape[0]
+    cu = np.arange(N + 1, dtype=np.int32)
+    out, sout = recurrent(q, k, v, g, beta, state_in, cu, scale, eps=eps, nthreads=nthreads,
+                          l2norm=l2norm)
+    o = round_bf16(out) if out_bf16 else out
+    return gated_rmsnorm(o, z, weight, norm_eps, out_bf16=False), sout
 
 
 def rel_l2(x, ref) -> float:

@@ -1,12 +1,13 @@
 """Plant one mistake at a time in a copy of the oracle's Python functions (the
-bf16 rounding, the bf16-state step and the decode prologue) and check that a
-pin fails.
+bf16 rounding, the bf16-state step, the decode prologue and the gated RMSNorm)
+and check that a pin fails.
 
 Each mutant is a textual edit of ``oracle/__init__.py`` loaded as a separate
 module.  Its functions replace the oracle's while the pins of
-``test_oracle_bf16_state.py`` and ``test_oracle_prologue.py`` run; a mutant
-that passes every pin would mean those pins cannot tell that mistake from the
-definition, so each must fail at least one.
+``test_oracle_bf16_state.py``, ``test_oracle_prologue.py`` and
+``test_oracle_gated_norm.py`` run; a mutant that passes every pin would mean
+those pins cannot tell that mistake from the definition, so each must fail at
+least one.
 """
 import importlib.util
 import inspect
@@ -16,6 +17,7 @@ import pytest
 
 import oracle
 from tests import test_oracle_bf16_state as pins_bf16
+from tests import test_oracle_gated_norm as pins_norm
 from tests import test_oracle_prologue as pins_prologue
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "__init__.py")
@@ -45,10 +47,24 @@ MUTANTS = {
     "prefill_new_window_from_start": ("new_state[n] = full[:, -K:]", "new_state[n] = full[:, :K]"),
     "A_log_not_exponentiated": ("g = -np.exp(_f64(A_log))[None, :] * softplus",
                                 "g = -_f64(A_log)[None, :] * softplus"),
+    "norm_sum_not_mean": ("inv = 1.0 / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)",
+                          "inv = 1.0 / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + eps)"),
+    "norm_eps_outside_root": ("inv = 1.0 / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)",
+                              "inv = 1.0 / (np.sqrt(np.mean(x * x, axis=-1, keepdims=True)) + eps)"),
+    "norm_over_wrong_axis": ("inv = 1.0 / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)",
+                             "inv = 1.0 / np.sqrt(np.mean(x * x, axis=0, keepdims=True) + eps)"),
+    "gate_sigmoid_not_silu": ("y = x * inv * w * (z / (1.0 + np.exp(-z)))",
+                              "y = x * inv * w * (1.0 / (1.0 + np.exp(-z)))"),
+    "gate_dropped": ("y = x * inv * w * (z / (1.0 + np.exp(-z)))", "y = x * inv * w"),
+    "norm_weight_dropped": ("y = x * inv * w * (z / (1.0 + np.exp(-z)))",
+                            "y = x * inv * (z / (1.0 + np.exp(-z)))"),
+    "norm_weight_one_plus": ("w = np.ones(x.shape[-1]) if weight is None else _f64(weight)",
+                             "w = np.ones(x.shape[-1]) if weight is None else 1.0 + _f64(weight)"),
+    "gated_step_not_cast": ("o = round_bf16(out) if out_bf16 else out", "o = out"),
 }
 
 REPLACED = ("round_bf16", "recurrent_step_bf16_state", "decode_prologue", "prefill_prologue",
-            "recurrent_step_conv")
+            "recurrent_step_conv", "gated_rmsnorm", "recurrent_step_gated")
 
 
 def _mutant_module(name, old, new):
@@ -63,7 +79,7 @@ def _mutant_module(name, old, new):
 
 
 def _pins():
-    for mod in (pins_bf16, pins_prologue):
+    for mod in (pins_bf16, pins_prologue, pins_norm):
         for n, fn in sorted(vars(mod).items()):
             if n.startswith("test_") and callable(fn):
                 yield n, fn
