@@ -26,8 +26,10 @@ so that no input is left in the 256 MB Infinity Cache.  Unless
 ``--chunk-only``: the decode step with its state stored in bf16
 (``decode_bf16_state``), ``gdr_recurrent_multi`` on 256 sequences x 4
 tokens (``multi_token``), the decode step with its conv update and gates
-fused in front (``decode_conv``) and the conv/gate prologue of the chunked
-path on the chunk workload (``conv_prefill``).  One JSON line is printed.
+fused in front (``decode_conv``), the gated RMSNorm on the chunk workload's
+output rows (``gated_rmsnorm``) and fused behind the decode step
+(``decode_gated``), and the conv/gate prologue of the chunked path on the
+chunk workload (``conv_prefill``).  One JSON line is printed.
 """
 from __future__ import annotations
 
@@ -96,6 +98,11 @@ def alg_bytes_conv_prefill(T, N, Nqk, Nv, K=4, es=2):
     beta written, kernels read once, every cached window read and written."""
     C = (2 * Nqk + Nv) * D
     return 2 * T * C * es + 4 * T * Nv * 4 + C * K * es + 2 * N * C * K * es + 2 * Nv * 4
+
+
+def alg_bytes_gated_rmsnorm(rows, es=2):
+    """x and z read, y written once: three rows of D values per row."""
+    return 3 * rows * D * es + D * es
 
 
 def measured_traffic(kernel: str):
@@ -413,6 +420,53 @@ def extras(gdr, dec, Dd, dout, pre, cfg, args, dev, scale):
                           "frac_hbm_peak": round(conv_gbps / HBM_PEAK_GBPS, 4),
                           "tokens_per_s": round(dec.N / conv_s, 1), "alg_bytes": conv_bytes}
     del cv, cf, cs_a, cs_b
+
+    # the gated RMSNorm behind the rule: standalone on the chunk workload's
+    # output rows (in place, as a caller applies it to gdr_chunk_fwd's out),
+    # and fused into the decode step
+    from gated_deltanet_chunked_amd.inputs import make_gate
+    rows = T * Nv
+    nx = torch.randn((T, Nv, D), device=dev, generator=torch.Generator(device=dev).manual_seed(cfg))
+    nx = nx.to(torch.bfloat16)
+    z, w = make_gate((T, Nv, D), seed=cfg)
+    nz = torch.from_numpy(z).to(dev, torch.bfloat16)
+    nw = torch.from_numpy(w).to(dev, torch.bfloat16)
+    ny = torch.empty_like(nx)
+    for _ in range(args.warmup):
+        gdr.gated_rmsnorm(nx, nz, nw, out=ny)
+    ntim = []
+    for _ in range(args.steps):
+        gdr.gated_rmsnorm(nx, nz, nw, out=ny, timings=ntim)
+    torch.cuda.synchronize()
+    norm_s = float(np.mean([ms for _, ms in ntim])) * 1e-3
+    norm_bytes = alg_bytes_gated_rmsnorm(rows)
+    norm_gbps = norm_bytes / norm_s / 1e9
+    res["gated_rmsnorm"] = {"workload": f"{rows} rows of {D} bf16 (T={T} x Nv={Nv}), weight given",
+                            "gpu_ms": round(norm_s * 1e3, 4), "gbps": round(norm_gbps, 1),
+                            "frac_hbm_peak": round(norm_gbps / HBM_PEAK_GBPS, 4),
+                            "alg_bytes": norm_bytes}
+    del nx, nz, nw, ny
+    dz, dw = make_gate((dec.N, dec.Nv, D), seed=4)
+    dz = torch.from_numpy(dz).to(dev, torch.bfloat16)
+    dw = torch.from_numpy(dw).to(dev, torch.bfloat16)
+    gstate = Dd["s0"].clone()
+    for _ in range(args.warmup):
+        gdr.recurrent_step_gated(Dd["q"], Dd["k"], Dd["v"], Dd["g"], Dd["beta"], gstate, dz, dw,
+                                 out=dout, scale=scale)
+    gtim = []
+    for _ in range(args.steps):
+        gdr.recurrent_step_gated(Dd["q"], Dd["k"], Dd["v"], Dd["g"], Dd["beta"], gstate, dz, dw,
+                                 out=dout, scale=scale, timings=gtim)
+    torch.cuda.synchronize()
+    gd_s = float(np.mean([ms for _, ms in gtim])) * 1e-3
+    gd_bytes = alg_bytes_decode(dec.N, dec.Nqk, dec.Nv) + dec.N * dec.Nv * D * 2 + D * 2
+    gd_gbps = gd_bytes / gd_s / 1e9
+    res["decode_gated"] = {"workload": f"{dec.N} sequences x 1 token, Nqk={dec.Nqk} Nv={dec.Nv} "
+                                       "bf16, gated RMSNorm fused behind, fp32 states",
+                           "gpu_ms": round(gd_s * 1e3, 4), "gbps": round(gd_gbps, 1),
+                           "frac_hbm_peak": round(gd_gbps / HBM_PEAK_GBPS, 4),
+                           "tokens_per_s": round(dec.N / gd_s, 1), "alg_bytes": gd_bytes}
+    del dz, dw, gstate
 
     # the conv/gate prologue of the chunked path (gdr_conv_prefill) on the
     # chunk workload's tokens: cached windows in, new windows out

@@ -7,6 +7,7 @@ missing, every call raises.
 
     out, state = chunk_fwd(q, k, v, g, beta, cu_seqlens, state_in=s0)
     out = recurrent_step(q, k, v, g, beta, state, state_out=state)   # in place
+    y = gated_rmsnorm(out, z, weight)                                 # before out_proj
 """
 from __future__ import annotations
 
@@ -84,6 +85,13 @@ def load(path: str = LIB_PATH):
     lib.gdr_chunk_fwd_no_alloc.restype = ctypes.c_int
     lib.gdr_chunk_fwd_no_alloc_scratch_bytes.argtypes = []
     lib.gdr_chunk_fwd_no_alloc_scratch_bytes.restype = sz
+    lib.gdr_gated_rmsnorm.argtypes = [vp, vp, vp, ctypes.c_int64, i32, ctypes.c_int, f32, vp, vp,
+                                      ctypes.POINTER(ctypes.c_float)]
+    lib.gdr_gated_rmsnorm.restype = ctypes.c_int
+    lib.gdr_recurrent_step_gated.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
+                                             ctypes.c_int, f32, u32, vp, vp, f32, vp, vp,
+                                             ctypes.POINTER(ctypes.c_float)]
+    lib.gdr_recurrent_step_gated.restype = ctypes.c_int
     lib.gdr_status_string.argtypes = [ctypes.c_int]
     lib.gdr_status_string.restype = ctypes.c_char_p
     lib.gdr_version.argtypes = []
@@ -444,4 +452,84 @@ def recurrent_step(q, k, v, g, beta, state_in, *, state_out=None, out=None,
     if st != 0:
         raise GdrError(st, "gdr_recurrent_step_timed")
     timings.append(("decode", float(ms.value)))
+    return out
+
+
+NORM_EPS = 1e-6
+
+
+def gated_rmsnorm(x, z, weight=None, *, eps: float = NORM_EPS, out=None,
+                  timings: Optional[list] = None):
+    """Gated RMSNorm over the last dimension (``gdr_gated_rmsnorm``):
+    y = x / sqrt(mean(x^2) + eps) * weight * SiLU(z).
+
+    x, z [..., 128] of one dtype (bf16 or f32), e.g. the rule's out [T, Nv, 128];
+    weight [128] of that dtype or None (ones).  ``out`` may be ``x`` (in place).
+    With a list as ``timings`` the call is timed (blocking) and appends
+    ("gated_rmsnorm", kernel milliseconds).
+    """
+    lib = load()
+    dev = x.device
+    dt = x.dtype
+    code = _dtype_code(x)
+    if x.shape[-1] != D:
+        raise ValueError(f"x: last dimension {x.shape[-1]}, expected {D}")
+    _check(x, "x", tuple(x.shape), dt, dev)
+    _check(z, "z", tuple(x.shape), dt, dev)
+    _check(weight, "weight", (D,), dt, dev)
+    if out is None:
+        import torch
+        out = torch.empty_like(x)
+    _check(out, "out", tuple(x.shape), dt, dev)
+    rows = x.numel() // D
+    ms = ctypes.c_float(0.0)
+    st = lib.gdr_gated_rmsnorm(_ptr(x), _ptr(z), _ptr(weight), rows, D, code, float(eps), _ptr(out),
+                               _stream(), ctypes.byref(ms) if timings is not None else None)
+    if st != 0:
+        raise GdrError(st, "gdr_gated_rmsnorm")
+    if timings is not None:
+        timings.append(("gated_rmsnorm", float(ms.value)))
+    return out
+
+
+def recurrent_step_gated(q, k, v, g, beta, state_in, z, weight=None, *, state_out=None, out=None,
+                         scale: Optional[float] = None, l2norm: bool = True,
+                         norm_eps: float = NORM_EPS, timings: Optional[list] = None):
+    """One decode step with the gated RMSNorm fused behind it
+    (``gdr_recurrent_step_gated``).  Arguments as ``recurrent_step`` (float32
+    states), plus z [N, Nv, 128] and weight [128] (or None) in q's dtype.
+    Returns the gated, normalised output [N, Nv, 128]."""
+    import torch
+    lib = load()
+    N, Nqk, _ = q.shape
+    Nv = v.shape[1]
+    dev = q.device
+    dt = q.dtype
+    code = _dtype_code(q)
+    _check(q, "q", (N, Nqk, D), dt, dev)
+    _check(k, "k", (N, Nqk, D), dt, dev)
+    _check(v, "v", (N, Nv, D), dt, dev)
+    _check(g, "g", (N, Nv), torch.float32, dev)
+    _check(beta, "beta", (N, Nv), torch.float32, dev)
+    _check(state_in, "state_in", (N, Nv, D, D), torch.float32, dev)
+    if state_out is None:
+        state_out = state_in
+    _check(state_out, "state_out", (N, Nv, D, D), torch.float32, dev)
+    _check(z, "z", (N, Nv, D), dt, dev)
+    _check(weight, "weight", (D,), dt, dev)
+    if out is None:
+        out = torch.empty((N, Nv, D), dtype=dt, device=dev)
+    _check(out, "out", (N, Nv, D), dt, dev)
+    if scale is None:
+        scale = D ** -0.5
+    ms = ctypes.c_float(0.0)
+    st = lib.gdr_recurrent_step_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                      _ptr(state_in), _ptr(state_out), N, Nqk, Nv, D, code,
+                                      float(scale), GDR_FLAG_QK_L2NORM if l2norm else 0, _ptr(z),
+                                      _ptr(weight), float(norm_eps), _ptr(out), _stream(),
+                                      ctypes.byref(ms) if timings is not None else None)
+    if st != 0:
+        raise GdrError(st, "gdr_recurrent_step_gated")
+    if timings is not None:
+        timings.append(("decode_gated", float(ms.value)))
     return out

@@ -248,11 +248,15 @@ void step_as(const StepArgs& a, int norm, hipStream_t st, LaunchEvents ev) {
   if (a.dtype == GDR_BF16)
     launch_decode<__bf16, St>(static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
                               static_cast<const __bf16*>(a.v), a.g, a.beta, sin, sout, a.N, a.Nqk,
-                              a.Nv, a.scale, norm, static_cast<__bf16*>(a.out), st, ev);
+                              a.Nv, a.scale, norm, static_cast<__bf16*>(a.out), st, ev,
+                              static_cast<const __bf16*>(a.z), static_cast<const __bf16*>(a.nw),
+                              a.norm_eps);
   else
     launch_decode<float, St>(static_cast<const float*>(a.q), static_cast<const float*>(a.k),
                              static_cast<const float*>(a.v), a.g, a.beta, sin, sout, a.N, a.Nqk,
-                             a.Nv, a.scale, norm, static_cast<float*>(a.out), st, ev);
+                             a.Nv, a.scale, norm, static_cast<float*>(a.out), st, ev,
+                             static_cast<const float*>(a.z), static_cast<const float*>(a.nw),
+                             a.norm_eps);
 }
 
 gdr_status run_step(const StepArgs& a, hipStream_t st, LaunchEvents ev) {
@@ -309,6 +313,49 @@ extern "C" gdr_status gdr_recurrent_step_bf16_state(const void* q, const void* k
                                                     void* out, void* stream, float* kernel_ms) {
   StepArgs a{q, k, v, g, beta, state_in, state_out, N, Nqk, Nv, D, dtype, scale, flags, out, true};
   return step_entry(a, static_cast<hipStream_t>(stream), kernel_ms);
+}
+
+extern "C" gdr_status gdr_recurrent_step_gated(const void* q, const void* k, const void* v,
+                                               const float* g, const float* beta,
+                                               const float* state_in, float* state_out, int32_t N,
+                                               int32_t Nqk, int32_t Nv, int32_t D,
+                                               gdr_dtype dtype, float scale, uint32_t flags,
+                                               const void* z, const void* weight, float norm_eps,
+                                               void* out, void* stream, float* kernel_ms) {
+  if (N > 0 && !z) return GDR_ERR_INVALID_ARGUMENT;
+  StepArgs a{q, k, v, g, beta, state_in, state_out, N, Nqk, Nv, D, dtype, scale, flags, out, false,
+             z, weight, norm_eps};
+  return step_entry(a, static_cast<hipStream_t>(stream), kernel_ms);
+}
+
+extern "C" gdr_status gdr_gated_rmsnorm(const void* x, const void* z, const void* weight,
+                                        int64_t rows, int32_t D, gdr_dtype dtype, float eps,
+                                        void* y, void* stream, float* kernel_ms) {
+  const NormArgs a{x, z, weight, rows, D, dtype, eps, y};
+  gdr_status s = validate_norm(a);
+  if (s != GDR_OK) return s;
+  if (kernel_ms) *kernel_ms = 0.0f;
+  if (rows == 0) return GDR_OK;
+  EventPairs pairs;
+  LaunchEvents ev{};
+  if (kernel_ms) {
+    if (!pairs.create(1)) return GDR_ERR_HIP;
+    ev = LaunchEvents{pairs.ev[0], pairs.ev[1]};
+  }
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (dtype == GDR_BF16)
+    launch_gated_rmsnorm<__bf16>(static_cast<const __bf16*>(x), static_cast<const __bf16*>(z),
+                                 static_cast<const __bf16*>(weight), rows, eps,
+                                 static_cast<__bf16*>(y), st, ev);
+  else
+    launch_gated_rmsnorm<float>(static_cast<const float*>(x), static_cast<const float*>(z),
+                                static_cast<const float*>(weight), rows, eps,
+                                static_cast<float*>(y), st, ev);
+  if (hipGetLastError() != hipSuccess) return GDR_ERR_HIP;
+  if (kernel_ms && (hipEventSynchronize(pairs.ev[1]) != hipSuccess ||
+                    hipEventElapsedTime(kernel_ms, pairs.ev[0], pairs.ev[1]) != hipSuccess))
+    return GDR_ERR_HIP;
+  return GDR_OK;
 }
 
 extern "C" gdr_status gdr_recurrent_multi(const void* q, const void* k, const void* v,

@@ -108,7 +108,8 @@ __global__ __launch_bounds__(256) void decode_kernel(const T* __restrict__ q, co
                                                      const float* __restrict__ beta,
                                                      const ST* state_in, ST* state_out,
                                                      int32_t Nqk, int32_t Nv, float scale, int norm,
-                                                     T* __restrict__ out) {
+                                                     T* __restrict__ out, const T* __restrict__ gz,
+                                                     const T* __restrict__ gw, float geps) {
   const int bh = blockIdx.x;
   const int n = bh / Nv, h = bh % Nv;
   const int j = h / (Nv / Nqk);
@@ -132,6 +133,13 @@ __global__ __launch_bounds__(256) void decode_kernel(const T* __restrict__ q, co
   for (int i = 0; i < 8; ++i) vr[i] = vp[rg + 16 * i];
   const float gv = g[(size_t)n * Nv + h];
   const float bt = beta[(size_t)n * Nv + h];
+  // gated norm (gz not NULL): lane cg < 8 of row group rg finishes row
+  // rg + 16 cg, so it loads that row's gate and weight
+  float zr = 0.f, wr = 1.f;
+  if (gz && cg < 8) {
+    zr = to_f32(gz[((size_t)n * Nv + h) * kD + rg + 16 * cg]);
+    if (gw) wr = to_f32(gw[rg + 16 * cg]);
+  }
 
   StatePiece<ST> s[8];
 #pragma unroll
@@ -156,6 +164,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const T* __restrict__ q, co
   kq = group16_sum(kq);
   const float alpha = expf(gv);
   T* op = out + ((size_t)n * Nv + h) * kD;
+  float ov[8];   // the group's output rows rg + 16 i, as stored (dtype T)
 
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -169,10 +178,30 @@ __global__ __launch_bounds__(256) void decode_kernel(const T* __restrict__ q, co
     a = group16_sum(a);
     b = group16_sum(b);
     const float delta = bt * (to_f32(vr[i]) - alpha * a);
-    if (cg == 0) op[row] = from_f32<T>(alpha * b + delta * kq);
+    ov[i] = to_f32(from_f32<T>(alpha * b + delta * kq));
+    if (cg == 0 && !gz) op[row] = from_f32<T>(ov[i]);
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] = alpha * x[e] + delta * kh[e];
     StatePiece<ST>::store(state_out + sb + (size_t)row * kD, cg, x);
+  }
+  if (gz) {
+    // out = o / sqrt(mean(o^2) + eps) * w * SiLU(z) over the head's 128 rows
+    // (blog post section 6): the 16 row groups' sums of squares meet in LDS
+    // and every thread adds them in the same order
+    __shared__ float part[16];
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ss += ov[i] * ov[i];
+    if (cg == 0) part[rg] = ss;
+    __syncthreads();
+    float tot = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) tot += part[r];
+    const float inv = 1.0f / sqrtf(tot * (1.0f / kD) + geps);
+    float o = ov[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) o = cg == i ? ov[i] : o;
+    if (cg < 8) op[rg + 16 * cg] = from_f32<T>(o * inv * wr * (zr / (1.0f + expf(-zr))));
   }
   (void)l;
 }
@@ -459,16 +488,17 @@ GDR_CONV_INST(__bf16)
 template <typename T, typename ST>
 void launch_decode(const T* q, const T* k, const T* v, const float* g, const float* beta,
                    const ST* state_in, ST* state_out, int32_t N, int32_t Nqk, int32_t Nv,
-                   float scale, int norm, T* out, hipStream_t stream, LaunchEvents ev) {
+                   float scale, int norm, T* out, hipStream_t stream, LaunchEvents ev,
+                   const T* gate_z, const T* gate_w, float gate_eps) {
   hipExtLaunchKernelGGL(decode_kernel<T, ST>, dim3((unsigned)N * (unsigned)Nv), dim3(256), 0,
                         stream, ev.start, ev.stop, 0, q, k, v, g, beta, state_in, state_out, Nqk,
-                        Nv, scale, norm, out);
+                        Nv, scale, norm, out, gate_z, gate_w, gate_eps);
 }
 
 #define GDR_DECODE_INST(T, ST)                                                                   \
   template void launch_decode<T, ST>(const T*, const T*, const T*, const float*, const float*,  \
                                      const ST*, ST*, int32_t, int32_t, int32_t, float, int, T*, \
-                                     hipStream_t, LaunchEvents);
+                                     hipStream_t, LaunchEvents, const T*, const T*, float);
 GDR_DECODE_INST(float, float)
 GDR_DECODE_INST(__bf16, float)
 GDR_DECODE_INST(float, __bf16)

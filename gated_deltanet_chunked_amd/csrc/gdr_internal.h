@@ -87,6 +87,19 @@ struct StepArgs {
   uint32_t flags;
   void* out;
   bool state_bf16;
+  // gated RMSNorm behind the step (z NULL: none); weight NULL means ones
+  const void* z = nullptr;
+  const void* nw = nullptr;
+  float norm_eps = 0.f;
+};
+
+struct NormArgs {
+  const void* x; const void* z; const void* w;
+  int64_t rows;
+  int32_t D;
+  gdr_dtype dtype;
+  float eps;
+  void* y;
 };
 
 struct ConvStepArgs {
@@ -115,6 +128,7 @@ gdr_status validate_conv_prefill(const ConvPrefillCheck& a);
 gdr_status validate_chunk(const ChunkArgs& a);
 gdr_status validate_conv_step(const ConvStepArgs& a);
 gdr_status validate_step(const StepArgs& a);
+gdr_status validate_norm(const NormArgs& a);
 
 inline size_t dtype_size(gdr_dtype d) { return d == GDR_BF16 ? 2 : 4; }
 

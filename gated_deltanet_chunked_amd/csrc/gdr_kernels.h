@@ -92,7 +92,14 @@ void launch_inter_bf16(const __bf16* inter, Chunks chunks, const float* gam, con
 template <typename Tin, typename St>
 void launch_decode(const Tin* q, const Tin* k, const Tin* v, const float* g, const float* beta,
                    const St* state_in, St* state_out, int32_t N, int32_t Nqk, int32_t Nv,
-                   float scale, int norm, Tin* out, hipStream_t stream, LaunchEvents ev = {});
+                   float scale, int norm, Tin* out, hipStream_t stream, LaunchEvents ev = {},
+                   const Tin* gate_z = nullptr, const Tin* gate_w = nullptr, float gate_eps = 0.f);
+
+// The gated RMSNorm y = x / rms(x) * w * SiLU(z) over rows of kD values; x may
+// equal y.  w NULL: ones.
+template <typename T>
+void launch_gated_rmsnorm(const T* x, const T* z, const T* w, int64_t rows, float eps, T* y,
+                          hipStream_t stream, LaunchEvents ev = {});
 
 // Several tokens per sequence, token by token with the state in registers;
 // sequence n owns tokens [cu[n], cu[n+1]) of the packed batch.

@@ -2,6 +2,8 @@
 // Plain C++: no HIP calls, so every error path runs without a GPU.
 #include <stdint.h>
 
+#include <cmath>
+
 #include "gdr_internal.h"
 
 namespace gdr {
@@ -138,6 +140,30 @@ gdr_status validate_step(const StepArgs& a) {
   R others[] = {{a.q, qk_bytes}, {a.k, qk_bytes}, {a.v, v_bytes}, {a.g, gb_bytes}, {a.beta, gb_bytes}};
   for (const R& r : others)
     if (overlap(a.state_out, st_bytes, r.p, r.n)) return GDR_ERR_INVALID_ARGUMENT;
+  if (a.z) {
+    if (!aligned16(a.z) || (a.nw && !aligned16(a.nw))) return GDR_ERR_INVALID_ARGUMENT;
+    if (!std::isfinite(a.norm_eps) || a.norm_eps < 0.0f) return GDR_ERR_INVALID_ARGUMENT;
+    if (overlap(a.out, v_bytes, a.z, v_bytes) || overlap(a.out, v_bytes, a.nw, 128 * es) ||
+        overlap(a.state_out, st_bytes, a.z, v_bytes) || overlap(a.state_out, st_bytes, a.nw, 128 * es))
+      return GDR_ERR_INVALID_ARGUMENT;
+  }
+  return GDR_OK;
+}
+
+gdr_status validate_norm(const NormArgs& a) {
+  if (a.D != 128) return GDR_ERR_UNSUPPORTED;
+  if (a.dtype != GDR_F32 && a.dtype != GDR_BF16) return GDR_ERR_UNSUPPORTED;
+  if (a.rows < 0 || a.rows >= (int64_t(1) << 31)) return GDR_ERR_INVALID_ARGUMENT;
+  if (!std::isfinite(a.eps) || a.eps < 0.0f) return GDR_ERR_INVALID_ARGUMENT;
+  if (a.rows == 0) return GDR_OK;
+  if (!a.x || !a.z || !a.y) return GDR_ERR_INVALID_ARGUMENT;
+  if (!aligned16(a.x) || !aligned16(a.z) || !aligned16(a.y) || (a.w && !aligned16(a.w)))
+    return GDR_ERR_INVALID_ARGUMENT;
+  const int64_t es = static_cast<int64_t>(dtype_size(a.dtype));
+  const int64_t bytes = a.rows * 128 * es;
+  if (a.y != a.x && overlap(a.y, bytes, a.x, bytes)) return GDR_ERR_INVALID_ARGUMENT;
+  if (overlap(a.y, bytes, a.z, bytes) || overlap(a.y, bytes, a.w, 128 * es))
+    return GDR_ERR_INVALID_ARGUMENT;
   return GDR_OK;
 }
 

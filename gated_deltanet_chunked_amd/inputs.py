@@ -112,6 +112,21 @@ def _draw(rng, lengths, Nqk, Nv, dtype, seed, state_std, A_range, dk, dv, name):
                      dtype=dtype, seed=seed, name=name)
 
 
+def make_gate(shape, *, dtype: str = "bf16", seed: int = 0, weight: bool = True):
+    """Inputs of the gated RMSNorm after the rule: the output gate z
+    (2 * standard normal, so that SiLU(z) spans its curved part and its linear
+    tail) of ``shape`` [..., D] and, with ``weight``, a per-channel weight
+    U(0.5, 1.5) of [D] (None otherwise: the norm's initial ones).  Rounded to
+    bf16 when dtype is "bf16".  Returns (z, w) as float32 arrays."""
+    rng = np.random.default_rng(seed)
+    z = (2.0 * rng.standard_normal(shape)).astype(np.float32)
+    w = rng.uniform(0.5, 1.5, size=shape[-1]).astype(np.float32) if weight else None
+    if dtype == "bf16":
+        z = round_to_bf16(z)
+        w = None if w is None else round_to_bf16(w)
+    return z, w
+
+
 # The five workloads the throughput and parity targets are quoted on.
 CONFIG_NAMES = {
     0: "tiny chunk fwd: B=1 T=512 Nqk=2 Nv=4 D=128 fp32, zero initial state",

@@ -22,7 +22,10 @@
  *   gdr_recurrent_step_conv       -- decode with the conv update and gates fused
  *                                    in front;
  * and the conv/gate prologue of the chunkwise path:
- *   gdr_conv_prefill              -- q, k, v, g, beta from projected channels.
+ *   gdr_conv_prefill              -- q, k, v, g, beta from projected channels;
+ * and the gated RMSNorm after the rule (blog post section 6):
+ *   gdr_gated_rmsnorm             -- on any output rows (e.g. gdr_chunk_fwd's);
+ *   gdr_recurrent_step_gated      -- decode with the norm fused behind it.
  *
  * Conventions shared by all calls:
  *   - All tensor pointers are DEVICE pointers, caller-owned, contiguous,
@@ -316,6 +319,55 @@ gdr_status gdr_conv_prefill(const void* mixed_qkv, const void* conv_state_in,
                             int32_t T, int32_t Nqk, int32_t Nv, int32_t D, gdr_dtype dtype,
                             void* q, void* k, void* v, float* g, float* beta, void* stream,
                             float* kernel_ms);
+
+/*
+ * The gated RMSNorm in front of the output projection (Qwen3-Next blog post:
+ * RMSNormGated in section 1, applied to the rule's output and the output gate
+ * z in section 6; the RMS form is the _norm of its Zero-Centered RMSNorm
+ * section).  Per row r of D values (one token and value head):
+ *   y[r][i] = x[r][i] / sqrt(mean_j x[r][j]^2 + eps) * weight[i] * SiLU(z[r][i])
+ * with SiLU(t) = t * sigmoid(t).  The pages name the module but not its gate
+ * function; SiLU is the library's reading (the activation the pages use for
+ * the block's conv and for gating in its MLP).  The arithmetic is float32 on
+ * the stored values; y is rounded to dtype (nearest even) when stored.
+ *
+ * x, z      [rows, D] dtype (row-major; the rule's out [T, Nv, D] is
+ *           rows = T * Nv)
+ * weight    [D] dtype, or NULL for ones (RMSNormGated's initial weight)
+ * rows      >= 0 and < 2^31;  D must be 128 (GDR_ERR_UNSUPPORTED)
+ * eps       >= 0 and finite (Qwen3-Next uses 1e-6)
+ * y         [rows, D] dtype; may equal x (in place), must not overlap x
+ *           otherwise, nor z or weight
+ * kernel_ms NULL, or where to write the kernel's GPU time (the call then
+ *           blocks until the kernel ends)
+ * One launch, HBM bound: 3 D dtype values move per row.
+ */
+gdr_status gdr_gated_rmsnorm(const void* x, const void* z, const void* weight, int64_t rows,
+                             int32_t D, gdr_dtype dtype, float eps, void* y, void* stream,
+                             float* kernel_ms);
+
+/*
+ * One decode step with the gated RMSNorm fused behind it (blog post sections
+ * 5(2) and 6): the step of gdr_recurrent_step, its output o cast to dtype,
+ * then out = gated RMSNorm of o as gdr_gated_rmsnorm defines it, per
+ * (sequence, value head).  Same arguments, layouts and errors as
+ * gdr_recurrent_step, plus:
+ *
+ * z          [N, Nv, D] dtype, the output gate (required); must not overlap out
+ * weight     [D] dtype, or NULL for ones
+ * norm_eps   >= 0 and finite
+ * kernel_ms  NULL, or where to write the kernel's GPU time (the call then
+ *            blocks until the kernel ends)
+ *
+ * out receives the normalised, gated rows only; o itself is not stored.
+ */
+gdr_status gdr_recurrent_step_gated(const void* q, const void* k, const void* v,
+                                    const float* g, const float* beta,
+                                    const float* state_in, float* state_out,
+                                    int32_t N, int32_t Nqk, int32_t Nv, int32_t D,
+                                    gdr_dtype dtype, float scale, uint32_t flags,
+                                    const void* z, const void* weight, float norm_eps,
+                                    void* out, void* stream, float* kernel_ms);
 
 /* A static, human-readable name for a status code. */
 const char* gdr_status_string(gdr_status s);

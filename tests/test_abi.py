@@ -29,7 +29,7 @@ def test_header_declares_the_entry_points():
     for n in ("gdr_chunk_fwd", "gdr_recurrent_step", "gdr_chunk_fwd_workspace_size",
               "gdr_status_string", "gdr_version", "gdr_chunk_fwd_timed",
               "gdr_recurrent_step_timed", "gdr_recurrent_step_bf16_state", "gdr_recurrent_multi",
-              "gdr_recurrent_step_conv"):
+              "gdr_recurrent_step_conv", "gdr_gated_rmsnorm", "gdr_recurrent_step_gated"):
         assert n in names
 
 
@@ -333,3 +333,67 @@ def test_conv_prefill_validates_before_launching():
     assert call(g=addr["beta"]) == INVALID
     ms = ctypes.c_float(1.0)
     assert call(T=0, cs_out=None, ms=ctypes.byref(ms)) == OK and ms.value == 0.0
+
+
+def test_gated_rmsnorm_validates_before_launching():
+    """gdr_gated_rmsnorm: D, dtype, rows, eps, pointers and overlaps."""
+    lib = gdr.load()
+    rows = 64
+    nb = rows * 128 * 2
+    addr = dict(x=1 << 40, z=(1 << 40) + (1 << 24), w=(1 << 40) + (2 << 24), y=(1 << 40) + (3 << 24))
+
+    def call(**over):
+        a = dict(addr, rows=rows, D=128, dtype=gdr.GDR_BF16, eps=1e-6, ms=None)
+        a.update(over)
+        return lib.gdr_gated_rmsnorm(a["x"], a["z"], a["w"], a["rows"], a["D"], a["dtype"], a["eps"],
+                                     a["y"], None, a["ms"])
+
+    assert call(D=64) == UNSUPPORTED
+    assert call(dtype=3) == UNSUPPORTED
+    assert call(rows=-1) == INVALID
+    assert call(rows=1 << 31) == INVALID
+    assert call(eps=-1e-6) == INVALID
+    assert call(eps=float("inf")) == INVALID
+    assert call(eps=float("nan")) == INVALID
+    for name in ("x", "z", "y"):
+        assert call(**{name: None}) == INVALID, name
+    assert call(x=addr["x"] + 8) == INVALID                  # misaligned
+    assert call(w=addr["w"] + 4) == INVALID
+    assert call(y=addr["x"] + 256) == INVALID                # partial overlap with x
+    assert call(y=addr["z"]) == INVALID                      # over the gate
+    assert call(y=addr["w"] - nb + 128) == INVALID           # over the weight
+    ms = ctypes.c_float(1.0)
+    assert call(rows=0, x=None, z=None, y=None, ms=ctypes.byref(ms)) == OK and ms.value == 0.0
+
+
+def test_recurrent_step_gated_validates_before_launching():
+    """gdr_recurrent_step_gated: the step's checks plus the gate's."""
+    lib = gdr.load()
+    N, Nqk, Nv = 2, 2, 4
+    sizes = dict(q=N * Nqk * 256, k=N * Nqk * 256, v=N * Nv * 256, g=N * Nv * 4, beta=N * Nv * 4,
+                 s_in=N * Nv * 65536, s_out=N * Nv * 65536, z=N * Nv * 256, w=256, out=N * Nv * 256)
+    base, addr = 1 << 40, {}
+    for k_, n in sizes.items():
+        addr[k_] = base
+        base += (n + (1 << 20)) & ~255
+
+    def call(**over):
+        a = dict(addr, N=N, Nqk=Nqk, Nv=Nv, D=128, dtype=gdr.GDR_BF16, eps=1e-6, ms=None)
+        a.update(over)
+        return lib.gdr_recurrent_step_gated(a["q"], a["k"], a["v"], a["g"], a["beta"], a["s_in"],
+                                            a["s_out"], a["N"], a["Nqk"], a["Nv"], a["D"],
+                                            a["dtype"], 0.088, 1, a["z"], a["w"], a["eps"],
+                                            a["out"], None, a["ms"])
+
+    assert call(D=64) == UNSUPPORTED
+    assert call(Nqk=3) == INVALID
+    assert call(z=None) == INVALID                           # the gate is required
+    assert call(z=addr["z"] + 4) == INVALID
+    assert call(w=addr["w"] + 4) == INVALID
+    assert call(eps=-1.0) == INVALID
+    assert call(eps=float("nan")) == INVALID
+    assert call(out=addr["z"]) == INVALID                    # output over the gate
+    assert call(s_out=addr["z"]) == INVALID                  # state over the gate
+    assert call(q=None) == INVALID
+    ms = ctypes.c_float(1.0)
+    assert call(N=0, z=None, ms=ctypes.byref(ms)) == OK and ms.value == 0.0

@@ -1,0 +1,236 @@
+"""GPU parity of the gated RMSNorm (Qwen3-Next blog post, RMSNormGated in
+sections 1 and 6) against the fp64 oracle, through the C ABI: the standalone
+``gdr_gated_rmsnorm`` on the rule's output rows and the decode step with the
+norm fused behind it (``gdr_recurrent_step_gated``).
+
+Tolerances as for the rule (relative L2 1e-4 for float32, 1e-2 for bf16), over
+the whole tensor and per row; the standalone norm is also held to a few bf16
+rounding steps per element, since it is one rounding away from the oracle.
+"""
+import numpy as np
+import pytest
+
+import gated_deltanet_chunked_amd as gdr
+import oracle
+from gated_deltanet_chunked_amd.inputs import config_inputs, make_gate, make_inputs
+from tests.gpu_util import SCALE, TOL, device_tensors, oracle_full, rel_l2, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    gdr.load()
+    yield
+    torch.cuda.synchronize()
+
+
+def _dev(a, dtype):
+    import torch
+    if a is None:
+        return None
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device="cuda:0", dtype=dt).contiguous()
+
+
+def _rows_rel(got, ref):
+    """Relative L2 error of every row (last dimension) separately."""
+    g = got.reshape(-1, got.shape[-1])
+    r = ref.reshape(-1, ref.shape[-1])
+    num = np.sqrt(((g - r) ** 2).sum(-1))
+    den = np.sqrt((r ** 2).sum(-1))
+    return np.where(den > 0, num / np.where(den > 0, den, 1), num)
+
+
+def _check(name, got, ref, tol):
+    assert np.isfinite(got).all(), f"{name}: non-finite values"
+    err = rel_l2(got, ref)
+    worst = float(_rows_rel(got, ref).max()) if got.size else 0.0
+    print(f"{name}: rel L2 {err:.3e}, worst row {worst:.3e} (tolerance {tol:.0e})")
+    assert err <= tol and worst <= tol, f"{name}: {err:.3e} / {worst:.3e} > {tol:.0e}"
+
+
+def _x(shape, dtype, seed):
+    from gated_deltanet_chunked_amd.inputs import round_to_bf16
+    rng = np.random.default_rng(seed)
+    # rows of different magnitudes, as the rule's outputs have
+    x = (rng.standard_normal(shape) * rng.uniform(0.01, 3.0, shape[:-1] + (1,))).astype(np.float32)
+    return round_to_bf16(x) if dtype == "bf16" else x
+
+
+# ---------------------------------------------------------------- standalone
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("rows", [1, 17, 1000, 4133])
+@pytest.mark.parametrize("weight", [True, False])
+def test_gated_rmsnorm_ragged_rows(dtype, rows, weight):
+    """Row counts that leave the grid's second row pass partly empty."""
+    import torch
+    x = _x((rows, 128), dtype, seed=rows)
+    z, w = make_gate((rows, 128), dtype=dtype, seed=rows + 1, weight=weight)
+    y = gdr.gated_rmsnorm(_dev(x, dtype), _dev(z, dtype), _dev(w, dtype))
+    torch.cuda.synchronize()
+    ref = oracle.gated_rmsnorm(x, z, w)
+    got = to_f64(y)
+    _check(f"norm {dtype} rows={rows} weight={weight}", got, ref, TOL[dtype])
+    if dtype == "bf16":
+        # one bf16 rounding of the fp32 result: within 2^-8 of |ref| per element
+        assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-30)
+    else:
+        assert np.all(np.abs(got - ref) <= 1e-5 * np.abs(ref) + 1e-6)
+
+
+def test_gated_rmsnorm_in_place_and_nd():
+    """out = x (in place) on a [T, Nv, 128] tensor, bf16, the chunk output's
+    layout; equal to the out-of-place call bit for bit."""
+    import torch
+    T, Nv = 300, 8
+    x = _x((T, Nv, 128), "bf16", seed=5)
+    z, w = make_gate((T, Nv, 128), seed=6)
+    xd, zd, wd = _dev(x, "bf16"), _dev(z, "bf16"), _dev(w, "bf16")
+    y = gdr.gated_rmsnorm(xd, zd, wd)
+    y2 = gdr.gated_rmsnorm(xd, zd, wd, out=xd)
+    torch.cuda.synchronize()
+    assert y2.data_ptr() == xd.data_ptr()
+    assert torch.equal(y, xd)
+    _check("norm in place", to_f64(xd), oracle.gated_rmsnorm(x, z, w), TOL["bf16"])
+
+
+def test_gated_rmsnorm_extremes():
+    """Zero rows give zeros (eps keeps the root positive); z = -30 gives
+    SiLU ~ -2.8e-12 (no overflow in exp(-z)), z = 30 gives SiLU = z; with
+    eps = 0 a scaled row gives the same result."""
+    import torch
+    x = _x((4, 128), "f32", seed=7)
+    x[0] = 0.0
+    z = np.zeros((4, 128), np.float32)
+    z[1] = -30.0
+    z[2] = 30.0
+    z[3] = np.linspace(-8, 8, 128)
+    y = to_f64(gdr.gated_rmsnorm(_dev(x, "f32"), _dev(z, "f32"), None))
+    torch.cuda.synchronize()
+    ref = oracle.gated_rmsnorm(x, z)
+    assert np.all(y[0] == 0.0)
+    assert np.allclose(y[1:], ref[1:], rtol=1e-5, atol=1e-30)
+    y0 = to_f64(gdr.gated_rmsnorm(_dev(x[1:], "f32"), _dev(z[1:], "f32"), None, eps=0.0))
+    y1 = to_f64(gdr.gated_rmsnorm(_dev(4 * x[1:], "f32"), _dev(z[1:], "f32"), None, eps=0.0))
+    torch.cuda.synchronize()
+    # a power-of-two scale cancels up to the root's rounding
+    assert np.allclose(y0, y1, rtol=1e-6, atol=0)
+
+
+def test_gated_rmsnorm_zero_rows():
+    import torch
+    e = torch.empty((0, 4, 128), dtype=torch.bfloat16, device="cuda:0")
+    y = gdr.gated_rmsnorm(e, e.clone())
+    assert y.shape == (0, 4, 128)
+
+
+def test_gated_rmsnorm_full_size_sampled():
+    """The long-context workload's output shape, T = 32768 x Nv = 32 rows of
+    bf16, in the launch configuration the benchmark times; checked on every
+    row against the oracle computed on a sample of 4096 rows, and in full
+    against float32 torch arithmetic on the device."""
+    import torch
+    T, Nv = 32768, 32
+    g = torch.Generator(device="cuda:0").manual_seed(9)
+    x = torch.randn((T, Nv, 128), device="cuda:0", generator=g).to(torch.bfloat16)
+    z = (2 * torch.randn((T, Nv, 128), device="cuda:0", generator=g)).to(torch.bfloat16)
+    w = (0.5 + torch.rand(128, device="cuda:0", generator=g)).to(torch.bfloat16)
+    y = gdr.gated_rmsnorm(x, z, w)
+    torch.cuda.synchronize()
+    rows = np.random.default_rng(10).choice(T * Nv, 4096, replace=False)
+    xs = to_f64(x.reshape(-1, 128)[rows])
+    zs = to_f64(z.reshape(-1, 128)[rows])
+    ref = oracle.gated_rmsnorm(xs, zs, to_f64(w))
+    _check("norm full size, sampled rows", to_f64(y.reshape(-1, 128)[rows]), ref, TOL["bf16"])
+    # every row: each element within two bf16 steps of an fp32 evaluation
+    xf, zf = x.float(), z.float()
+    yf = xf * torch.rsqrt(xf.pow(2).mean(-1, keepdim=True) + 1e-6) * w.float() * (zf * torch.sigmoid(zf))
+    d = (y.float() - yf).abs()
+    assert bool((d <= 2.0 ** -7 * yf.abs() + 1e-30).all())
+
+
+# -------------------------------------------------------- chunk output + norm
+
+
+def test_chunk_fwd_then_gated_rmsnorm():
+    """The prefill order of the blog's section 6: the chunkwise rule, its
+    bf16 output, then the norm with the gate, against the oracle's recurrence
+    cast to bf16 and normed (ragged sequences, several chunks)."""
+    import torch
+    inp = make_inputs([300, 1, 129, 700], 2, 4, dtype="bf16", seed=41)
+    t = device_tensors(inp)
+    out, _ = gdr.chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], t["cu"], t["state_in"],
+                           scale=SCALE, want_state=False)
+    z, w = make_gate(tuple(out.shape), seed=42)
+    y = gdr.gated_rmsnorm(out, _dev(z, "bf16"), _dev(w, "bf16"), out=out)
+    torch.cuda.synchronize()
+    ro, _ = oracle_full(inp)
+    ref = oracle.gated_rmsnorm(oracle.round_bf16(ro), z, w)
+    _check("chunk + norm", to_f64(y), ref, TOL["bf16"])
+
+
+# ------------------------------------------------------------ decode, fused
+
+
+def _gated_step(inp, z, w, in_place=True):
+    import torch
+    t = device_tensors(inp)
+    s = t["state_in"].clone()
+    s_out = s if in_place else torch.empty_like(s)
+    y = gdr.recurrent_step_gated(t["q"], t["k"], t["v"], t["g"], t["beta"], s, _dev(z, inp.dtype),
+                                 _dev(w, inp.dtype), state_out=s_out, scale=SCALE)
+    torch.cuda.synchronize()
+    return y, s_out, t
+
+
+@pytest.mark.parametrize("in_place", [True, False])
+@pytest.mark.parametrize("weight", [True, False])
+def test_decode_gated_config(in_place, weight):
+    """The decode workload (256 sequences, Nqk=16, Nv=32, bf16) with the norm
+    fused: against the oracle's gated step; the state is the plain step's,
+    bit for bit."""
+    import torch
+    inp = config_inputs(4)
+    z, w = make_gate((inp.N, inp.Nv, 128), seed=43, weight=weight)
+    y, s_out, t = _gated_step(inp, z, w, in_place)
+    ref, rs = oracle.recurrent_step_gated(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.state_in, z, w,
+                                          SCALE, out_bf16=True)
+    _check(f"decode gated (weight={weight})", to_f64(y), ref, TOL["bf16"])
+    assert rel_l2(to_f64(s_out), rs) <= TOL["bf16"]
+    s2 = t["state_in"].clone()
+    o_plain = gdr.recurrent_step(t["q"], t["k"], t["v"], t["g"], t["beta"], s2, scale=SCALE)
+    torch.cuda.synchronize()
+    assert torch.equal(s2, s_out)
+    # the fused norm and the standalone norm of the plain output agree
+    y2 = gdr.gated_rmsnorm(o_plain, _dev(z, "bf16"), _dev(w, "bf16"))
+    torch.cuda.synchronize()
+    d = (y.float() - y2.float()).abs()
+    assert bool((d <= 2.0 ** -7 * y2.float().abs() + 1e-30).all())
+
+
+def test_decode_gated_fp32():
+    inp = make_inputs([1] * 5, 1, 3, dtype="f32", seed=44, state_std=1.0)
+    z, w = make_gate((inp.N, inp.Nv, 128), dtype="f32", seed=45)
+    y, s_out, _ = _gated_step(inp, z, w)
+    ref, rs = oracle.recurrent_step_gated(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.state_in, z, w,
+                                          SCALE)
+    _check("decode gated fp32", to_f64(y), ref, TOL["f32"])
+    assert rel_l2(to_f64(s_out), rs) <= TOL["f32"]
+
+
+def test_decode_gated_empty():
+    import torch
+    inp = make_inputs([1], 1, 2, dtype="bf16", seed=46)
+    t = device_tensors(inp)
+    e = lambda *s: torch.empty(s, dtype=torch.bfloat16, device="cuda:0")
+    st = torch.empty((0, 2, 128, 128), device="cuda:0")
+    y = gdr.recurrent_step_gated(e(0, 1, 128), e(0, 1, 128), e(0, 2, 128),
+                                 t["g"][:0].contiguous(), t["beta"][:0].contiguous(), st,
+                                 e(0, 2, 128), None)
+    assert y.shape == (0, 2, 128)
