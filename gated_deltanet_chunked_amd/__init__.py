@@ -25,7 +25,7 @@ CHUNK = 128
 D = 128
 
 STATUS = {0: "GDR_OK", -1: "GDR_ERR_INVALID_ARGUMENT", -2: "GDR_ERR_UNSUPPORTED",
-          -3: "GDR_ERR_WORKSPACE_TOO_SMALL", -4: "GDR_ERR_HIP"}
+          -3: "GDR_ERR_WORKSPACE_TOO_SMALL", -4: "GDR_ERR_HIP", -5: "GDR_ERR_CONTRACT"}
 
 _lib = None
 
@@ -92,6 +92,10 @@ def load(path: str = LIB_PATH):
                                              ctypes.c_int, f32, u32, vp, vp, f32, vp, vp,
                                              ctypes.POINTER(ctypes.c_float)]
     lib.gdr_recurrent_step_gated.restype = ctypes.c_int
+    lib.gdr_set_debug.argtypes = [ctypes.c_int]
+    lib.gdr_set_debug.restype = ctypes.c_int
+    lib.gdr_debug_broken.argtypes = []
+    lib.gdr_debug_broken.restype = u32
     lib.gdr_status_string.argtypes = [ctypes.c_int]
     lib.gdr_status_string.restype = ctypes.c_char_p
     lib.gdr_version.argtypes = []
@@ -533,3 +537,16 @@ def recurrent_step_gated(q, k, v, g, beta, state_in, z, weight=None, *, state_ou
     if timings is not None:
         timings.append(("decode_gated", float(ms.value)))
     return out
+
+
+def set_debug(on: bool) -> bool:
+    """Switch the library's device-side contract checks on or off
+    (``gdr_set_debug``); returns the previous setting."""
+    return bool(load().gdr_set_debug(1 if on else 0))
+
+
+def debug_broken() -> int:
+    """Bits of the contracts the calling thread's last checked call found
+    broken (``gdr_debug_broken``): 1 cu[0] != 0, 2 cu decreases, 4 cu[N] != T,
+    8 a gate is positive or not finite."""
+    return int(load().gdr_debug_broken())

@@ -20,7 +20,7 @@ LIB = os.path.join(HERE, "libgdr.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["gdr_api.hip", "gdr_table.hip", "gdr_intra.hip", "gdr_intra_bf16.hip", "gdr_inter.hip", "gdr_inter_bf16.hip", "gdr_decode.hip",
-           "gdr_conv.hip", "gdr_norm.hip",
+           "gdr_conv.hip", "gdr_norm.hip", "gdr_debug.hip",
            "gdr_validate.cpp"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

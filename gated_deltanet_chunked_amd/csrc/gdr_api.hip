@@ -105,6 +105,14 @@ gdr_status run_chunk(const ChunkArgs& a, hipStream_t st, Recorder& rec) {
   return GDR_OK;
 }
 
+// With debug checks on: cu_seqlens and the gates, checked on the device
+// before any other launch (the call then waits for the check).
+gdr_status chunk_contract(const ChunkArgs& a, hipStream_t st) {
+  if (!debug_enabled()) return GDR_OK;
+  uint32_t broken = 0u;
+  return debug_check(a.cu_seqlens, a.N, a.T, a.g, static_cast<int64_t>(a.T) * a.Nv, st, &broken);
+}
+
 gdr_status dispatch_chunk(const ChunkArgs& a, hipStream_t st, Recorder& rec) {
   if (a.dtype == GDR_BF16) return run_chunk<__bf16>(a, st, rec);
   return run_chunk<float>(a, st, rec);
@@ -128,7 +136,9 @@ extern "C" gdr_status gdr_chunk_fwd(const void* q, const void* k, const void* v,
                                     size_t workspace_bytes, void* stream) {
   ChunkArgs a{q, k, v, g, beta, state_in, cu_seqlens, N, T, Nqk, Nv, D, dtype, scale, flags,
               out, state_out, workspace, workspace_bytes};
-  const gdr_status s = validate_chunk(a);
+  gdr_status s = validate_chunk(a);
+  if (s != GDR_OK) return s;
+  s = chunk_contract(a, static_cast<hipStream_t>(stream));
   if (s != GDR_OK) return s;
   Recorder none;
   return dispatch_chunk(a, static_cast<hipStream_t>(stream), none);
@@ -148,6 +158,8 @@ extern "C" gdr_status gdr_chunk_fwd_timed(const void* q, const void* k, const vo
   gdr_status s = validate_chunk(a);
   if (s != GDR_OK) return s;
   if (!kernel_ms || !kernel_kind || !n || max_kernels < 0) return GDR_ERR_INVALID_ARGUMENT;
+  s = chunk_contract(a, static_cast<hipStream_t>(stream));
+  if (s != GDR_OK) return s;
   const int32_t need = launches_needed(plan_workspace(T, N, Nqk, Nv, dtype), N);
   // more launches than the caller's arrays hold: the span alone is timed
   const bool span_only = need > max_kernels;
@@ -235,6 +247,8 @@ extern "C" gdr_status gdr_chunk_fwd_no_alloc(const void* q, const void* k, const
               out, state_out, ws, static_cast<size_t>(kScratchBytes), false, kScratchBytes};
   s = validate_chunk(a);
   if (s != GDR_OK) return s;
+  s = chunk_contract(a, static_cast<hipStream_t>(stream));
+  if (s != GDR_OK) return s;
   Recorder none;
   return dispatch_chunk(a, static_cast<hipStream_t>(stream), none);
 }
@@ -273,6 +287,11 @@ gdr_status step_entry(const StepArgs& a, hipStream_t st, float* kernel_ms) {
   if (s != GDR_OK) return s;
   if (kernel_ms) *kernel_ms = 0.0f;
   if (a.N == 0) return GDR_OK;
+  if (debug_enabled()) {
+    uint32_t broken = 0u;
+    s = debug_check(nullptr, a.N, 0, a.g, static_cast<int64_t>(a.N) * a.Nv, st, &broken);
+    if (s != GDR_OK) return s;
+  }
   if (!kernel_ms) return run_step(a, st, LaunchEvents{});
   EventPairs pairs;
   if (!pairs.create(1)) return GDR_ERR_HIP;
@@ -369,6 +388,8 @@ extern "C" gdr_status gdr_recurrent_multi(const void* q, const void* k, const vo
   gdr_status s = validate_chunk(a);
   if (s != GDR_OK) return s;
   if (kernel_ms) *kernel_ms = 0.0f;
+  s = chunk_contract(a, static_cast<hipStream_t>(stream));
+  if (s != GDR_OK) return s;
   if (T == 0 && !state_out) return GDR_OK;   // nothing to write
   EventPairs pairs;
   LaunchEvents ev{};
@@ -445,10 +466,15 @@ extern "C" gdr_status gdr_conv_prefill(const void* mixed_qkv, const void* conv_s
                                        void* stream, float* kernel_ms) {
   ConvPrefillCheck c{mixed_qkv, conv_state_in, conv_state_out, conv_weight, conv_bias, conv_k,
                      a, b, A_log, dt_bias, cu_seqlens, N, T, Nqk, Nv, D, dtype, q, k, v, g, beta};
-  const gdr_status s = validate_conv_prefill(c);
+  gdr_status s = validate_conv_prefill(c);
   if (s != GDR_OK) return s;
   if (kernel_ms) *kernel_ms = 0.0f;
   if (T == 0 && !conv_state_out) return GDR_OK;
+  if (debug_enabled()) {
+    uint32_t broken = 0u;
+    s = debug_check(cu_seqlens, N, T, nullptr, 0, static_cast<hipStream_t>(stream), &broken);
+    if (s != GDR_OK) return s;
+  }
   EventPairs pairs;
   LaunchEvents e0{}, e1{};
   if (kernel_ms) {
@@ -494,6 +520,7 @@ extern "C" const char* gdr_status_string(gdr_status s) {
     case GDR_ERR_UNSUPPORTED: return "unsupported size, dtype or flag";
     case GDR_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
     case GDR_ERR_HIP: return "HIP runtime error";
+    case GDR_ERR_CONTRACT: return "device values break the contract (debug checks)";
   }
   return "unknown status";
 }

@@ -252,38 +252,46 @@ struct Pieces {
   }
 };
 
-// Slot BASE scaled in place: element (r, c) times f[c].
+// Slot BASE scaled in place: element (r, c) times f[c].  All eight pieces
+// are read before the first is written back, so the reads are in flight
+// together (one LDS round trip instead of eight).
 template <uint32_t BASE>
 __device__ __forceinline__ void scale_cols(Lds& s, const Lane& L, const float* f) {
   const uint32_t c0 = (threadIdx.x & 15u) * 8u;
   const f32x4 f0 = *reinterpret_cast<const f32x4*>(f + c0);
   const f32x4 f1 = *reinterpret_cast<const f32x4*>(f + c0 + 4);
+  u32x4 raw[8];
+#pragma unroll
+  for (int it = 0; it < 8; ++it)
+    raw[it] = *reinterpret_cast<const u32x4*>(lds_m(s) + BASE + L.stg + 4096u * it);
 #pragma unroll
   for (int it = 0; it < 8; ++it) {
-    char* p = lds_m(s) + BASE + L.stg + 4096u * it;
-    u32x4 raw = *reinterpret_cast<const u32x4*>(p);
-    bf* e = reinterpret_cast<bf*>(&raw);
+    bf* e = reinterpret_cast<bf*>(&raw[it]);
 #pragma unroll
     for (int x = 0; x < 4; ++x) e[x] = (bf)((float)e[x] * f0[x]);
 #pragma unroll
     for (int x = 0; x < 4; ++x) e[4 + x] = (bf)((float)e[4 + x] * f1[x]);
-    *reinterpret_cast<u32x4*>(p) = raw;
+    *reinterpret_cast<u32x4*>(lds_m(s) + BASE + L.stg + 4096u * it) = raw[it];
   }
 }
 
-// Slot BASE scaled in place: element (r, c) times f[r].
+// Slot BASE scaled in place: element (r, c) times f[r]; reads first, as above.
 template <uint32_t BASE>
 __device__ __forceinline__ void scale_rows(Lds& s, const Lane& L, const float* f) {
   const uint32_t r0 = threadIdx.x >> 4;
+  u32x4 raw[8];
+  float fr[8];
 #pragma unroll
   for (int it = 0; it < 8; ++it) {
-    char* p = lds_m(s) + BASE + L.stg + 4096u * it;
-    const float fr = f[r0 + 16 * it];
-    u32x4 raw = *reinterpret_cast<const u32x4*>(p);
-    bf* e = reinterpret_cast<bf*>(&raw);
+    raw[it] = *reinterpret_cast<const u32x4*>(lds_m(s) + BASE + L.stg + 4096u * it);
+    fr[it] = f[r0 + 16 * it];
+  }
 #pragma unroll
-    for (int x = 0; x < 8; ++x) e[x] = (bf)((float)e[x] * fr);
-    *reinterpret_cast<u32x4*>(p) = raw;
+  for (int it = 0; it < 8; ++it) {
+    bf* e = reinterpret_cast<bf*>(&raw[it]);
+#pragma unroll
+    for (int x = 0; x < 8; ++x) e[x] = (bf)((float)e[x] * fr[it]);
+    *reinterpret_cast<u32x4*>(lds_m(s) + BASE + L.stg + 4096u * it) = raw[it];
   }
 }
 
@@ -704,6 +712,13 @@ __global__ __launch_bounds__(256, 2) void intra_bf16_kernel(
     f32x4 acc[4][4];
     zero(acc);
     gemm64<kT1, true, kT0, false, false>(acc, s, L);
+    // q is converted only here: without this the compiler hoists the
+    // conversions of the first pieces into phase 9, whose scalings then
+    // wait for the loads
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) asm volatile("" : "+v"(qx[i][jj]));
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       const float qsr = s.qs[n0 + 16 * jj + r16];

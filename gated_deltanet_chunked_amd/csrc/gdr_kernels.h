@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/gdr.h"
+
 namespace gdr {
 
 // Optional timing of one launch: events recorded by the runtime at the
@@ -94,6 +96,14 @@ void launch_decode(const Tin* q, const Tin* k, const Tin* v, const float* g, con
                    const St* state_in, St* state_out, int32_t N, int32_t Nqk, int32_t Nv,
                    float scale, int norm, Tin* out, hipStream_t stream, LaunchEvents ev = {},
                    const Tin* gate_z = nullptr, const Tin* gate_w = nullptr, float gate_eps = 0.f);
+
+// Debug checks of device-side values (gdr_debug.hip): on when GDR_DEBUG is
+// set in the environment or after gdr_set_debug(1).  debug_check runs one
+// kernel over cu_seqlens (may be NULL) and ng gates and waits for it; it
+// returns GDR_ERR_CONTRACT with the broken contracts' bits in *broken.
+bool debug_enabled();
+gdr_status debug_check(const int32_t* cu, int32_t N, int32_t T, const float* g, int64_t ng,
+                       hipStream_t st, uint32_t* broken);
 
 // The gated RMSNorm y = x / rms(x) * w * SiLU(z) over rows of kD values; x may
 // equal y.  w NULL: ones.

@@ -44,8 +44,14 @@
  *   - Errors are reported by the returned status; nothing aborts or prints.
  *     Argument validation happens before any launch, and on a validation
  *     error no output is touched.  Values that live only on the device
- *     (cu_seqlens being non-decreasing with cu[N] = T, g <= 0) are the
- *     caller's contract and are not checked.
+ *     (cu_seqlens starting at 0, non-decreasing, with cu[N] = T; every g
+ *     finite and <= 0) are the caller's contract and are not checked by
+ *     default.  With debug checks on (GDR_DEBUG set to anything but "" or
+ *     "0" in the environment when the library first looks, or
+ *     gdr_set_debug(1)), every call that reads them first runs one checking
+ *     kernel and waits for it, and returns GDR_ERR_CONTRACT, with no output
+ *     touched, if a value breaks the contract (gdr_debug_broken says which).
+ *     Checked calls block the host, so they cannot be captured in a graph.
  */
 #ifndef GDR_H
 #define GDR_H
@@ -64,7 +70,8 @@ typedef enum {
     GDR_ERR_INVALID_ARGUMENT = -1,   /* bad size, null pointer, misalignment, ... */
     GDR_ERR_UNSUPPORTED = -2,        /* D != 128, Nv > 32768, unknown dtype or flag */
     GDR_ERR_WORKSPACE_TOO_SMALL = -3,
-    GDR_ERR_HIP = -4                 /* a HIP runtime call or launch failed */
+    GDR_ERR_HIP = -4,                /* a HIP runtime call or launch failed */
+    GDR_ERR_CONTRACT = -5            /* debug checks on: a device value breaks the contract */
 } gdr_status;
 
 /* Normalise q and k by their L2 norm inside the call (the blog's
@@ -368,6 +375,21 @@ gdr_status gdr_recurrent_step_gated(const void* q, const void* k, const void* v,
                                     gdr_dtype dtype, float scale, uint32_t flags,
                                     const void* z, const void* weight, float norm_eps,
                                     void* out, void* stream, float* kernel_ms);
+
+/*
+ * Debug checks of the device-side contract (see the conventions above).
+ * mode 1 switches them on, 0 off, any other value only queries; returns the
+ * state before the call (1 on, 0 off).  The setting is process-wide.
+ */
+int gdr_set_debug(int mode);
+
+/*
+ * Which contracts the calling thread's last checked call found broken
+ * (0: none, or no checked call yet): bit 0 cu_seqlens[0] != 0, bit 1
+ * cu_seqlens decreases somewhere, bit 2 cu_seqlens[N] != T, bit 3 a gate g
+ * is positive, infinite or NaN.
+ */
+uint32_t gdr_debug_broken(void);
 
 /* A static, human-readable name for a status code. */
 const char* gdr_status_string(gdr_status s);

@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol():
 def test_version_and_status_strings():
     lib = gdr.load()
     assert lib.gdr_version().startswith(b"libgdr")
-    for code in (0, -1, -2, -3, -4):
+    for code in (0, -1, -2, -3, -4, -5):
         assert lib.gdr_status_string(code)
     assert lib.gdr_status_string(7) == b"unknown status"
 
@@ -397,3 +397,21 @@ def test_recurrent_step_gated_validates_before_launching():
     assert call(q=None) == INVALID
     ms = ctypes.c_float(1.0)
     assert call(N=0, z=None, ms=ctypes.byref(ms)) == OK and ms.value == 0.0
+
+
+def test_debug_switch_and_contract_status():
+    """gdr_set_debug toggles the device-side contract checks and reports the
+    previous setting; the contract status has its own name.  No GPU call."""
+    lib = gdr.load()
+    before = lib.gdr_set_debug(-1)
+    try:
+        assert lib.gdr_set_debug(1) == before
+        assert lib.gdr_set_debug(-1) == 1
+        assert lib.gdr_set_debug(0) == 1
+        assert lib.gdr_set_debug(7) == 0          # any other value only queries
+        assert lib.gdr_set_debug(-1) == 0
+    finally:
+        lib.gdr_set_debug(before)
+    assert lib.gdr_status_string(-5) == b"device values break the contract (debug checks)"
+    assert gdr.STATUS[-5] == "GDR_ERR_CONTRACT"
+    assert lib.gdr_debug_broken() == 0            # no checked call in this thread
