@@ -246,9 +246,11 @@ __device__ __forceinline__ int frag_off(int row, int k) {
   const int lane = (row & 15) + 16 * ((k % K) / E);
   return blk * 64 * E + lane * E + (k % E);
 }
-// block (vb, wave half, 16-row tile i, 16-column tile t) of 64 lanes x 4 values
+// block (vb, wave half, 16-row tile i, 16-column tile t) of 64 lanes x 4 values;
+// t is outside wh and i, so the blocks of the 16 state rows 32 vb + 16 t .. are
+// one contiguous 4 KiB run (and those of 32 vb .. one 8 KiB run)
 __device__ __forceinline__ int pass_blk(int vb, int wh, int i, int t) {
-  return (((vb * 2 + wh) * 4 + i) * 2 + t) * 256;
+  return (((vb * 2 + t) * 2 + wh) * 4 + i) * 256;
 }
 __device__ __forceinline__ int bm_off(int v, int d) {
   return pass_blk(v >> 5, d >> 6, (d & 63) >> 4, (v & 31) >> 4) + ((v & 15) + 16 * ((d & 15) >> 2)) * 4 +

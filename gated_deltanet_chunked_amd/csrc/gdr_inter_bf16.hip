@@ -6,12 +6,13 @@
 // each chunk of a sequence, in order,
 //   O      = Qp S^T + Ou                        (the chunk's output rows)
 //   S_next = exp(gc_last) S + S M' + Bm         (the state after the chunk)
-// with S in R^{Dv x Dk}; a workgroup owns BV = 32 rows of S of one (sequence,
-// value head), four workgroups per (sequence, head) on one XCD.
+// with S in R^{Dv x Dk}; a workgroup owns BV = 16 rows of S of one (sequence,
+// value head), eight workgroups per (sequence, head) on one XCD, so a single
+// sequence of 32 heads fills all 256 compute units.
 //
-// What bounds a chunk step is the compute unit's vector-memory path: per
-// chunk a workgroup needs about 80 KB of operands (all of Mt and Qp, its
-// slices of Bm and Ou).  A wave issues its instructions in order, so a wave
+// What bounds a chunk step is how early each chunk's operands arrive: per
+// chunk a workgroup needs its full Mt and Qp (32 KiB each) and its slices of
+// Bm and Ou (4 KiB each).  A wave issues its instructions in order, so a wave
 // that issues loads stalls while the path is busy.  Here the waves on the
 // serial chain never issue one:
 //   waves 0, 1 (state):   (S M')^T for 64 key rows each, and the update of S
@@ -20,11 +21,11 @@
 //                         stores; Qp and Ou prefetched two chunks ahead into a
 //                         ring of register sets;
 //   waves 6, 7 (loaders): copy each chunk's Mt and the workgroup's slice of
-//                         Bm into a three-deep LDS ring, two chunks ahead,
+//                         Bm into a four-deep LDS ring, three chunks ahead,
 //                         with direct global-to-LDS loads, then wait for the
 //                         chunk the next step needs.
 // One barrier per chunk step hands over the ring slot and the bf16 copy of S
-// (double-buffered).
+// (double-buffered).  The ring takes 144 KiB of the 160 KiB of LDS.
 #include "gdr_device.h"
 #include "gdr_internal.h"
 #include "gdr_kernels.h"
@@ -33,13 +34,17 @@ namespace gdr {
 namespace {
 
 typedef __bf16 bf;
-constexpr int kBV = 32;                       // state rows per workgroup
+constexpr int kBV = 16;                       // state rows per workgroup
 constexpr int kMtBytes = 128 * 128 * 2;       // one chunk's Mt (32 KiB)
-constexpr int kBmBytes = kBV * 128 * 2;       // the workgroup's Bm slice (8 KiB)
-constexpr int kRing = 3;
+constexpr int kBmBytes = kBV * 128 * 2;       // the workgroup's Bm slice (4 KiB)
+constexpr int kRing = 4;
+constexpr int kDmaPerChunk = 16 + 2;          // 1 KiB pieces per loader wave per chunk
+// the loaders' waits count the pieces of the two chunks issued after the one
+// they wait for
+static_assert(2 * kDmaPerChunk == 36, "s_waitcnt vmcnt(36) below");
 
 struct InterLds {
-  char mt[kRing][kMtBytes];   // Mt of chunks c, c + 1, c + 2 (workspace fragment order)
+  char mt[kRing][kMtBytes];   // Mt of chunks c .. c + 3 (workspace fragment order)
   char bm[kRing][kBmBytes];   // the workgroup's Bm blocks (workspace order)
   bf s[2][kBV * 128];         // bf16 copy of the workgroup's rows of S, swizzled
   int2 tab[kMaxSegSlots];     // {first token, length} of the segment's chunks
@@ -117,7 +122,7 @@ __global__ __launch_bounds__(512, 1) void inter_bf16_kernel(
 
   if (w >= 6) {
     // ---------------- loaders: Mt blocks 16 lw .. 16 lw + 15 and Bm blocks
-    // 4 lw .. 4 lw + 3 of each chunk, two chunks ahead
+    // 2 lw, 2 lw + 1 of each chunk, three chunks ahead
     const int lw = w - 6;
     auto issue = [&](int c, int slot) {
       const char* m = reinterpret_cast<const char*>(mats(c));
@@ -126,25 +131,27 @@ __global__ __launch_bounds__(512, 1) void inter_bf16_kernel(
         const int bi = 16 * lw + k;
         dma16(m + bi * 1024, s.mt[slot] + bi * 1024, l);
       }
+      // the workgroup's 16 rows of Bm: one 4 KiB run (pass_blk in gdr_device.h)
       const char* bmv = reinterpret_cast<const char*>(mats(c) + 2 * 128 * 128) + vb * kBmBytes;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int bj = 4 * lw + k;
+      for (int k = 0; k < 2; ++k) {
+        const int bj = 2 * lw + k;
         dma16(bmv + bj * 1024, s.bm[slot] + bj * 1024, l);
       }
     };
     issue(cb, 0);
     issue(min(cb + 1, ce - 1), 1);
-    asm volatile("s_waitcnt vmcnt(20)" ::: "memory");   // chunk cb in LDS
+    issue(min(cb + 2, ce - 1), 2);
+    asm volatile("s_waitcnt vmcnt(36)" ::: "memory");   // chunk cb in LDS
     lds_barrier();                                         // tables, ring slot 0, S(cb)
-    int slot = 2;
+    int slot = 3;
     for (int c = cb; c < ce; ++c) {
-      // ring slot (c + 2) % 3 was read in step c - 1, which ended at the
+      // ring slot (c + 3) % 4 was read in step c - 1, which ended at the
       // last barrier; past the end the last chunk is loaded again, so every
       // step issues the same loads and the wait below stays exact
-      issue(min(c + 2, ce - 1), slot);
+      issue(min(c + 3, ce - 1), slot);
       slot = slot == kRing - 1 ? 0 : slot + 1;
-      asm volatile("s_waitcnt vmcnt(20)" ::: "memory");   // chunk c + 1 in LDS
+      asm volatile("s_waitcnt vmcnt(36)" ::: "memory");   // chunk c + 1 in LDS
       lds_barrier();
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -152,61 +159,53 @@ __global__ __launch_bounds__(512, 1) void inter_bf16_kernel(
   }
 
   if (w < 2) {
-    // ---------------- state waves: rows v0 .. v0 + 31 of S, key rows
+    // ---------------- state waves: rows v0 .. v0 + 15 of S, key rows
     // rb .. rb + 63 of the product (S M')^T
     const int rb = 64 * w;
-    f32x4 st[4][2];
+    f32x4 st[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        st[i][t] = zero4();
-        if (src)
-          st[i][t] = *reinterpret_cast<const f32x4*>(
-              src + sb + (size_t)(v0 + 16 * t + r16) * 128 + rb + 16 * i + 4 * q4);
-      }
+    for (int i = 0; i < 4; ++i) {
+      st[i] = zero4();
+      if (src)
+        st[i] = *reinterpret_cast<const f32x4*>(src + sb + (size_t)(v0 + r16) * 128 + rb + 16 * i +
+                                                4 * q4);
+    }
     auto put_s = [&](int buf) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          bf16x4 v;
-          v[0] = (bf)st[i][t][0]; v[1] = (bf)st[i][t][1]; v[2] = (bf)st[i][t][2]; v[3] = (bf)st[i][t][3];
-          *reinterpret_cast<bf16x4*>(s.s[buf] + Sw<bf>::at(16 * t + r16, rb + 16 * i + 4 * q4)) = v;
-        }
+      for (int i = 0; i < 4; ++i) {
+        bf16x4 v;
+        v[0] = (bf)st[i][0]; v[1] = (bf)st[i][1]; v[2] = (bf)st[i][2]; v[3] = (bf)st[i][3];
+        *reinterpret_cast<bf16x4*>(s.s[buf] + Sw<bf>::at(r16, rb + 16 * i + 4 * q4)) = v;
+      }
     };
     put_s(0);
     lds_barrier();
     int slot = 0, buf = 0;
     for (int c = cb; c < ce; ++c) {
       const float gC = s.gam[c - cb];
-      f32x4 acc[4][2];
+      f32x4 acc[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i][0] = acc[i][1] = zero4();
+      for (int i = 0; i < 4; ++i) acc[i] = zero4();
       const char* mt = s.mt[slot];
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const bf16x8 s0 = sw_frag<bf>(s.s[buf], r16, ks * 32 + 8 * q4);
-        const bf16x8 s1 = sw_frag<bf>(s.s[buf], 16 + r16, ks * 32 + 8 * q4);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           // block (key row block rb / 16 + i, k-step ks) of Mt: lane l's 8 values
           const bf16x8 a = *reinterpret_cast<const bf16x8*>(
               mt + (((rb >> 4) + i) * 4 + ks) * 1024 + l * 16);
-          acc[i][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, s0, acc[i][0], 0, 0, 0);
-          acc[i][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, s1, acc[i][1], 0, 0, 0);
+          acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, s0, acc[i], 0, 0, 0);
         }
       }
-      // S = exp(gc_last) S + S M' + Bm; this wave's Bm blocks are (wh = w, i, t)
-      const char* bmw = s.bm[slot] + w * 4096;
+      // S = exp(gc_last) S + S M' + Bm; this wave's Bm blocks are (wh = w, i)
+      const char* bmw = s.bm[slot] + w * 2048;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i) {
+        const bf16x4 x = *reinterpret_cast<const bf16x4*>(bmw + i * 512 + l * 8);
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const bf16x4 x = *reinterpret_cast<const bf16x4*>(bmw + (i * 2 + t) * 512 + l * 8);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) st[i][t][e] = gC * st[i][t][e] + acc[i][t][e] + (float)x[e];
-        }
+        for (int e = 0; e < 4; ++e) st[i][e] = gC * st[i][e] + acc[i][e] + (float)x[e];
+      }
       buf ^= 1;
       put_s(buf);
       slot = slot == kRing - 1 ? 0 : slot + 1;
@@ -215,19 +214,16 @@ __global__ __launch_bounds__(512, 1) void inter_bf16_kernel(
     if (dstS) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-          *reinterpret_cast<f32x4*>(dstS + sb + (size_t)(v0 + 16 * t + r16) * 128 + rb + 16 * i +
-                                    4 * q4) = st[i][t];
+        *reinterpret_cast<f32x4*>(dstS + sb + (size_t)(v0 + r16) * 128 + rb + 16 * i + 4 * q4) = st[i];
     }
     return;
   }
 
-  // ---------------- output waves: chunk rows rr0 .. rr0 + 31, all 32 state rows
+  // ---------------- output waves: chunk rows rr0 .. rr0 + 31, the 16 state rows
   const int ow = w - 2, rr0 = 32 * ow;
   struct Ops {
     bf16x8 a[2][4];     // rows rr0 + 16 i of Qp, k-step ks
-    bf16x4 x[2][2];     // Ou[r][v0 + 16 t + 4 q ..]
+    bf16x4 x[2];        // Ou[r][v0 + 4 q ..]
   };
   auto load_ops = [&](Ops& o, int c) {
     const bf* m = mats(c);
@@ -237,14 +233,13 @@ __global__ __launch_bounds__(512, 1) void inter_bf16_kernel(
       for (int ks = 0; ks < 4; ++ks)
         o.a[i][ks] = *reinterpret_cast<const bf16x8*>(
             m + 128 * 128 + ((((rr0 >> 4) + i) * 4 + ks) * 512) + l * 8);
-    // Ou blocks pass_blk(vb, r / 64, (r % 64) / 16, t) of 256 values, 4 per lane
+    // Ou blocks pass_blk(v0 / 32, r / 64, (r % 64) / 16, (v0 / 16) % 2) of 256
+    // values, 4 per lane
     const bf* ou = m + 3 * 128 * 128;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-        o.x[i][t] = *reinterpret_cast<const bf16x4*>(
-            ou + pass_blk(vb, rr0 >> 6, ((rr0 & 63) >> 4) + i, t) + l * 4);
+      o.x[i] = *reinterpret_cast<const bf16x4*>(
+          ou + pass_blk(vb >> 1, rr0 >> 6, ((rr0 & 63) >> 4) + i, vb & 1) + l * 4);
   };
   Ops ops[3];
   load_ops(ops[0], cb);
@@ -255,33 +250,27 @@ __global__ __launch_bounds__(512, 1) void inter_bf16_kernel(
     // the chunk two ahead (past the end, the last chunk again)
     load_ops(next, min(c + 2, ce - 1));
     const int2 e = s.tab[c - cb];
-    f32x4 acc[2][2];
+    f32x4 acc[2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) acc[i][0] = acc[i][1] = zero4();
+    for (int i = 0; i < 2; ++i) acc[i] = zero4();
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const bf16x8 s0 = sw_frag<bf>(s.s[buf], r16, ks * 32 + 8 * q4);
-      const bf16x8 s1 = sw_frag<bf>(s.s[buf], 16 + r16, ks * 32 + 8 * q4);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        acc[i][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(s0, o.a[i][ks], acc[i][0], 0, 0, 0);
-        acc[i][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(s1, o.a[i][ks], acc[i][1], 0, 0, 0);
-      }
+      for (int i = 0; i < 2; ++i)
+        acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(s0, o.a[i][ks], acc[i], 0, 0, 0);
     }
-    // acc[i][t] = (Qp S^T)[r][v .. v + 3], r = rr0 + 16 i + r16, v = 16 t + 4 q4;
+    // acc[i] = (Qp S^T)[r][v .. v + 3], r = rr0 + 16 i + r16, v = v0 + 4 q4;
     // rows past the chunk's end go to the discard line (the store count
     // stays fixed, so the memory waits of later steps stay exact)
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int r = rr0 + 16 * i + r16;
       bf* orow = r < e.y ? out + ((size_t)(e.x + r) * Nv + h) * 128 + v0 : discard;
+      bf16x4 v;
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        bf16x4 v;
-#pragma unroll
-        for (int x = 0; x < 4; ++x) v[x] = (bf)(acc[i][t][x] + (float)o.x[i][t][x]);
-        *reinterpret_cast<bf16x4*>(orow + 16 * t + 4 * q4) = v;
-      }
+      for (int x = 0; x < 4; ++x) v[x] = (bf)(acc[i][x] + (float)o.x[i][x]);
+      *reinterpret_cast<bf16x4*>(orow + 4 * q4) = v;
     }
     buf ^= 1;
     lds_barrier();

@@ -456,17 +456,17 @@ __device__ __forceinline__ void store_block(bf* dst, const f32x4 (&acc)[4][4], i
   if (LY == Lay::Frag)
     base = n0 * 128u + m0 * 16u + r16 * 8u + 128u * (q >> 1) + 4u * (q & 1u);
   else if (LY == Lay::Bm)
-    base = (n0 / 32) * 4096u + (m0 / 64) * 2048u + l * 4u;
+    base = (n0 / 32) * 4096u + (m0 / 64) * 1024u + l * 4u;
   else
-    base = (m0 / 32) * 4096u + (n0 / 64) * 2048u + l * 4u;
+    base = (m0 / 32) * 4096u + (n0 / 64) * 1024u + l * 4u;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       uint32_t off;
       if (LY == Lay::Frag) off = j * 2048u + (i >> 1) * 512u + (i & 1) * 256u;
-      else if (LY == Lay::Bm) off = (j >> 1) * 4096u + i * 512u + (j & 1) * 256u;
-      else off = (i >> 1) * 4096u + j * 512u + (i & 1) * 256u;
+      else if (LY == Lay::Bm) off = (j >> 1) * 4096u + (j & 1) * 2048u + i * 256u;
+      else off = (i >> 1) * 4096u + (i & 1) * 2048u + j * 256u;
       *reinterpret_cast<bf16x4*>(dst + base + off) =
           bf16x4{(bf)(sign * acc[i][j][0]), (bf)(sign * acc[i][j][1]), (bf)(sign * acc[i][j][2]),
                  (bf)(sign * acc[i][j][3])};
