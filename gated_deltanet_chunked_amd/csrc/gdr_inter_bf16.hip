@@ -12,7 +12,11 @@
 //
 // What bounds a chunk step is how early each chunk's operands arrive: per
 // chunk a workgroup needs its full Mt and Qp (32 KiB each) and its slices of
-// Bm and Ou (4 KiB each).  A wave issues its instructions in order, so a wave
+// Bm and Ou (4 KiB each), in the workspace orders the intra-chunk kernel
+// writes (store_block in gdr_intra_bf16.hip): Mt and Qp in matrix-core operand
+// order with the 32 k of a step permuted per lane group (k = 4q .. 4q + 3,
+// 16 + 4q .. 16 + 4q + 3), which the copy of S in LDS repeats, and Bm and Ou
+// as 16-byte pieces per lane.  A wave issues its instructions in order, so a wave
 // that issues loads stalls while the path is busy.  Here the waves on the
 // serial chain never issue one:
 //   waves 0, 1 (state):   (S M')^T for 64 key rows each, and the update of S
@@ -131,7 +135,7 @@ __global__ __launch_bounds__(512, 1) void inter_bf16_kernel(
         const int bi = 16 * lw + k;
         dma16(m + bi * 1024, s.mt[slot] + bi * 1024, l);
       }
-      // the workgroup's 16 rows of Bm: one 4 KiB run (pass_blk in gdr_device.h)
+      // the workgroup's 16 rows of Bm: one 4 KiB run
       const char* bmv = reinterpret_cast<const char*>(mats(c) + 2 * 128 * 128) + vb * kBmBytes;
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
@@ -170,12 +174,16 @@ __global__ __launch_bounds__(512, 1) void inter_bf16_kernel(
         st[i] = *reinterpret_cast<const f32x4*>(src + sb + (size_t)(v0 + r16) * 128 + rb + 16 * i +
                                                 4 * q4);
     }
+    // S's columns in the k order of the workspace's Mt and Qp (see the
+    // header): column rb + 16 i + 4 q4 + x goes to 16-byte chunk
+    // 4 ((rb + 16 i) / 32) + q4 of the row, half i % 2
     auto put_s = [&](int buf) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         bf16x4 v;
         v[0] = (bf)st[i][0]; v[1] = (bf)st[i][1]; v[2] = (bf)st[i][2]; v[3] = (bf)st[i][3];
-        *reinterpret_cast<bf16x4*>(s.s[buf] + Sw<bf>::at(r16, rb + 16 * i + 4 * q4)) = v;
+        const int col = (4 * ((rb >> 5) + (i >> 1)) + q4) * 8 + 4 * (i & 1);
+        *reinterpret_cast<bf16x4*>(s.s[buf] + Sw<bf>::at(r16, col)) = v;
       }
     };
     put_s(0);
@@ -198,13 +206,17 @@ __global__ __launch_bounds__(512, 1) void inter_bf16_kernel(
           acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, s0, acc[i], 0, 0, 0);
         }
       }
-      // S = exp(gc_last) S + S M' + Bm; this wave's Bm blocks are (wh = w, i)
+      // S = exp(gc_last) S + S M' + Bm; this wave's Bm blocks are (d / 64 = w,
+      // pair p): lane l's 8 values are tiles i = 2p and 2p + 1
       const char* bmw = s.bm[slot] + w * 2048;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bf16x4 x = *reinterpret_cast<const bf16x4*>(bmw + i * 512 + l * 8);
+      for (int p = 0; p < 2; ++p) {
+        const bf16x8 x = *reinterpret_cast<const bf16x8*>(bmw + p * 1024 + l * 16);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) st[i][e] = gC * st[i][e] + acc[i][e] + (float)x[e];
+        for (int e = 0; e < 4; ++e) {
+          st[2 * p][e] = gC * st[2 * p][e] + acc[2 * p][e] + (float)x[e];
+          st[2 * p + 1][e] = gC * st[2 * p + 1][e] + acc[2 * p + 1][e] + (float)x[4 + e];
+        }
       }
       buf ^= 1;
       put_s(buf);
@@ -223,7 +235,7 @@ __global__ __launch_bounds__(512, 1) void inter_bf16_kernel(
   const int ow = w - 2, rr0 = 32 * ow;
   struct Ops {
     bf16x8 a[2][4];     // rows rr0 + 16 i of Qp, k-step ks
-    bf16x4 x[2];        // Ou[r][v0 + 4 q ..]
+    bf16x8 x;           // Ou[rr0 + 16 i + r16][v0 + 4 q ..], i = 0 (first 4), 1
   };
   auto load_ops = [&](Ops& o, int c) {
     const bf* m = mats(c);
@@ -233,13 +245,8 @@ __global__ __launch_bounds__(512, 1) void inter_bf16_kernel(
       for (int ks = 0; ks < 4; ++ks)
         o.a[i][ks] = *reinterpret_cast<const bf16x8*>(
             m + 128 * 128 + ((((rr0 >> 4) + i) * 4 + ks) * 512) + l * 8);
-    // Ou blocks pass_blk(v0 / 32, r / 64, (r % 64) / 16, (v0 / 16) % 2) of 256
-    // values, 4 per lane
-    const bf* ou = m + 3 * 128 * 128;
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-      o.x[i] = *reinterpret_cast<const bf16x4*>(
-          ou + pass_blk(vb >> 1, rr0 >> 6, ((rr0 & 63) >> 4) + i, vb & 1) + l * 4);
+    // Ou: the workgroup's 16 columns, block rr0 / 32, 8 values per lane
+    o.x = *reinterpret_cast<const bf16x8*>(m + 3 * 128 * 128 + vb * 2048 + ow * 512 + l * 8);
   };
   Ops ops[3];
   load_ops(ops[0], cb);
@@ -269,7 +276,7 @@ __global__ __launch_bounds__(512, 1) void inter_bf16_kernel(
       bf* orow = r < e.y ? out + ((size_t)(e.x + r) * Nv + h) * 128 + v0 : discard;
       bf16x4 v;
 #pragma unroll
-      for (int x = 0; x < 4; ++x) v[x] = (bf)(acc[i][x] + (float)o.x[i][x]);
+      for (int x = 0; x < 4; ++x) v[x] = (bf)(acc[i][x] + (float)o.x[4 * i + x]);
       *reinterpret_cast<bf16x4*>(orow + 4 * q4) = v;
     }
     buf ^= 1;

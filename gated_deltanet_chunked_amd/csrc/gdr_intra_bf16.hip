@@ -8,8 +8,8 @@
 //   Qp = diag(exp(gc)) Q - R diag(beta exp(gc)) K              [l x Dk]
 //   Bm = V^T diag(beta) Z                                      [Dv x Dk]
 //   Ou = R diag(beta) V                                        [l x Dv]
-// in the workspace orders the chunk-serial pass reads (frag_off, bm_off,
-// ou_off in gdr_device.h), and exp(gc_last) of the chunk.
+// in the workspace orders the chunk-serial pass reads (store_block below),
+// and exp(gc_last) of the chunk.
 //
 // What differs from the fp32 kernel is how the work maps onto gfx950:
 //  * K, Q and V enter the matrix cores as the raw bf16 inputs (exact); the
@@ -443,33 +443,42 @@ __device__ __forceinline__ void invert_unit_upper(Lds& s) {
   merge_level<64>(s, w, l);
 }
 
-// Global store of a 64x64 accumulator block, transposed, in one of the state
-// pass's workspace orders: element (row n, column m) = sign * acc(m, n),
-// n = n0 + 16 j + r16, m = m0 + 16 i + 4 q .. (4 consecutive values).
+// Global store of a 64x64 accumulator block, transposed, in one of the bf16
+// state pass's workspace orders: element (row n, column m) = sign * acc(m, n),
+// n = n0 + 16 j + r16, m = m0 + 16 i + 4 q ..  In every order a lane's values
+// of two neighbouring 16-wide tiles form one 16-byte piece, so a lane stores
+// 8 pieces per matrix:
+//   Frag (Mt, Qp; rows n, k = m): 1 KiB block (n / 16, m / 32); lane
+//     (n % 16) + 16 ((m % 16) / 4) holds value m % 4 + 4 ((m % 32) / 16), i.e.
+//     lane group q holds k = {4q .. 4q + 3, 16 + 4q .. 16 + 4q + 3} of the
+//     32 k of a matrix-core step.  The state pass keeps its copy of S in the
+//     same k order (gdr_inter_bf16.hip), so both operands of its products
+//     pair the same k.
+//   Bm (rows v = n, columns d = m): 4 KiB per 16 rows v, then block
+//     (d / 64, (d % 64) / 32); lane (v % 16) + 16 ((d % 16) / 4) holds value
+//     d % 4 + 4 ((d % 32) / 16).
+//   Ou (rows r = n, columns v = m): 4 KiB per 16 columns v, then block r / 32;
+//     lane (r % 16) + 16 ((v % 16) / 4) holds value v % 4 + 4 ((r % 32) / 16).
 enum class Lay { Frag, Bm, Ou };
 template <Lay LY>
 __device__ __forceinline__ void store_block(bf* dst, const f32x4 (&acc)[4][4], int m0, int n0,
                                             float sign) {
-  const uint32_t l = threadIdx.x & 63u, r16 = l & 15u, q = l >> 4;
-  // lane part and per-tile constants of frag_off / bm_off / ou_off (gdr_device.h)
+  const uint32_t l = threadIdx.x & 63u;
   uint32_t base;
-  if (LY == Lay::Frag)
-    base = n0 * 128u + m0 * 16u + r16 * 8u + 128u * (q >> 1) + 4u * (q & 1u);
-  else if (LY == Lay::Bm)
-    base = (n0 / 32) * 4096u + (m0 / 64) * 1024u + l * 4u;
-  else
-    base = (m0 / 32) * 4096u + (n0 / 64) * 1024u + l * 4u;
+  if (LY == Lay::Frag) base = ((uint32_t)(n0 >> 4) * 4u + (uint32_t)(m0 >> 5)) * 512u + l * 8u;
+  else if (LY == Lay::Bm) base = (uint32_t)(n0 >> 4) * 2048u + (uint32_t)(m0 >> 6) * 1024u + l * 8u;
+  else base = (uint32_t)(m0 >> 4) * 2048u + (uint32_t)(n0 >> 5) * 512u + l * 8u;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      uint32_t off;
-      if (LY == Lay::Frag) off = j * 2048u + (i >> 1) * 512u + (i & 1) * 256u;
-      else if (LY == Lay::Bm) off = (j >> 1) * 4096u + (j & 1) * 2048u + i * 256u;
-      else off = (i >> 1) * 4096u + (i & 1) * 2048u + j * 256u;
-      *reinterpret_cast<bf16x4*>(dst + base + off) =
-          bf16x4{(bf)(sign * acc[i][j][0]), (bf)(sign * acc[i][j][1]), (bf)(sign * acc[i][j][2]),
-                 (bf)(sign * acc[i][j][3])};
+    for (int p = 0; p < 2; ++p) {
+      // Frag, Bm: column tiles i = 2p, 2p + 1 of row tile j = a;
+      // Ou: row tiles j = 2p, 2p + 1 of column tile i = a
+      const f32x4& x0 = LY == Lay::Ou ? acc[a][2 * p] : acc[2 * p][a];
+      const f32x4& x1 = LY == Lay::Ou ? acc[a][2 * p + 1] : acc[2 * p + 1][a];
+      *reinterpret_cast<bf16x8*>(dst + base + (uint32_t)a * 2048u + (uint32_t)p * 512u) =
+          bf16x8{(bf)(sign * x0[0]), (bf)(sign * x0[1]), (bf)(sign * x0[2]), (bf)(sign * x0[3]),
+                 (bf)(sign * x1[0]), (bf)(sign * x1[1]), (bf)(sign * x1[2]), (bf)(sign * x1[3])};
     }
 }
 
