@@ -10,14 +10,17 @@ are resident in HBM before the timed region starts:
     single-GPU workload), and
   * gdr_recurrent_step on the decode workload (256 sequences x 1 token, same
     heads, fp32 states updated in place).
-``value`` is the chunkwise forward's tokens/s from its GPU time: the span from
-its first kernel's start to its last kernel's end, taken from HIP events that
-the runtime records at each kernel's start and end inside the timed region.
-The same events give every kernel's own duration (the figure rocprofv3's
-kernel trace reports), from which the rooflines are computed: ``roofline`` is
-the chunk path's dominant kernel against the bf16 matrix-core peak,
-``roofline_decode`` the decode step against HBM bandwidth.  ``ms_per_step``
-is the host wall clock of a whole step.
+``value`` is the chunkwise forward's tokens/s from its GPU time in the timed
+region: K whole steps through the untimed entry points, each chunk call
+between two events on the launch stream.  The same K steps then run through
+the timed entry points, whose events, recorded by the runtime at each
+kernel's start and end, give every kernel's own duration (the figure
+rocprofv3's kernel trace reports); those events add about 3 us at each kernel
+boundary, which is why the throughput is taken without them.  The rooflines
+come from the kernel durations: ``roofline`` is the chunk path's dominant
+kernel against the bf16 matrix-core peak, ``roofline_decode`` the decode step
+against HBM bandwidth.  ``ms_per_step`` is the host wall clock of a whole step
+of the timed region.
 
 After the timed steps, outside the step: the prefill workload (T=4096) is
 timed the same way beside the chunk workload (``chunk_fwd_prefill``); both
@@ -154,8 +157,10 @@ class ChunkLeg:
     def flops(self):
         return alg_flops_chunk(np.diff(self.inp.cu_seqlens).tolist(), self.inp.Nqk, self.inp.Nv)
 
-    def summarise(self, tims, steps):
-        """Span and per-kernel figures from the timed calls' event records."""
+    def summarise(self, tims, steps, call_ms):
+        """The call's GPU time from stream events around untimed calls
+        (``call_ms``), and per-kernel figures from the timed calls' event
+        records (``tims``: one list of (kernel, ms) per call)."""
         spans = [ms for tim in tims for n, ms in tim if n == "span"]
         per_kernel = {}
         for tim in tims:
@@ -163,7 +168,7 @@ class ChunkLeg:
                 if n != "span":
                     per_kernel.setdefault(n, []).append(ms)
         f_intra, f_inter = self.flops()
-        span_s = float(np.mean(spans)) * 1e-3
+        span_s = float(np.mean(call_ms)) * 1e-3
         kst = {}
         for n, lst in per_kernel.items():
             per_call = len(lst) / steps
@@ -178,17 +183,35 @@ class ChunkLeg:
                 "alg_tflops": round(f_tot / span_s / 1e12, 2),
                 "frac_bf16_mfma_peak": round(f_tot / span_s / 1e12 / MFMA_PEAK_TFLOPS["bf16"], 4),
                 "kernel_sum_ms": round(sum(v["avg_ms"] * v["launches_per_call"] for v in kst.values()), 4),
+                "span_with_kernel_events_ms": round(float(np.mean(spans)), 4),
                 "kernels": kst}
 
 
+def call_events(n):
+    import torch
+    return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(n)]
+
+
 def time_chunk(leg, steps, warmup, flush=None):
-    """`steps` timed calls after `warmup` untimed ones; with `flush` (a 512 MiB
-    device buffer) the buffer is rewritten before every call, so the call
-    starts with no input left in the Infinity Cache (cold)."""
+    """After `warmup` untimed calls: `steps` untimed calls, each between two
+    events on the launch stream (the call's GPU time), then `steps` calls
+    through the timed entry point (each kernel's duration).  With `flush` (a
+    512 MiB device buffer) the buffer is rewritten before every call, so the
+    call starts with no input left in the Infinity Cache (cold)."""
     import torch
     for _ in range(warmup):
         leg()
     torch.cuda.synchronize()
+    evs = call_events(steps)
+    for a, b in evs:
+        if flush is not None:
+            flush.add_(1.0)
+        a.record()
+        leg()
+        b.record()
+    torch.cuda.synchronize()
+    call_ms = [a.elapsed_time(b) for a, b in evs]
     tims = []
     for _ in range(steps):
         if flush is not None:
@@ -197,7 +220,7 @@ def time_chunk(leg, steps, warmup, flush=None):
         leg(tim)
         tims.append(tim)
     torch.cuda.synchronize()
-    return leg.summarise(tims, steps)
+    return leg.summarise(tims, steps, call_ms)
 
 
 def main() -> int:
@@ -260,17 +283,33 @@ def main() -> int:
         step([])
     torch.cuda.synchronize()
 
-    chunk_tims, dec_ms = [], []
+    # the timed region: K whole steps through the untimed entry points, with
+    # one event pair on the launch stream around each chunk call
+    evs = call_events(args.steps)
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
+    for a, b in evs:
+        a.record()
+        leg()
+        b.record()
+        gdr.recurrent_step(Dd["q"], Dd["k"], Dd["v"], Dd["g"], Dd["beta"], dstate,
+                           state_out=dstate, out=dout, scale=scale)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    call_ms = [a.elapsed_time(b) for a, b in evs]
+
+    # the same K steps through the timed entry points: every kernel's duration
+    # from events the runtime records at its start and end (they add about
+    # 3 us at each kernel boundary, so the throughput above is taken without)
+    chunk_tims, dec_ms = [], []
     for _ in range(args.steps):
         tim = []
         step(tim)
         dec_ms.extend(ms for n, ms in tim if n == "decode")
         chunk_tims.append([(n, ms) for n, ms in tim if n != "decode"])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
 
-    chunk = leg.summarise(chunk_tims, args.steps)
+    chunk = leg.summarise(chunk_tims, args.steps, call_ms)
     tok_s = chunk["tokens_per_s"]
     dec_s = float(np.mean(dec_ms)) * 1e-3
     dec_bytes = alg_bytes_decode(dec.N, dec.Nqk, dec.Nv)

@@ -11,9 +11,12 @@ namespace gdr {
 
 // Number of 128-token chunk slots reserved for T packed tokens in N
 // sequences.  Chunks restart at every sequence start, so sequence b needs
-// ceil(len_b / 128) <= floor(len_b / 128) + 1 slots, and the sum over b is at
-// most floor(T / 128) + N.
-inline int64_t max_slots(int64_t T, int64_t N) { return T / 128 + N; }
+// ceil(len_b / 128) <= (len_b + 127) / 128 slots, and the sum over b is at
+// most floor((T + 127 N) / 128).  For one sequence that is exactly its chunk
+// count, so no segment carries an empty slot (at T = 32768 and 32 heads a
+// segment of 32 slots is 1024 units of the intra kernel: two full rounds of
+// two workgroups per CU, where a 33rd slot would start a third).
+inline int64_t max_slots(int64_t T, int64_t N) { return (T + 127 * N) / 128; }
 
 // Upper bound on the chunk slots of one segment (the state pass stages a
 // segment's chunk table in LDS).
