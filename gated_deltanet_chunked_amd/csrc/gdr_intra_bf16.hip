@@ -577,13 +577,21 @@ __device__ __forceinline__ void gram_mask(Lds& s, const Lane& L, P4& Pp, int m0,
 __global__ __launch_bounds__(256, 2) void intra_bf16_kernel(
     const bf* __restrict__ q, const bf* __restrict__ k, const bf* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, Chunks chunks, int32_t Nqk,
-    int32_t Nv, int32_t slot0, float scale, int norm, bf* __restrict__ inter,
+    int32_t Nv, int32_t slot0, int32_t nseg, float scale, int norm, bf* __restrict__ inter,
     float* __restrict__ gam_out) {
   __shared__ Lds s;
-  const int local_slot = blockIdx.x, h = blockIdx.y;
+  // Workgroup id -> (chunk slot, value head).  Workgroups go to the 8 XCDs
+  // round-robin by id; the G = Nv / Nqk value heads of one (slot, q/k head)
+  // read the same k and q rows, so they are given ids with the same id % 8
+  // and share that XCD's L2.  Groups p = slot * Nqk + j are dealt in order;
+  // ids past the last group (the grid is padded to whole rounds of 8 G) exit.
+  const int G = Nv / Nqk;
+  const int id = blockIdx.x, xcd = id & 7, r = id >> 3;
+  const int p = (r / G) * 8 + xcd;
+  if (p >= nseg * Nqk) return;
+  const int local_slot = p / Nqk, j = p % Nqk, h = j * G + r % G;
   int start, len;
   if (!chunks.slot(slot0 + local_slot, start, len)) return;
-  const int j = h / (Nv / Nqk);
   const int tid = threadIdx.x, l = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int m0 = 64 * (w >> 1), n0 = 64 * (w & 1);
@@ -788,8 +796,10 @@ hipError_t launch_intra_bf16(const __bf16* q, const __bf16* k, const __bf16* v, 
                              const float* beta, Chunks chunks, int32_t Nqk, int32_t Nv,
                              int32_t slot0, int32_t nseg, float scale, int norm, __bf16* inter,
                              float* gam, hipStream_t stream, LaunchEvents ev) {
-  hipExtLaunchKernelGGL(intra_bf16_kernel, dim3(nseg, Nv), dim3(256), 0, stream, ev.start, ev.stop,
-                        0, q, k, v, g, beta, chunks, Nqk, Nv, slot0, scale, norm, inter, gam);
+  const unsigned groups = (unsigned)nseg * (unsigned)Nqk;
+  const unsigned blocks = (groups + 7u) / 8u * 8u * (unsigned)(Nv / Nqk);
+  hipExtLaunchKernelGGL(intra_bf16_kernel, dim3(blocks), dim3(256), 0, stream, ev.start, ev.stop,
+                        0, q, k, v, g, beta, chunks, Nqk, Nv, slot0, nseg, scale, norm, inter, gam);
   return hipGetLastError();
 }
 
