@@ -43,39 +43,105 @@ __device__ __forceinline__ int owner(const int32_t* cu, int32_t N, int32_t T, in
 
 }  // namespace
 
-// One workgroup per (16 tokens, 256 channels).  A thread walks its channel
-// through the 16 tokens with the window's three older values in registers,
-// so each projected value is read once; at a sequence start the window
-// restarts from that sequence's cached values.
+// One workgroup per (16 tokens, 2048 channels): a thread owns 8 consecutive
+// channels (one 16-byte piece of a bf16 row; the q | k | v boundaries are
+// multiples of 128 channels, so a piece never straddles two parts) and walks
+// them through the 16 tokens with the window's three older values in
+// registers, so each projected value is read once, 16 bytes per access; at a
+// sequence start the window restarts from that sequence's cached values.
 constexpr int kTokPerBlock = 16;
+constexpr int kChPerThread = 8;
+constexpr int kChPerBlock = 256 * kChPerThread;
+
+// 8 consecutive values of type T as float (one 16-byte load for bf16, two for
+// fp32), and the other way.
+template <typename T>
+__device__ __forceinline__ void get8(const T* p, float* x) {
+  get4<T>(p, x);
+  get4<T>(p + 4, x + 4);
+}
+template <>
+__device__ __forceinline__ void get8<__bf16>(const __bf16* p, float* x) {
+  const bf16x8 a = *reinterpret_cast<const bf16x8*>(p);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = (float)a[e];
+}
+template <typename T>
+__device__ __forceinline__ void put8(T* p, const float* y) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) p[e] = from_f32<T>(y[e]);
+}
+template <>
+__device__ __forceinline__ void put8<__bf16>(__bf16* p, const float* y) {
+  bf16x8 a;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) a[e] = (__bf16)y[e];
+  *reinterpret_cast<bf16x8*>(p) = a;
+}
+template <>
+__device__ __forceinline__ void put8<float>(float* p, const float* y) {
+  *reinterpret_cast<f32x4*>(p) = f32x4{y[0], y[1], y[2], y[3]};
+  *reinterpret_cast<f32x4*>(p + 4) = f32x4{y[4], y[5], y[6], y[7]};
+}
+
+// Raw 8 values of type T (kept unconverted while in flight).
+template <typename T>
+struct Raw8 {
+  typedef __attribute__((ext_vector_type(8))) T type;
+};
 
 template <typename T>
 __global__ __launch_bounds__(256) void conv_prefill_kernel(ConvPrefillArgs<T> p) {
   const int t0 = blockIdx.x * kTokPerBlock;
   const int t1 = min(t0 + kTokPerBlock, p.Ttok);
-  const int c = blockIdx.y * 256 + threadIdx.x;
+  const int c = (blockIdx.y * 256 + threadIdx.x) * kChPerThread;
   if (c < p.C) {
-    float w[4];
-    get4<T>(p.w + (size_t)c * 4, w);
-    const float bias = p.bias ? to_f32(p.bias[c]) : 0.0f;
+    // kernels of the 8 channels: 32 consecutive values of [C, 4]
+    float w[kChPerThread][4];
+#pragma unroll
+    for (int e = 0; e < kChPerThread; ++e) get4<T>(p.w + (size_t)(c + e) * 4, w[e]);
+    float bias[kChPerThread];
+    if (p.bias) get8<T>(p.bias + c, bias);
+    else
+#pragma unroll
+      for (int e = 0; e < kChPerThread; ++e) bias[e] = 0.0f;
     int b = owner(p.cu, p.N, p.Ttok, t0);
     int start = min(max(p.cu[b], 0), p.Ttok);
     int end = min(max(p.cu[b + 1], start), p.Ttok);
-    // value `back` (1..3) places before sequence b's first token: its cached window
-    auto cached = [&](int bb, int back) -> float {
-      return p.cs_in ? to_f32(p.cs_in[((size_t)bb * p.C + c) * 4 + 4 - back]) : 0.0f;
+    // window values 1..3 places before sequence bb's first token, from its
+    // cached window [bb][c + e][4] (zeros without a cache)
+    auto cached = [&](int bb, int back, float* x) {
+      if (p.cs_in) {
+#pragma unroll
+        for (int e = 0; e < kChPerThread; ++e)
+          x[e] = to_f32(p.cs_in[((size_t)bb * p.C + c + e) * 4 + 4 - back]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < kChPerThread; ++e) x[e] = 0.0f;
+      }
     };
-    // value at position pos < t0, in the sequence of t0
-    auto before = [&](int pos) -> float {
-      return pos >= start ? to_f32(p.x[(size_t)pos * p.C + c]) : cached(b, min(start - pos, 3));
+    // the values at position pos < t0, in the sequence of t0
+    auto before = [&](int pos, float* x) {
+      if (pos >= start) get8<T>(p.x + (size_t)pos * p.C + c, x);
+      else cached(b, min(start - pos, 3), x);
     };
     // all of the block's token values at once (the tail repeats the block's
     // last token, which exists), so the loads are in flight together
-    T xs[kTokPerBlock];
+    typename Raw8<T>::type xs[kTokPerBlock];
 #pragma unroll
-    for (int i = 0; i < kTokPerBlock; ++i) xs[i] = p.x[(size_t)min(t0 + i, t1 - 1) * p.C + c];
-    float w1 = before(t0 - 3), w2 = before(t0 - 2), w3 = before(t0 - 1);
+    for (int i = 0; i < kTokPerBlock; ++i)
+      xs[i] = *reinterpret_cast<const typename Raw8<T>::type*>(
+          p.x + (size_t)min(t0 + i, t1 - 1) * p.C + c);
+    float w1[kChPerThread], w2[kChPerThread], w3[kChPerThread];
+    before(t0 - 3, w1);
+    before(t0 - 2, w2);
+    before(t0 - 1, w3);
     const int qk = p.Nqk * kD;
+    T* dst;
+    int stride;
+    if (c < qk) { dst = p.q + c; stride = qk; }
+    else if (c < 2 * qk) { dst = p.k + (c - qk); stride = qk; }
+    else { dst = p.v + (c - 2 * qk); stride = p.C - 2 * qk; }
 #pragma unroll
     for (int i = 0; i < kTokPerBlock; ++i) {
       const int t = t0 + i;
@@ -84,19 +150,21 @@ __global__ __launch_bounds__(256) void conv_prefill_kernel(ConvPrefillArgs<T> p)
         b = owner(p.cu, p.N, p.Ttok, t);
         start = min(max(p.cu[b], 0), p.Ttok);
         end = min(max(p.cu[b + 1], start), p.Ttok);
-        w1 = cached(b, 3);
-        w2 = cached(b, 2);
-        w3 = cached(b, 1);
+        cached(b, 3, w1);
+        cached(b, 2, w2);
+        cached(b, 1, w3);
       }
-      const float xt = to_f32(xs[i]);
-      float y = bias + w[0] * w1 + w[1] * w2 + w[2] * w3 + w[3] * xt;
-      y = y / (1.0f + expf(-y));
-      if (c < qk) p.q[(size_t)t * qk + c] = from_f32<T>(y);
-      else if (c < 2 * qk) p.k[(size_t)t * qk + (c - qk)] = from_f32<T>(y);
-      else p.v[(size_t)t * (p.C - 2 * qk) + (c - 2 * qk)] = from_f32<T>(y);
-      w1 = w2;
-      w2 = w3;
-      w3 = xt;
+      float y[kChPerThread];
+#pragma unroll
+      for (int e = 0; e < kChPerThread; ++e) {
+        const float xt = to_f32(xs[i][e]);
+        float a = bias[e] + w[e][0] * w1[e] + w[e][1] * w2[e] + w[e][2] * w3[e] + w[e][3] * xt;
+        y[e] = silu(a);
+        w1[e] = w2[e];
+        w2[e] = w3[e];
+        w3[e] = xt;
+      }
+      put8<T>(dst + (size_t)t * stride, y);
     }
   }
   if (blockIdx.y == 0) {
@@ -142,9 +210,9 @@ void launch_conv_prefill(const ConvPrefillArgs<T>& p, hipStream_t stream, Launch
   const unsigned cb = (unsigned)((p.C + 255) / 256);
   if (p.Ttok > 0)
     hipExtLaunchKernelGGL(conv_prefill_kernel<T>,
-                          dim3((unsigned)((p.Ttok + kTokPerBlock - 1) / kTokPerBlock), cb), dim3(256),
-                          0, stream,
-                          ev_conv.start, ev_conv.stop, 0, p);
+                          dim3((unsigned)((p.Ttok + kTokPerBlock - 1) / kTokPerBlock),
+                               (unsigned)((p.C + kChPerBlock - 1) / kChPerBlock)),
+                          dim3(256), 0, stream, ev_conv.start, ev_conv.stop, 0, p);
   if (p.cs_out)
     hipExtLaunchKernelGGL(conv_window_kernel<T>, dim3((unsigned)p.N, cb), dim3(256), 0, stream,
                           ev_window.start, ev_window.stop, 0, p);

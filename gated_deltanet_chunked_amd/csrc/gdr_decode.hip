@@ -201,7 +201,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const T* __restrict__ q, co
     float o = ov[0];
 #pragma unroll
     for (int i = 1; i < 8; ++i) o = cg == i ? ov[i] : o;
-    if (cg < 8) op[rg + 16 * cg] = from_f32<T>(o * inv * wr * (zr / (1.0f + expf(-zr))));
+    if (cg < 8) op[rg + 16 * cg] = from_f32<T>(o * inv * wr * silu(zr));
   }
   (void)l;
 }
@@ -378,7 +378,7 @@ struct ConvLoad {
     const float s1 = to_f32(win[1]), s2 = to_f32(win[2]), s3 = to_f32(win[3]), xf = to_f32(x);
     float y = to_f32(w[0]) * s1 + to_f32(w[1]) * s2 + to_f32(w[2]) * s3 + to_f32(w[3]) * xf;
     y += to_f32(bias);
-    y = y / (1.0f + expf(-y));
+    y = silu(y);
     if (write) put4<T>(p.cs_out + ((size_t)n * p.C + c) * 4, s1, s2, s3, xf);   // exact
     return to_f32(from_f32<T>(y));
   }

@@ -337,6 +337,16 @@ __device__ __forceinline__ float dpp_f32(float x) {
 }
 
 // Sum over aligned groups of 16 lanes; every lane of the group gets the total.
+// SiLU(x) = x sigmoid(x) = x / (1 + e^-x) with the hardware exponential and
+// reciprocal (v_exp_f32, v_rcp_f32, about 1 ulp each): it runs once per
+// element of the HBM-bound activation kernels, where the exact division and
+// exponential cost more issue slots than the bytes take; its results are
+// rounded to the activation dtype or enter fp32 sums far above that error.
+// Saturates like the exact form: e^-x = inf gives -0, e^-x = 0 gives x.
+__device__ __forceinline__ float silu(float x) {
+  return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x));
+}
+
 // Butterfly on DPP: swap neighbours, swap pairs (quad sums), mirror within 8
 // (half-row sums), mirror within 16 (row sums).
 __device__ __forceinline__ float group16_sum(float x) {

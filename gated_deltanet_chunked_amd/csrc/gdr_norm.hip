@@ -47,7 +47,7 @@ __device__ __forceinline__ void gate_row(const float* x, const float* z, const f
   ss = group16_sum(ss);
   const float inv = 1.0f / sqrtf(ss * (1.0f / kD) + eps);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) y[e] = x[e] * inv * w[e] * (z[e] / (1.0f + expf(-z[e])));
+  for (int e = 0; e < 8; ++e) y[e] = x[e] * inv * w[e] * silu(z[e]);
 }
 
 // x and y may be the same buffer (in place), so neither is restrict.
