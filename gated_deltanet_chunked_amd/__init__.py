@@ -21,6 +21,7 @@ LIB_PATH = os.path.join(HERE, "libgdr.so")
 GDR_F32 = 0
 GDR_BF16 = 1
 GDR_FLAG_QK_L2NORM = 1
+GDR_FLAG_CHUNK64 = 2
 CHUNK = 128
 D = 128
 
@@ -143,16 +144,23 @@ def workspace_size(T: int, N: int, Nqk: int, Nv: int, dtype_code: int) -> int:
 STAGE_NAMES = {0: "table", 1: "intra", 2: "inter"}
 
 
+def _chunk_flags(l2norm: bool, chunk: int) -> int:
+    if chunk not in (64, 128):
+        raise ValueError(f"chunk must be 64 or 128, got {chunk}")
+    return (GDR_FLAG_QK_L2NORM if l2norm else 0) | (GDR_FLAG_CHUNK64 if chunk == 64 else 0)
+
+
 def chunk_fwd(q, k, v, g, beta, cu_seqlens, state_in=None, *, scale: Optional[float] = None,
               out=None, state_out=None, want_state: bool = True, workspace=None,
-              l2norm: bool = True, timings: Optional[list] = None
+              l2norm: bool = True, chunk: int = CHUNK, timings: Optional[list] = None
               ) -> Tuple["torch.Tensor", Optional["torch.Tensor"]]:
     """Chunkwise gated delta rule over packed sequences (``gdr_chunk_fwd``).
 
     q, k [T, Nqk, 128], v [T, Nv, 128] (bf16 or f32); g, beta [T, Nv] f32;
     cu_seqlens [N + 1] int32 (device); state_in [N, Nv, 128, 128] f32 or None.
     Returns (out [T, Nv, 128] in q's dtype, state_out or None).
-    ``state_out`` may be ``state_in`` for an in-place update.
+    ``state_out`` may be ``state_in`` for an in-place update.  ``chunk``: the
+    chunk length, 128 or 64 (``GDR_FLAG_CHUNK64``; same results up to rounding).
     With a list as ``timings`` the call goes through ``gdr_chunk_fwd_timed``
     (blocking) and appends one (stage name, GPU milliseconds) per kernel, then
     ("span", milliseconds from the first kernel's start to the last one's end).
@@ -187,7 +195,7 @@ def chunk_fwd(q, k, v, g, beta, cu_seqlens, state_in=None, *, scale: Optional[fl
         scale = D ** -0.5
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_in),
             _ptr(cu_seqlens), N, T, Nqk, Nv, D, code, float(scale),
-            GDR_FLAG_QK_L2NORM if l2norm else 0, _ptr(out), _ptr(state_out),
+            _chunk_flags(l2norm, chunk), _ptr(out), _ptr(state_out),
             _ptr(workspace), workspace.numel(), _stream())
     if timings is None:
         st = lib.gdr_chunk_fwd(*args)
@@ -208,7 +216,7 @@ def chunk_fwd(q, k, v, g, beta, cu_seqlens, state_in=None, *, scale: Optional[fl
 
 
 def chunk_fwd_no_alloc(q, k, v, g, beta, cu_seqlens, state_in, out, state_out, *,
-                       scale: Optional[float] = None, l2norm: bool = True):
+                       scale: Optional[float] = None, l2norm: bool = True, chunk: int = CHUNK):
     """``gdr_chunk_fwd_no_alloc``: the chunkwise forward with the library's
     fixed scratch as workspace.  The caller passes every buffer (``state_in``
     and ``state_out`` may be None), so this function allocates nothing either.
@@ -234,7 +242,7 @@ def chunk_fwd_no_alloc(q, k, v, g, beta, cu_seqlens, state_in, out, state_out, *
         scale = D ** -0.5
     st = lib.gdr_chunk_fwd_no_alloc(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                     _ptr(state_in), _ptr(cu_seqlens), N, T, Nqk, Nv, D, code,
-                                    float(scale), GDR_FLAG_QK_L2NORM if l2norm else 0, _ptr(out),
+                                    float(scale), _chunk_flags(l2norm, chunk), _ptr(out),
                                     _ptr(state_out), _stream())
     if st != 0:
         raise GdrError(st, "gdr_chunk_fwd_no_alloc")

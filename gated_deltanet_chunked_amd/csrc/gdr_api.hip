@@ -68,7 +68,8 @@ int32_t launches_needed(const Workspace& w, int64_t N) {
 
 template <typename T>
 gdr_status run_chunk(const ChunkArgs& a, hipStream_t st, Recorder& rec) {
-  const Workspace w = plan_workspace(a.T, a.N, a.Nqk, a.Nv, a.dtype, a.budget);
+  const int32_t L = chunk_len(a.flags);
+  const Workspace w = plan_workspace(a.T, a.N, a.Nqk, a.Nv, a.dtype, a.budget, L);
   char* ws = static_cast<char*>(a.workspace);
   int4* table = reinterpret_cast<int4*>(ws + w.table);
   int32_t* choff = reinterpret_cast<int32_t*>(ws + w.choff);
@@ -85,9 +86,9 @@ gdr_status run_chunk(const ChunkArgs& a, hipStream_t st, Recorder& rec) {
 
   // Every launch is checked at once: hipGetLastError also clears the error,
   // so a failed launch followed by a good one would otherwise go unseen.
-  Chunks chunks{nullptr, nullptr, a.cu_seqlens, a.T};
+  Chunks chunks{nullptr, nullptr, a.cu_seqlens, a.T, L};
   if (a.N > 1) {
-    launch_table(a.cu_seqlens, a.N, a.T, nslots, table, choff, st, rec.next(GDR_STAGE_TABLE));
+    launch_table(a.cu_seqlens, a.N, a.T, L, nslots, table, choff, st, rec.next(GDR_STAGE_TABLE));
     if (hipGetLastError() != hipSuccess) return GDR_ERR_HIP;
     chunks.table = table;
     chunks.choff = choff;
@@ -125,7 +126,10 @@ extern "C" size_t gdr_chunk_fwd_workspace_size(int32_t T, int32_t N, int32_t Nqk
   if (T < 0 || N < 1 || Nqk < 1 || Nv < 1 || Nv > kMaxNv || Nv % Nqk != 0 || D != 128) return 0;
   if (dtype != GDR_F32 && dtype != GDR_BF16) return 0;
   if (static_cast<int64_t>(T) * Nv > (int64_t(1) << 40)) return 0;
-  return static_cast<size_t>(plan_workspace(T, N, Nqk, Nv, dtype).total);
+  // enough for either chunk length (64-token chunks need more table slots)
+  const int64_t a = plan_workspace(T, N, Nqk, Nv, dtype, 0, 128).total;
+  const int64_t b = plan_workspace(T, N, Nqk, Nv, dtype, 0, 64).total;
+  return static_cast<size_t>(a > b ? a : b);
 }
 
 extern "C" gdr_status gdr_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
@@ -160,7 +164,8 @@ extern "C" gdr_status gdr_chunk_fwd_timed(const void* q, const void* k, const vo
   if (!kernel_ms || !kernel_kind || !n || max_kernels < 0) return GDR_ERR_INVALID_ARGUMENT;
   s = chunk_contract(a, static_cast<hipStream_t>(stream));
   if (s != GDR_OK) return s;
-  const int32_t need = launches_needed(plan_workspace(T, N, Nqk, Nv, dtype), N);
+  const int32_t need =
+      launches_needed(plan_workspace(T, N, Nqk, Nv, dtype, 0, chunk_len(flags)), N);
   // more launches than the caller's arrays hold: the span alone is timed
   const bool span_only = need > max_kernels;
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -238,7 +243,7 @@ extern "C" gdr_status gdr_chunk_fwd_no_alloc(const void* q, const void* k, const
                       flags, out, state_out, nullptr, 0, true, 0};
   gdr_status s = validate_chunk(pre);
   if (s != GDR_OK) return s;
-  if (plan_workspace(T, N, Nqk, Nv, dtype, kScratchBytes).total < 0)
+  if (plan_workspace(T, N, Nqk, Nv, dtype, kScratchBytes, chunk_len(flags)).total < 0)
     return GDR_ERR_WORKSPACE_TOO_SMALL;
   void* ws = nullptr;
   const gdr_status p = scratch_ptr(&ws);

@@ -9,14 +9,17 @@
 
 namespace gdr {
 
-// Number of 128-token chunk slots reserved for T packed tokens in N
-// sequences.  Chunks restart at every sequence start, so sequence b needs
-// ceil(len_b / 128) <= (len_b + 127) / 128 slots, and the sum over b is at
-// most floor((T + 127 N) / 128).  For one sequence that is exactly its chunk
+// Number of chunk slots (chunks of L = 128 or 64 tokens) reserved for T packed
+// tokens in N sequences.  Chunks restart at every sequence start, so sequence
+// b needs ceil(len_b / L) <= (len_b + L - 1) / L slots, and the sum over b is
+// at most floor((T + (L - 1) N) / L).  For one sequence that is exactly its chunk
 // count, so no segment carries an empty slot (at T = 32768 and 32 heads a
 // segment of 32 slots is 1024 units of the intra kernel: two full rounds of
 // two workgroups per CU, where a 33rd slot would start a third).
-inline int64_t max_slots(int64_t T, int64_t N) { return (T + 127 * N) / 128; }
+inline int64_t max_slots(int64_t T, int64_t N, int64_t L = 128) { return (T + (L - 1) * N) / L; }
+
+// Chunk length of a chunkwise call: 128, or 64 with GDR_FLAG_CHUNK64.
+inline int32_t chunk_len(uint32_t flags) { return (flags & GDR_FLAG_CHUNK64) ? 64 : 128; }
 
 // Upper bound on the chunk slots of one segment (the state pass stages a
 // segment's chunk table in LDS).
@@ -64,7 +67,7 @@ struct Workspace {
 // (segment_slots).  budget > 0: the largest even split whose whole layout
 // fits in `budget` bytes; total = -1 when not even one chunk slot fits.
 Workspace plan_workspace(int64_t T, int64_t N, int64_t Nqk, int64_t Nv, gdr_dtype dtype,
-                         int64_t budget = 0);
+                         int64_t budget = 0, int64_t L = 128);
 
 struct ChunkArgs {
   const void* q; const void* k; const void* v;

@@ -26,6 +26,7 @@ struct Chunks {
   const int32_t* choff;
   const int32_t* cu;
   int32_t T;
+  int32_t L;   // chunk length: 128, or 64
   __device__ __forceinline__ void one_range(int& lo, int& hi) const {
     lo = min(max(cu[0], 0), T);
     hi = min(max(cu[1], lo), T);
@@ -40,8 +41,8 @@ struct Chunks {
     }
     int lo, hi;
     one_range(lo, hi);
-    start = lo + 128 * s;
-    len = min(128, hi - start);
+    start = lo + L * s;
+    len = min(L, hi - start);
     return start < hi;
   }
   // slots [c0, c1) of sequence b
@@ -54,11 +55,11 @@ struct Chunks {
     int lo, hi;
     one_range(lo, hi);
     c0 = 0;
-    c1 = (hi - lo + 127) / 128;
+    c1 = (hi - lo + L - 1) / L;
   }
 };
 
-void launch_table(const int32_t* cu, int32_t N, int32_t T, int32_t nslots, int4* table,
+void launch_table(const int32_t* cu, int32_t N, int32_t T, int32_t L, int32_t nslots, int4* table,
                   int32_t* choff, hipStream_t stream, LaunchEvents ev = {});
 
 // Intra-chunk products for chunk slots [slot0, slot0 + nseg) of every value head;

@@ -9,7 +9,7 @@
 namespace gdr {
 namespace {
 
-constexpr uint32_t kKnownFlags = GDR_FLAG_QK_L2NORM;
+constexpr uint32_t kKnownFlags = GDR_FLAG_QK_L2NORM | GDR_FLAG_CHUNK64;
 
 int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
 
@@ -33,11 +33,11 @@ gdr_status common_sizes(int32_t Nqk, int32_t Nv, int32_t D, gdr_dtype dtype, uin
 }  // namespace
 
 Workspace plan_workspace(int64_t T, int64_t N, int64_t Nqk, int64_t Nv, gdr_dtype dtype,
-                         int64_t budget) {
+                         int64_t budget, int64_t L) {
   Workspace w{};
   const int64_t es = static_cast<int64_t>(dtype_size(dtype));
   const int64_t per_slot = Nv * kInterMats * kMatElems * es;
-  w.nslots = max_slots(T, N);
+  w.nslots = max_slots(T, N, L);
   // everything but the segment's matrices
   const int64_t fixed = align256(w.nslots * 4 * 4) + align256((N + 1) * 4) +
                         align256(w.nslots * Nv * 4) + align256(N * Nv * kMatElems * 4) + 256;
@@ -82,7 +82,7 @@ gdr_status validate_chunk(const ChunkArgs& a) {
     if (p && !aligned16(p)) return GDR_ERR_INVALID_ARGUMENT;
   if (!a.no_workspace) {
     if ((reinterpret_cast<uintptr_t>(a.workspace) & 255u) != 0) return GDR_ERR_INVALID_ARGUMENT;
-    const Workspace w = plan_workspace(a.T, a.N, a.Nqk, a.Nv, a.dtype, a.budget);
+    const Workspace w = plan_workspace(a.T, a.N, a.Nqk, a.Nv, a.dtype, a.budget, chunk_len(a.flags));
     if (w.total < 0 || a.workspace_bytes < static_cast<size_t>(w.total))
       return GDR_ERR_WORKSPACE_TOO_SMALL;
   }

@@ -79,7 +79,15 @@ typedef enum {
  * (then scale still multiplies q). */
 #define GDR_FLAG_QK_L2NORM 1u
 
-/* The chunk length of the chunkwise form (operator page: fixed at 128). */
+/* Chunkwise calls only: chunks of 64 tokens instead of 128 (the Blog's
+ * torch_chunk_gated_delta_rule default chunk_size=64).  The chunkwise form is
+ * exact for any chunk length, so the results equal those with 128 up to
+ * rounding; the kernels are the same (a 64-token chunk is a 128-row tile with
+ * its last 64 rows absent), so it costs about twice the time.  The other
+ * calls ignore it. */
+#define GDR_FLAG_CHUNK64 2u
+
+/* The default chunk length of the chunkwise form (operator page: 128). */
 #define GDR_CHUNK 128
 
 /*

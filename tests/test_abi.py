@@ -97,7 +97,7 @@ def call_chunk(fb, **over):
 @pytest.mark.parametrize("over,expect", [
     (dict(D=64), UNSUPPORTED),
     (dict(dtype=7), UNSUPPORTED),
-    (dict(flags=2), UNSUPPORTED),
+    (dict(flags=4), UNSUPPORTED),
     (dict(Nqk=1, Nv=65536), UNSUPPORTED),   # more than 32768 value heads
     (dict(Nqk=3), INVALID),            # Nv % Nqk != 0
     (dict(N=0), INVALID),
@@ -242,7 +242,7 @@ def test_multi_token_validates_before_launching():
 
     assert call(D=64) == UNSUPPORTED
     assert call(dtype=9) == UNSUPPORTED
-    assert call(flags=2) == UNSUPPORTED
+    assert call(flags=4) == UNSUPPORTED
     assert call(Nqk=3) == INVALID
     assert call(N=0) == INVALID
     assert call(T=-1) == INVALID
@@ -415,3 +415,30 @@ def test_debug_switch_and_contract_status():
     assert lib.gdr_status_string(-5) == b"device values break the contract (debug checks)"
     assert gdr.STATUS[-5] == "GDR_ERR_CONTRACT"
     assert lib.gdr_debug_broken() == 0            # no checked call in this thread
+
+
+def test_chunk64_flag_and_workspace():
+    """GDR_FLAG_CHUNK64 is a known flag of the chunkwise call; the workspace
+    size covers both chunk lengths (64-token chunks need more table slots)."""
+    lib = gdr.load()
+    assert gdr.GDR_FLAG_CHUNK64 == 2
+    b = FakeBuffers()
+    a = b.addr
+    T, N, Nqk, Nv = 256, 2, 2, 4
+
+    def call(flags, ws_bytes):
+        return lib.gdr_chunk_fwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["state_in"], a["cu"],
+                                 N, T, Nqk, Nv, 128, gdr.GDR_BF16, 0.088, flags, a["out"],
+                                 a["state_out"], a["ws"], ws_bytes, None)
+
+    # a missing workspace is rejected for both lengths, before any launch
+    need = gdr.workspace_size(T, N, Nqk, Nv, gdr.GDR_BF16)
+    assert call(gdr.GDR_FLAG_CHUNK64 | 1, 0) == WS_SMALL
+    assert call(1, 0) == WS_SMALL
+    assert call(4, need) == UNSUPPORTED                      # unknown flag
+    # the size covers a 64-token-chunk call of many short sequences
+    assert gdr.workspace_size(4096, 64, 16, 32, gdr.GDR_BF16) >= \
+        gdr.workspace_size(4096, 1, 16, 32, gdr.GDR_BF16)
+    with pytest.raises(ValueError):
+        gdr._chunk_flags(True, 32)
+    assert gdr._chunk_flags(True, 64) == 3 and gdr._chunk_flags(False, 128) == 0
