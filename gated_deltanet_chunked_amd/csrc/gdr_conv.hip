@@ -167,8 +167,10 @@ __global__ __launch_bounds__(256) void conv_prefill_kernel(ConvPrefillArgs<T> p)
       put8<T>(dst + (size_t)t * stride, y);
     }
   }
-  if (blockIdx.y == 0) {
-    for (int idx = threadIdx.x; idx < (t1 - t0) * p.Nv; idx += 256) {
+  // the gates of the block's tokens, dealt over the channel blocks
+  {
+    const int per = (t1 - t0) * p.Nv, nb = (int)gridDim.y;
+    for (int idx = threadIdx.x + 256 * (int)blockIdx.y; idx < per; idx += 256 * nb) {
       const int t = t0 + idx / p.Nv, h = idx % p.Nv;
       const size_t gi = (size_t)t * p.Nv + h;
       const float z = p.a[gi] + p.dt_bias[h];
