@@ -109,10 +109,10 @@ size_t gdr_chunk_fwd_workspace_size(int32_t T, int32_t N, int32_t Nqk, int32_t N
  *                         for zeros
  * cu_seqlens [N + 1]      int32, device: cu[0] = 0 <= cu[1] <= ... <= cu[N] = T;
  *                         sequence b owns tokens [cu[b], cu[b+1]).  Chunks of
- *                         128 tokens restart at every sequence start, so a
- *                         sequence boundary may fall anywhere.
+ *                         128 (or 64) tokens restart at every sequence start,
+ *                         so a sequence boundary may fall anywhere.
  * scale      multiplies the normalised query (the blog uses 1/sqrt(D))
- * flags      GDR_FLAG_QK_L2NORM or 0
+ * flags      any of GDR_FLAG_QK_L2NORM, GDR_FLAG_CHUNK64
  * out        [T, Nv, D]   dtype, written for every token; must not alias inputs
  * state_out  [N, Nv, D, D] float32 final states, or NULL.  May equal state_in
  *                         (in-place update); must not partially overlap it.
