@@ -82,14 +82,25 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// Byte offset of element (r, c) of a swizzled 128-wide bf16 tile: the 16-byte
-// chunk index of row r is XORed with r mod 16.
+// XOR key of row r's 16-byte chunk indices: r mod 16, with bit 0 also folded
+// into bits 2 and 3.  Measured on gfx950, ds_read_b128 serves 16 lanes and
+// ds_read_b64_tr_b16 32 lanes per cycle from 64 banks (a 256-byte line).  Any
+// 16 consecutive rows from a multiple of 16 get 16 distinct keys, so a row
+// fragment read (16 rows, one chunk each) is conflict-free; the 8 rows
+// {8 q + x + 4 h} (q < 2, x < 4) of half a transposed read (two adjacent
+// chunks each) get 8 distinct keys / 2, so it is conflict-free too (with
+// r mod 16 alone: two-way).  Rows 16 apart share the key.
+__device__ __forceinline__ uint32_t swkey(uint32_t r) { return (r & 15u) ^ ((r & 1u) * 12u); }
+
+// Byte offset of element (r, c) of a swizzled 128-wide bf16 tile.
 __device__ __forceinline__ uint32_t sw(uint32_t r, uint32_t c) {
-  return r * 256u + ((((c >> 3) ^ (r & 15u))) << 4) + ((c & 7u) << 1);
+  return r * 256u + ((((c >> 3) ^ swkey(r))) << 4) + ((c & 7u) << 1);
 }
-// The same for the 64-wide scratch (8 chunks per row, XOR with r mod 8).
+// The same for the 64-wide scratch (8 chunks per row, two rows per 256-byte
+// line): the key (r / 2) mod 8 gives 16 consecutive rows 16 distinct chunk
+// positions (with r mod 8, rows r and r + 8 met on the same banks).
 __device__ __forceinline__ uint32_t sw64(uint32_t r, uint32_t c) {
-  return kW + r * 128u + ((((c >> 3) ^ (r & 7u))) << 4) + ((c & 7u) << 1);
+  return kW + r * 128u + ((((c >> 3) ^ ((r >> 1) & 7u))) << 4) + ((c & 7u) << 1);
 }
 
 // Per-lane LDS offsets, fixed for the whole kernel.  A wave owns the 64x64
@@ -107,8 +118,8 @@ __device__ __forceinline__ Lane make_lane(int m0, int n0) {
   const uint32_t t = threadIdx.x, l = t & 63u, r16 = l & 15u, q = l >> 4;
 #pragma unroll
   for (uint32_t ks = 0; ks < 4; ++ks) {
-    L.fa[ks] = (m0 + r16) * 256u + ((((4u * ks + q) ^ r16)) << 4);
-    L.fb[ks] = (n0 + r16) * 256u + ((((4u * ks + q) ^ r16)) << 4);
+    L.fa[ks] = (m0 + r16) * 256u + ((((4u * ks + q) ^ swkey(r16))) << 4);
+    L.fb[ks] = (n0 + r16) * 256u + ((((4u * ks + q) ^ swkey(r16))) << 4);
   }
 #pragma unroll
   for (uint32_t i = 0; i < 4; ++i) {
@@ -159,15 +170,27 @@ __device__ __forceinline__ void gemm64(f32x4 (&acc)[4][4], const Lds& s, const L
                                 BBASE + (L.ta[j][1] ^ L.tflip) + 8192u * ks)
                       : rd16(s, BBASE + L.fb[ks] + 4096u * j);
   };
+  constexpr int NR = (ATR ? 8 : 4) + (BTR ? 8 : 4);   // LDS reads per k-step
   if (DB) load(0, 0);
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
+    if (DB) __builtin_amdgcn_sched_barrier(0);
     if (!DB) load(0, ks);
     else if (ks + 1 < 4) load((ks + 1) % NS, ks + 1);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = mma(a[ks % NS][i], b[ks % NS][j], acc[i][j]);
+    if (DB && ks + 1 < 4) {
+      // the next step's reads go out between this step's matrix instructions
+#pragma unroll
+      for (int x = 0; x < NR; ++x) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      if (NR < 16) __builtin_amdgcn_sched_group_barrier(0x008, 16 - NR, 0);
+    }
+    if (DB) __builtin_amdgcn_sched_barrier(0);
   }
 }
 
