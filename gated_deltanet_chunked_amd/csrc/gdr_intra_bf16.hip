@@ -43,7 +43,7 @@ struct Lds {
   bf t0[128 * 128];
   bf t1[128 * 128];
   bf w[64 * 64];
-  float gc[128];        // chunk-local cumsum of g (fp32 copy of an fp64 scan)
+  float gc[128];        // chunk-local cumsum of g times log2(e) (fp32, from an fp64 scan)
   float beta[128];
   float rk[128];        // 1 / |k_r| (0 past the chunk's end)
   float rq[128];        // scale / |q_r|
@@ -242,12 +242,20 @@ struct Pieces {
       p[it] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(src) + (rr * gs + c) * 2u);
     }
   }
-  // sum of squares of piece it
+  // sum of squares of piece it, bf16 pairs on the dot-product unit (the
+  // pairs are shuffled out of the whole piece: this compiler lowers a bit
+  // cast of one 32-bit element to a bf16 pair as element 0)
   __device__ __forceinline__ float sumsq(int it) const {
-    const bf* e = reinterpret_cast<const bf*>(&p[it]);
+    const bf16x8 e = __builtin_bit_cast(bf16x8, p[it]);
     float acc = 0.0f;
-#pragma unroll
-    for (int x = 0; x < 8; ++x) { const float f = (float)e[x]; acc += f * f; }
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(e, e, 0, 1),
+                                          __builtin_shufflevector(e, e, 0, 1), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(e, e, 2, 3),
+                                          __builtin_shufflevector(e, e, 2, 3), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(e, e, 4, 5),
+                                          __builtin_shufflevector(e, e, 4, 5), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(e, e, 6, 7),
+                                          __builtin_shufflevector(e, e, 6, 7), acc, false);
     return acc;
   }
   // the pieces as they are, into slot BASE
@@ -572,7 +580,7 @@ __device__ __forceinline__ void gram_mask(Lds& s, const Lane& L, P4& Pp, int m0,
       float nv[4], pv[4];
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
-        const float ex = __builtin_amdgcn_exp2f(-fabsf(ga[x] - gcc[jj]) * 1.44269504088896341f);
+        const float ex = __builtin_amdgcn_exp2f(-fabsf(ga[x] - gcc[jj]));
         if (WT == 2) {
           nv[x] = fn[x] * fc[jj] * ex * g1[i][jj][x];
           pv[x] = 0.0f;
@@ -645,17 +653,25 @@ __global__ __launch_bounds__(256, 2) void intra_bf16_kernel(
     }
     if (l == 63) s.part[w] = gsum;
   }
-  // L2 norms over the 16 lanes holding a row
+  // L2 norms over the 16 lanes holding a row; every lane has all 16 sums
+  // of its row group (rows tid / 16 + 16 it of k and of q) and finishes one:
+  // lane c takes piece c mod 8 of k (c < 8) or of q
+  {
+    float ssk[8], ssq[8];
 #pragma unroll
-  for (int it = 0; it < 8; ++it) {
-    const float sk = group16_sum(kr.sumsq(it));
-    const float sq = group16_sum(qr.sumsq(it));
-    const int r = (tid >> 4) + 16 * it;
-    const bool ok = r < len;
-    if ((tid & 15) == 0) {
-      s.rk[r] = ok ? (norm ? 1.0f / sqrtf(sk + 1e-6f) : 1.0f) : 0.0f;
-      s.rq[r] = ok ? (norm ? scale / sqrtf(sq + 1e-6f) : scale) : 0.0f;
+    for (int it = 0; it < 8; ++it) {
+      ssk[it] = group16_sum(kr.sumsq(it));
+      ssq[it] = group16_sum(qr.sumsq(it));
     }
+    const int c = tid & 15, it = c & 7;
+    const bool isq = c >= 8;
+    float ss = isq ? ssq[0] : ssk[0];
+#pragma unroll
+    for (int x = 1; x < 8; ++x)
+      if (it == x) ss = isq ? ssq[x] : ssk[x];
+    const int r = (tid >> 4) + 16 * it;
+    const float f = (norm ? __builtin_amdgcn_rsqf(ss + 1e-6f) : 1.0f) * (isq ? scale : 1.0f);
+    (isq ? s.rq : s.rk)[r] = r < len ? f : 0.0f;
   }
   kr.store<kT0>(s, L);
   qr.store<kT1>(s, L);
@@ -666,7 +682,7 @@ __global__ __launch_bounds__(256, 2) void intra_bf16_kernel(
     const double gcd = gsum + (w == 1 ? s.part[0] : 0.0);
     const double glast = s.part[0] + s.part[1];
     const float e = __expf((float)gcd), rk = s.rk[tid];
-    s.gc[tid] = (float)gcd;
+    s.gc[tid] = (float)(gcd * 1.4426950408889634);   // in log2 units, for the mask
     s.beta[tid] = bt;
     s.brk[tid] = bt * rk;
     s.ck[tid] = __expf((float)(glast - gcd)) * rk;
