@@ -10,9 +10,13 @@
 // value head), eight workgroups per (sequence, head) on one XCD, so a single
 // sequence of 32 heads fills all 256 compute units.
 //
-// What bounds a chunk step is how early each chunk's operands arrive: per
-// chunk a workgroup needs its full Mt and Qp (32 KiB each) and its slices of
-// Bm and Ou (4 KiB each), in the workspace orders the intra-chunk kernel
+// What bounds a chunk step is the compute unit's vector memory path: per
+// chunk a workgroup reads its full Mt and Qp (32 KiB each) and its slices of
+// Bm and Ou (4 KiB each), and writes 32 bytes of each of the chunk's 128
+// output rows (a partial line each).  Leaving each out in turn (timing only)
+// shortens a launch of 32 chunks by: Qp 8 us, the output stores 7 us, half
+// of Mt 4.5 us, the Bm slice 2.5 us (of 34).  The operands come in the
+// workspace orders the intra-chunk kernel
 // writes (store_block in gdr_intra_bf16.hip): Mt and Qp in matrix-core operand
 // order with the 32 k of a step permuted per lane group (k = 4q .. 4q + 3,
 // 16 + 4q .. 16 + 4q + 3), which the copy of S in LDS repeats, and Bm and Ou
@@ -267,17 +271,26 @@ __global__ __launch_bounds__(512, 1) void inter_bf16_kernel(
       for (int i = 0; i < 2; ++i)
         acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(s0, o.a[i][ks], acc[i], 0, 0, 0);
     }
-    // acc[i] = (Qp S^T)[r][v .. v + 3], r = rr0 + 16 i + r16, v = v0 + 4 q4;
-    // rows past the chunk's end go to the discard line (the store count
-    // stays fixed, so the memory waits of later steps stay exact)
+    // acc[i] = (Qp S^T)[r][v .. v + 3], r = rr0 + 16 i + r16, v = v0 + 4 q4.
+    // One 16-byte store per lane: a swap between neighbouring 16-lane rows
+    // (q4 = 2p, 2p + 1) gives the even row the 8 values of r = rr0 + r16 and
+    // the odd row those of r = rr0 + 16 + r16, columns v0 + 8 p ..  Rows past
+    // the chunk's end go to the discard line (the store count stays fixed, so
+    // the memory waits of later steps stay exact).
+    {
+      bf16x4 va, vb;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int r = rr0 + 16 * i + r16;
+      for (int x = 0; x < 4; ++x) {
+        va[x] = (bf)(acc[0][x] + (float)o.x[x]);
+        vb[x] = (bf)(acc[1][x] + (float)o.x[4 + x]);
+      }
+      const u32x2 a2 = __builtin_bit_cast(u32x2, va), b2 = __builtin_bit_cast(u32x2, vb);
+      const auto s0 = __builtin_amdgcn_permlane16_swap(a2[0], b2[0], false, false);
+      const auto s1 = __builtin_amdgcn_permlane16_swap(a2[1], b2[1], false, false);
+      const int odd = q4 & 1;
+      const int r = rr0 + 16 * odd + r16;
       bf* orow = r < e.y ? out + ((size_t)(e.x + r) * Nv + h) * 128 + v0 : discard;
-      bf16x4 v;
-#pragma unroll
-      for (int x = 0; x < 4; ++x) v[x] = (bf)(acc[i][x] + (float)o.x[4 * i + x]);
-      *reinterpret_cast<bf16x4*>(orow + 4 * q4) = v;
+      *reinterpret_cast<u32x4*>(orow + 4 * (q4 - odd)) = u32x4{s0[0], s1[0], s0[1], s1[1]};
     }
     buf ^= 1;
     lds_barrier();
