@@ -23,8 +23,8 @@
 //  * Every LDS address is a per-lane offset computed once at kernel start
 //    plus a compile-time constant (the 16-byte swizzle of a row depends only
 //    on the row's low bits and the lane), so fragment reads and tile stores
-//    cost no vector ALU work and the reads of one k-step are in flight
-//    together ahead of its matrix instructions.
+//    cost no vector ALU work, and the reads of the next k-step go out
+//    between the current step's matrix instructions.
 #include "gdr_device.h"
 #include "gdr_kernels.h"
 
