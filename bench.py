@@ -25,7 +25,8 @@ of the timed region.
 After the timed steps, outside the step: the prefill workload (T=4096) is
 timed the same way beside the chunk workload (``chunk_fwd_prefill``); both
 are also timed cold (``cold``), with a 512 MiB buffer written between calls
-so that no input is left in the 256 MB Infinity Cache.  Unless
+so that no input is left in the 256 MB Infinity Cache; the chunk workload
+with 64-token chunks is timed warm (``chunk_fwd_chunk64``).  Unless
 ``--chunk-only``: the decode step with its state stored in bf16
 (``decode_bf16_state``), ``gdr_recurrent_multi`` on 256 sequences x 4
 tokens (``multi_token``), the decode step with its conv update and gates
@@ -50,15 +51,16 @@ D = 128
 L = 128
 
 
-def alg_flops_chunk(lengths, Nqk, Nv):
-    """Algorithmic FLOPs of the chunkwise forward, split by the kernel that
-    performs each term: intra (Grams once per query/key head, the triangular
-    inverse, the U/W/P products on triangles) and inter (the three products
-    with the state: W S^T, Q S^T, V_new^T K)."""
+def alg_flops_chunk(lengths, Nqk, Nv, chunk=L):
+    """Algorithmic FLOPs of the chunkwise forward with chunks of `chunk`
+    tokens, split by the kernel that performs each term: intra (Grams once
+    per query/key head, the triangular inverse, the U/W/P products on
+    triangles) and inter (the three products with the state: W S^T, Q S^T,
+    V_new^T K)."""
     intra = inter = 0.0
     for n in lengths:
-        full, tail = divmod(int(n), L)
-        for ell, cnt in ((L, full), (tail, 1 if tail else 0)):
+        full, tail = divmod(int(n), chunk)
+        for ell, cnt in ((chunk, full), (tail, 1 if tail else 0)):
             if cnt == 0:
                 continue
             intra += cnt * (Nqk * 2 * D * ell * ell + Nv * (ell ** 3 / 3 + 3 * D * ell * (ell + 1)))
@@ -133,9 +135,9 @@ class ChunkLeg:
     """One chunk workload resident on the device, with its outputs and
     workspace, called through the timed entry point."""
 
-    def __init__(self, gdr, inp, dev, scale):
+    def __init__(self, gdr, inp, dev, scale, chunk=L):
         import torch
-        self.gdr, self.inp, self.scale = gdr, inp, scale
+        self.gdr, self.inp, self.scale, self.chunk = gdr, inp, scale, chunk
         dt = torch.bfloat16 if inp.dtype == "bf16" else torch.float32
         self.t = dict(q=torch.from_numpy(inp.q).to(dev, dt), k=torch.from_numpy(inp.k).to(dev, dt),
                       v=torch.from_numpy(inp.v).to(dev, dt), g=torch.from_numpy(inp.g).to(dev),
@@ -152,10 +154,11 @@ class ChunkLeg:
         t = self.t
         self.gdr.chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], t["cu"], t["s0"],
                            scale=self.scale, out=self.out, state_out=self.sout, workspace=self.ws,
-                           timings=timings)
+                           chunk=self.chunk, timings=timings)
 
     def flops(self):
-        return alg_flops_chunk(np.diff(self.inp.cu_seqlens).tolist(), self.inp.Nqk, self.inp.Nv)
+        return alg_flops_chunk(np.diff(self.inp.cu_seqlens).tolist(), self.inp.Nqk, self.inp.Nv,
+                               self.chunk)
 
     def summarise(self, tims, steps, call_ms):
         """The call's GPU time from stream events around untimed calls
@@ -370,6 +373,12 @@ def main() -> int:
         cold["prefill"] = time_chunk(leg1, args.steps, 1, flush)
     res["cold"] = cold
     del flush, leg1
+
+    # the same workload with 64-token chunks (GDR_FLAG_CHUNK64): same inputs
+    # and results up to rounding, twice the chunks
+    leg64 = ChunkLeg(gdr, leg.inp, dev, scale, chunk=64)
+    res["chunk_fwd_chunk64"] = time_chunk(leg64, args.steps, args.warmup)
+    del leg64
 
     if not args.chunk_only:
         res.update(extras(gdr, dec, Dd, dout, pre, cfg, args, dev, scale))
