@@ -555,13 +555,13 @@ def cpu_baseline(pre, scale):
     G = pre.Nv // pre.Nqk
     T0, T1 = int(pre.cu_seqlens[0]), int(pre.cu_seqlens[1])
 
-    def run(heads):
+    def run(heads, nthreads=nthr, t1=T1):
         j0, j1 = heads[0] // G, heads[-1] // G + 1
         t = time.perf_counter()
-        oracle.recurrent(pre.q[T0:T1, j0:j1], pre.k[T0:T1, j0:j1], pre.v[T0:T1, heads[0]:heads[-1] + 1],
-                         pre.g[T0:T1, heads[0]:heads[-1] + 1], pre.beta[T0:T1, heads[0]:heads[-1] + 1],
+        oracle.recurrent(pre.q[T0:t1, j0:j1], pre.k[T0:t1, j0:j1], pre.v[T0:t1, heads[0]:heads[-1] + 1],
+                         pre.g[T0:t1, heads[0]:heads[-1] + 1], pre.beta[T0:t1, heads[0]:heads[-1] + 1],
                          None if pre.state_in is None else pre.state_in[:1, heads[0]:heads[-1] + 1],
-                         np.array([0, T1 - T0], np.int32), scale, nthreads=nthr)
+                         np.array([0, t1 - T0], np.int32), scale, nthreads=nthreads)
         return time.perf_counter() - t
 
     heads = list(range(G))           # one query/key group first
@@ -581,9 +581,16 @@ def cpu_baseline(pre, scale):
                 break
     except OSError:
         pass
+    # one thread, on the first 4096 tokens of one query/key group (the T=4096
+    # prefill workload's length)
+    n1 = min(4096, T1 - T0)
+    dt1 = run(list(range(G)), nthreads=1, t1=T0 + n1)
+    single = {"value": round(n1 * G / pre.Nv / dt1, 1), "unit": "tokens/s", "cores": 1,
+              "sample": f"first {n1} tokens, value heads 0..{G - 1} of {pre.Nv}, {dt1:.2f} s"}
     return {"value": round(tok_s, 1), "unit": "tokens/s", "cores": nthr, "kind": "oracle",
             "sample": f"first sequence ({T1 - T0} tokens), value heads 0..{len(heads) - 1} of "
-                      f"{pre.Nv}, fp64 per-token recurrence, {dt:.1f} s on {cpu}"}
+                      f"{pre.Nv}, fp64 per-token recurrence, {dt:.1f} s on {cpu}",
+            "single_thread": single}
 
 
 if __name__ == "__main__":
