@@ -62,6 +62,8 @@ def test_tiny_fp32_config():
     ([640], 1, 4),                            # G = 4
     ([200, 57], 4, 4),                        # G = 1
     ([128, 256, 384], 2, 2),                  # whole chunks only
+    ([1000, 37], 1, 1),                       # a single head
+    ([513, 64, 3], 2, 8),                     # Nv = 8 (operator page), G = 4
 ])
 def test_ragged(dtype, lengths, Nqk, Nv):
     inp = make_inputs(lengths, Nqk, Nv, dtype=dtype, seed=11 + len(lengths), state_std=0.01)
