@@ -237,6 +237,10 @@ __global__ __launch_bounds__(512, 1) void inter_bf16_kernel(
 
   // ---------------- output waves: chunk rows rr0 .. rr0 + 31, the 16 state rows
   const int ow = w - 2, rr0 = 32 * ow;
+  // with 64-token chunks no chunk has rows past 63: the waves of rows 64 ..
+  // 127 have nothing to load or store (a wave that has ended no longer
+  // counts at the barriers)
+  if (rr0 >= chunks.L) return;
   struct Ops {
     bf16x8 a[2][4];     // rows rr0 + 16 i of Qp, k-step ks
     bf16x8 x;           // Ou[rr0 + 16 i + r16][v0 + 4 q ..], i = 0 (first 4), 1
