@@ -150,12 +150,13 @@ __device__ __forceinline__ f32x4 mma(const bf16x8& a, const bf16x8& b, const f32
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// A wave's 64x64 block of C = A B^T over k in [0, 128): A rows m0 + 16 i from
+// A wave's 64x64 block of C = A B^T over k in [0, 32 NK): A rows m0 + 16 i from
 // the tile at ABASE (ATR: read transposed, i.e. A(m, k) = X[k][m]), B rows
 // n0 + 16 j from BBASE likewise.  DB: the reads of k-step ks + 1 are issued
 // before the matrix instructions of step ks (two fragment sets); without it
-// one set, for phases where registers are short.
-template <uint32_t ABASE, bool ATR, uint32_t BBASE, bool BTR, bool DB = true>
+// one set, for phases where registers are short.  NK < 4 stops early (the
+// products over a chunk's token rows when no row past 32 NK exists).
+template <uint32_t ABASE, bool ATR, uint32_t BBASE, bool BTR, bool DB = true, int NK = 4>
 __device__ __forceinline__ void gemm64(f32x4 (&acc)[4][4], const Lds& s, const Lane& L) {
   constexpr int NS = DB ? 2 : 1;
   bf16x8 a[NS][4], b[NS][4];
@@ -173,15 +174,15 @@ __device__ __forceinline__ void gemm64(f32x4 (&acc)[4][4], const Lds& s, const L
   constexpr int NR = (ATR ? 8 : 4) + (BTR ? 8 : 4);   // LDS reads per k-step
   if (DB) load(0, 0);
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
+  for (int ks = 0; ks < NK; ++ks) {
     if (DB) __builtin_amdgcn_sched_barrier(0);
     if (!DB) load(0, ks);
-    else if (ks + 1 < 4) load((ks + 1) % NS, ks + 1);
+    else if (ks + 1 < NK) load((ks + 1) % NS, ks + 1);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = mma(a[ks % NS][i], b[ks % NS][j], acc[i][j]);
-    if (DB && ks + 1 < 4) {
+    if (DB && ks + 1 < NK) {
       // the next step's reads go out between this step's matrix instructions
 #pragma unroll
       for (int x = 0; x < NR; ++x) {
@@ -605,11 +606,16 @@ __device__ __forceinline__ void gram_mask(Lds& s, const Lane& L, P4& Pp, int m0,
   }
 }
 
+// HALF: every chunk has at most 64 tokens (64-token chunks), so the products
+// that contract over the chunk's token rows stop after two k-steps (rows past
+// a chunk's end carry zero factors, so the skipped steps only add zeros).
+template <bool HALF>
 __global__ __launch_bounds__(256, 2) void intra_bf16_kernel(
     const bf* __restrict__ q, const bf* __restrict__ k, const bf* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, Chunks chunks, int32_t Nqk,
     int32_t Nv, int32_t slot0, int32_t nseg, float scale, int norm, bf* __restrict__ inter,
     float* __restrict__ gam_out) {
+  constexpr int NKT = HALF ? 2 : 4;   // k-steps of the products over token rows
   __shared__ Lds s;
   // Workgroup id -> (chunk slot, value head).  Workgroups go to the 8 XCDs
   // round-robin by id; the G = Nv / Nqk value heads of one (slot, q/k head)
@@ -717,7 +723,7 @@ __global__ __launch_bounds__(256, 2) void intra_bf16_kernel(
   {
     f32x4 acc[4][4];
     zero(acc);
-    gemm64<kT0, false, kT1, false>(acc, s, L);
+    gemm64<kT0, false, kT1, false, true, NKT>(acc, s, L);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -735,7 +741,7 @@ __global__ __launch_bounds__(256, 2) void intra_bf16_kernel(
   {
     f32x4 acc[4][4];
     zero(acc);
-    gemm64<kT0, false, kT1, true, false>(acc, s, L);
+    gemm64<kT0, false, kT1, true, false, NKT>(acc, s, L);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -767,7 +773,7 @@ __global__ __launch_bounds__(256, 2) void intra_bf16_kernel(
   {
     f32x4 acc[4][4];
     zero(acc);
-    gemm64<kT1, true, kT0, false, false>(acc, s, L);
+    gemm64<kT1, true, kT0, false, false, NKT>(acc, s, L);
     // q is converted only here: without this the compiler hoists the
     // conversions of the first pieces into phase 9, whose scalings then
     // wait for the loads
@@ -798,7 +804,7 @@ __global__ __launch_bounds__(256, 2) void intra_bf16_kernel(
   {
     f32x4 acc[4][4];
     zero(acc);
-    gemm64<kT1, true, kT0, false>(acc, s, L);
+    gemm64<kT1, true, kT0, false, true, NKT>(acc, s, L);
     store_block<Lay::Frag>(dst + 0 * 128 * 128, acc, m0, n0, -1.0f);
   }
   lds_barrier();
@@ -811,7 +817,7 @@ __global__ __launch_bounds__(256, 2) void intra_bf16_kernel(
   {
     f32x4 acc[4][4];
     zero(acc);
-    gemm64<kT0, false, kT1, true>(acc, s, L);
+    gemm64<kT0, false, kT1, true, true, NKT>(acc, s, L);
     store_block<Lay::Bm>(dst + 2 * 128 * 128, acc, m0, n0, 1.0f);
   }
   lds_barrier();
@@ -824,7 +830,7 @@ __global__ __launch_bounds__(256, 2) void intra_bf16_kernel(
   {
     f32x4 acc[4][4];
     zero(acc);
-    gemm64<kT1, true, kT0, false>(acc, s, L);
+    gemm64<kT1, true, kT0, false, true, NKT>(acc, s, L);
     store_block<Lay::Ou>(dst + 3 * 128 * 128, acc, m0, n0, 1.0f);
   }
 }
@@ -837,8 +843,14 @@ hipError_t launch_intra_bf16(const __bf16* q, const __bf16* k, const __bf16* v, 
                              float* gam, hipStream_t stream, LaunchEvents ev) {
   const unsigned groups = (unsigned)nseg * (unsigned)Nqk;
   const unsigned blocks = (groups + 7u) / 8u * 8u * (unsigned)(Nv / Nqk);
-  hipExtLaunchKernelGGL(intra_bf16_kernel, dim3(blocks), dim3(256), 0, stream, ev.start, ev.stop,
-                        0, q, k, v, g, beta, chunks, Nqk, Nv, slot0, nseg, scale, norm, inter, gam);
+  if (chunks.L <= 64)
+    hipExtLaunchKernelGGL(intra_bf16_kernel<true>, dim3(blocks), dim3(256), 0, stream, ev.start,
+                          ev.stop, 0, q, k, v, g, beta, chunks, Nqk, Nv, slot0, nseg, scale, norm,
+                          inter, gam);
+  else
+    hipExtLaunchKernelGGL(intra_bf16_kernel<false>, dim3(blocks), dim3(256), 0, stream, ev.start,
+                          ev.stop, 0, q, k, v, g, beta, chunks, Nqk, Nv, slot0, nseg, scale, norm,
+                          inter, gam);
   return hipGetLastError();
 }
 
