@@ -150,13 +150,15 @@ __device__ __forceinline__ f32x4 mma(const bf16x8& a, const bf16x8& b, const f32
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// A wave's 64x64 block of C = A B^T over k in [0, 32 NK): A rows m0 + 16 i from
+// A wave's 64x64 block of C = A B^T over k in [32 KB, 32 KE): A rows m0 + 16 i from
 // the tile at ABASE (ATR: read transposed, i.e. A(m, k) = X[k][m]), B rows
 // n0 + 16 j from BBASE likewise.  DB: the reads of k-step ks + 1 are issued
 // before the matrix instructions of step ks (two fragment sets); without it
-// one set, for phases where registers are short.  NK < 4 stops early (the
-// products over a chunk's token rows when no row past 32 NK exists).
-template <uint32_t ABASE, bool ATR, uint32_t BBASE, bool BTR, bool DB = true, int NK = 4>
+// one set, for phases where registers are short.  A k range narrower than
+// [0, 4) serves products over token rows where the other rows contribute
+// exact zeros (a pair of 64-token chunks).
+template <uint32_t ABASE, bool ATR, uint32_t BBASE, bool BTR, bool DB = true, int KB = 0,
+          int KE = 4>
 __device__ __forceinline__ void gemm64(f32x4 (&acc)[4][4], const Lds& s, const Lane& L) {
   constexpr int NS = DB ? 2 : 1;
   bf16x8 a[NS][4], b[NS][4];
@@ -172,17 +174,18 @@ __device__ __forceinline__ void gemm64(f32x4 (&acc)[4][4], const Lds& s, const L
                       : rd16(s, BBASE + L.fb[ks] + 4096u * j);
   };
   constexpr int NR = (ATR ? 8 : 4) + (BTR ? 8 : 4);   // LDS reads per k-step
-  if (DB) load(0, 0);
+  if (DB) load(0, KB);
 #pragma unroll
-  for (int ks = 0; ks < NK; ++ks) {
+  for (int ks = KB; ks < KE; ++ks) {
     if (DB) __builtin_amdgcn_sched_barrier(0);
     if (!DB) load(0, ks);
-    else if (ks + 1 < NK) load((ks + 1) % NS, ks + 1);
+    else if (ks + 1 < KE) load((ks - KB + 1) % NS, ks + 1);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mma(a[ks % NS][i], b[ks % NS][j], acc[i][j]);
-    if (DB && ks + 1 < NK) {
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = mma(a[(ks - KB) % NS][i], b[(ks - KB) % NS][j], acc[i][j]);
+    if (DB && ks + 1 < KE) {
       // the next step's reads go out between this step's matrix instructions
 #pragma unroll
       for (int x = 0; x < NR; ++x) {
@@ -193,6 +196,14 @@ __device__ __forceinline__ void gemm64(f32x4 (&acc)[4][4], const Lds& s, const L
     }
     if (DB) __builtin_amdgcn_sched_barrier(0);
   }
+}
+
+// gemm64 over the k-steps of one 64-row half: [0, 2) for hi == 0, else [2, 4)
+// (hi is uniform over the wave).
+template <uint32_t ABASE, bool ATR, uint32_t BBASE, bool BTR, bool DB = true>
+__device__ __forceinline__ void gemm64_half(f32x4 (&acc)[4][4], const Lds& s, const Lane& L, int hi) {
+  if (hi) gemm64<ABASE, ATR, BBASE, BTR, DB, 2, 4>(acc, s, L);
+  else gemm64<ABASE, ATR, BBASE, BTR, DB, 0, 2>(acc, s, L);
 }
 
 template <int M, int N>
@@ -241,6 +252,21 @@ struct Pieces {
       const int r = (int)(t >> 4) + 16 * it;
       const uint32_t rr = (uint32_t)min(r, len - 1);
       p[it] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(src) + (rr * gs + c) * 2u);
+    }
+  }
+  // Rows 0..63 from chunk A (la rows at srcA), rows 64..127 from chunk B (lb
+  // at srcB), each half clamped to its own last row like `load` (la, lb >= 1).
+  __device__ __forceinline__ void load_pair(const bf* srcA, int la, const bf* srcB, int lb,
+                                            uint32_t gs) {
+    uint32_t t = threadIdx.x;
+    asm volatile("" : "+v"(t));
+    const uint32_t c = (t & 15u) * 8u;
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int r = (int)(t >> 4) + 16 * (it & 3);   // row within the half
+      const uint32_t rr = (uint32_t)min(r, (it < 4 ? la : lb) - 1);
+      p[it] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(it < 4 ? srcA : srcB) +
+                                              (rr * gs + c) * 2u);
     }
   }
   // sum of squares of piece it, bf16 pairs on the dot-product unit (the
@@ -518,11 +544,23 @@ __device__ __forceinline__ void store_block(bf* dst, const f32x4 (&acc)[4][4], i
 // Tiles strictly below the diagonal need K K^T (g1: k_a . k_c, for A+), tiles
 // above it K Q^T (g2: k_a . q_c, for P), diagonal tiles both; rows
 // a = m0 + 16 i + 4 q + x, columns c = n0 + 16 j + r16.  WT: 0 = block on the
-// diagonal, 1 = block above it (P only), 2 = block below it (N only).
+// diagonal, 1 = block above it (P only), 2 = block below it (N only), 3 = a
+// block between the two chunks of a pair (no terms: zeros).
 // The barrier between the products and the mask is inside.
 template <int WT>
 __device__ __forceinline__ void gram_mask(Lds& s, const Lane& L, P4& Pp, int m0, int n0) {
   const uint32_t l = threadIdx.x & 63u, r16 = l & 15u, qd = l >> 4;
+  if (WT == 3) {
+    lds_barrier();   // the other waves' Grams still read the slots
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        Pp.set(i, jj, 0.f, 0.f, 0.f, 0.f);
+        wr8(s, kT0 + L.pt[i] + 4096u * jj, 0.f, 0.f, 0.f, 0.f);
+      }
+    return;
+  }
   f32x4 g1[4][4], g2[4][4];
   zero(g1);
   zero(g2);
@@ -606,49 +644,84 @@ __device__ __forceinline__ void gram_mask(Lds& s, const Lane& L, P4& Pp, int m0,
   }
 }
 
-// HALF: every chunk has at most 64 tokens (64-token chunks), so the products
-// that contract over the chunk's token rows stop after two k-steps (rows past
-// a chunk's end carry zero factors, so the skipped steps only add zeros).
-template <bool HALF>
+// PAIR: 64-token chunks, two per workgroup.  Chunk slots 2u (rows 0..63)
+// and 2u + 1 (rows 64..127) of the segment share the unit's 128 rows; their
+// gate cumsums restart at row 64, every term between the two chunks is zero
+// (the Grams' cross blocks are not formed), so T, R and Z come out block
+// diagonal, and the products over token rows take only the k-steps of the
+// half they need.  M' and Bm, which sum over a chunk's rows, are formed per
+// chunk from its half of the k range.  Each chunk's matrices go to its own
+// slot in the workspace (Qp and Ou in rows 0..63, the rows the state pass
+// reads for 64-token chunks).
+template <bool PAIR>
 __global__ __launch_bounds__(256, 2) void intra_bf16_kernel(
     const bf* __restrict__ q, const bf* __restrict__ k, const bf* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, Chunks chunks, int32_t Nqk,
     int32_t Nv, int32_t slot0, int32_t nseg, float scale, int norm, bf* __restrict__ inter,
     float* __restrict__ gam_out) {
-  constexpr int NKT = HALF ? 2 : 4;   // k-steps of the products over token rows
   __shared__ Lds s;
-  // Workgroup id -> (chunk slot, value head).  Workgroups go to the 8 XCDs
-  // round-robin by id; the G = Nv / Nqk value heads of one (slot, q/k head)
-  // read the same k and q rows, so they are given ids with the same id % 8
-  // and share that XCD's L2.  Groups p = slot * Nqk + j are dealt in order;
-  // ids past the last group (the grid is padded to whole rounds of 8 G) exit.
+  // Workgroup id -> (unit, value head); a unit is one chunk slot, or two
+  // (PAIR).  Workgroups go to the 8 XCDs round-robin by id; the G = Nv / Nqk
+  // value heads of one (unit, q/k head) read the same k and q rows, so they
+  // are given ids with the same id % 8 and share that XCD's L2.  Groups
+  // p = unit * Nqk + j are dealt in order; ids past the last group (the grid
+  // is padded to whole rounds of 8 G) exit.
+  const int units = PAIR ? (nseg + 1) / 2 : nseg;
   const int G = Nv / Nqk;
   const int id = blockIdx.x, xcd = id & 7, r = id >> 3;
   const int p = (r / G) * 8 + xcd;
-  if (p >= nseg * Nqk) return;
-  const int local_slot = p / Nqk, j = p % Nqk, h = j * G + r % G;
-  int start, len;
-  if (!chunks.slot(slot0 + local_slot, start, len)) return;
+  if (p >= units * Nqk) return;
+  const int unit = p / Nqk, j = p % Nqk, h = j * G + r % G;
+  // the unit's chunks: A (rows 0..63, or all 128) and B (rows 64..127, PAIR)
+  const int slA = PAIR ? 2 * unit : unit, slB = slA + 1;
+  int sa = 0, la = 0, sb = 0, lb = 0;
+  const bool hasA = chunks.slot(slot0 + slA, sa, la);
+  const bool hasB = PAIR && slB < nseg && chunks.slot(slot0 + slB, sb, lb);
+  if (!hasA && !hasB) return;
+  if (!hasA) { sa = sb; la = 0; }
+  if (!hasB) { sb = sa; lb = 0; }
+  // uniform over the workgroup: kept in scalar registers
+  sa = __builtin_amdgcn_readfirstlane(sa);
+  la = __builtin_amdgcn_readfirstlane(la);
+  sb = __builtin_amdgcn_readfirstlane(sb);
+  lb = __builtin_amdgcn_readfirstlane(lb);
+  // rows past a chunk's end repeat its last row (an absent chunk: the other
+  // one's first row); every factor of such a row is zero
+  const int lac = max(la, 1), lbc = max(lb, 1);
+  const int len = PAIR ? 0 : la;   // the single chunk's length
   const int tid = threadIdx.x, l = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int m0 = 64 * (w >> 1), n0 = 64 * (w & 1);
   const uint32_t r16 = l & 15, qd = l >> 4;
   const uint32_t qk_gs = (uint32_t)Nqk * 128u, v_gs = (uint32_t)Nv * 128u;
-  const bf* kc = k + ((size_t)start * Nqk + j) * 128;
-  const bf* qc = q + ((size_t)start * Nqk + j) * 128;
-  const bf* vc = v + ((size_t)start * Nv + h) * 128;
-  bf* dst = inter + ((size_t)local_slot * Nv + h) * 4 * (size_t)(128 * 128);
+  const bf* kc = k + ((size_t)sa * Nqk + j) * 128;
+  const bf* qc = q + ((size_t)sa * Nqk + j) * 128;
+  const bf* vc = v + ((size_t)sa * Nv + h) * 128;
+  // chunk B's rows and matrices, formed where they are used
+  auto rowsB = [&](const bf* base, uint32_t gs, int hh) { return base + ((size_t)sb * gs / 128 + hh) * 128; };
+  bf* dst = inter + ((size_t)slA * Nv + h) * 4 * (size_t)(128 * 128);
+  auto dstB = [&]() { return dst + (size_t)Nv * 4 * (128 * 128); };   // slot slA + 1
+  // row r of the unit is a real token row
+  auto valid = [&](int row) { return PAIR ? (row < 64 ? row < la : row - 64 < lb) : row < len; };
   const Lane L = make_lane(m0, n0);
 
   // ---- 1. k, q rows; norms; gate cumsum (fp64, waves 0 and 1)
   Pieces kr, qr;
-  kr.load(kc, qk_gs, len);
-  qr.load(qc, qk_gs, len);
+  if (PAIR) {
+    kr.load_pair(kc, lac, rowsB(k, qk_gs, j), lbc, qk_gs);
+    qr.load_pair(qc, lac, rowsB(q, qk_gs, j), lbc, qk_gs);
+  } else {
+    kr.load(kc, qk_gs, len);
+    qr.load(qc, qk_gs, len);
+  }
   double gsum = 0.0;
   float bt = 0.0f;
   if (tid < 128) {
-    const bool ok = tid < len;
-    const size_t gi = (size_t)(start + min(tid, len - 1)) * Nv + h;
+    // row tid; in PAIR mode wave 0 holds chunk A's rows and wave 1 chunk B's
+    const int row = PAIR ? l : tid;
+    const int st = PAIR && w == 1 ? sb : sa, ln = PAIR ? (w == 1 ? lb : la) : len;
+    const bool ok = row < ln;
+    const size_t gi = (size_t)(st + min(row, max(ln, 1) - 1)) * Nv + h;
     const float gv = g[gi], bv = beta[gi];
     gsum = ok ? (double)gv : 0.0;
     bt = ok ? bv : 0.0f;
@@ -675,9 +748,9 @@ __global__ __launch_bounds__(256, 2) void intra_bf16_kernel(
 #pragma unroll
     for (int x = 1; x < 8; ++x)
       if (it == x) ss = isq ? ssq[x] : ssk[x];
-    const int r = (tid >> 4) + 16 * it;
+    const int row = (tid >> 4) + 16 * it;
     const float f = (norm ? __builtin_amdgcn_rsqf(ss + 1e-6f) : 1.0f) * (isq ? scale : 1.0f);
-    (isq ? s.rq : s.rk)[r] = r < len ? f : 0.0f;
+    (isq ? s.rq : s.rk)[row] = valid(row) ? f : 0.0f;
   }
   kr.store<kT0>(s, L);
   qr.store<kT1>(s, L);
@@ -685,8 +758,9 @@ __global__ __launch_bounds__(256, 2) void intra_bf16_kernel(
 
   // ---- 2. per-row factors (waves 0, 1) and the Grams of the raw rows
   if (tid < 128) {
-    const double gcd = gsum + (w == 1 ? s.part[0] : 0.0);
-    const double glast = s.part[0] + s.part[1];
+    // a pair's second chunk starts its own cumsum at row 64
+    const double gcd = PAIR ? gsum : gsum + (w == 1 ? s.part[0] : 0.0);
+    const double glast = PAIR ? s.part[w] : s.part[0] + s.part[1];
     const float e = __expf((float)gcd), rk = s.rk[tid];
     s.gc[tid] = (float)(gcd * 1.4426950408889634);   // in log2 units, for the mask
     s.beta[tid] = bt;
@@ -694,11 +768,17 @@ __global__ __launch_bounds__(256, 2) void intra_bf16_kernel(
     s.ck[tid] = __expf((float)(glast - gcd)) * rk;
     s.xk[tid] = bt * e * rk;
     s.qs[tid] = e * s.rq[tid];
-    if (tid == 0) gam_out[(size_t)(slot0 + local_slot) * Nv + h] = __expf((float)glast);
+    if (PAIR) {
+      if (l == 0 && (w == 0 ? hasA : hasB))
+        gam_out[(size_t)(slot0 + (w == 0 ? slA : slB)) * Nv + h] = __expf((float)glast);
+    } else if (tid == 0) {
+      gam_out[(size_t)(slot0 + slA) * Nv + h] = __expf((float)glast);
+    }
   }
   // ---- 3. Grams and decay mask, one code path per kind of wave block
   P4 Pp;
-  if (m0 > n0) gram_mask<2>(s, L, Pp, m0, n0);
+  if (PAIR && m0 != n0) gram_mask<3>(s, L, Pp, m0, n0);
+  else if (m0 > n0) gram_mask<2>(s, L, Pp, m0, n0);
   else if (m0 < n0) gram_mask<1>(s, L, Pp, m0, n0);
   else gram_mask<0>(s, L, Pp, m0, n0);
   // zero slot 1: the lower form of the inverse is built into it
@@ -709,7 +789,8 @@ __global__ __launch_bounds__(256, 2) void intra_bf16_kernel(
 
   // k rows for phase 7, loaded now so the inverse hides their latency
   Pieces kn;
-  kn.load(kc, qk_gs, len);
+  if (PAIR) kn.load_pair(kc, lac, rowsB(k, qk_gs, j), lbc, qk_gs);
+  else kn.load(kc, qk_gs, len);
 
   // ---- 4. T^T = (I + N)^-1 in slot 0
   invert_unit_upper(s);
@@ -719,11 +800,13 @@ __global__ __launch_bounds__(256, 2) void intra_bf16_kernel(
   lds_barrier();
 
   // ---- 6. R^T = T^T P^T: acc[j][r] = sum_i T^T[j][i] P[r][i] = R[r][j]
+  // (PAIR: zero between the chunks; within one, i runs over its half)
   P4 Rp;
   {
     f32x4 acc[4][4];
     zero(acc);
-    gemm64<kT0, false, kT1, false, true, NKT>(acc, s, L);
+    if (!PAIR) gemm64<kT0, false, kT1, false>(acc, s, L);
+    else if (m0 == n0) gemm64_half<kT0, false, kT1, false>(acc, s, L, m0);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -737,11 +820,13 @@ __global__ __launch_bounds__(256, 2) void intra_bf16_kernel(
   lds_barrier();
 
   // ---- 8. Z = T^T diag(ck) K:  acc[j][d] = sum_i (T^T ck)[j][i] K[i][d]
+  // (PAIR: i over the half of row j)
   P4 Zp;
   {
     f32x4 acc[4][4];
     zero(acc);
-    gemm64<kT0, false, kT1, true, false, NKT>(acc, s, L);
+    if (!PAIR) gemm64<kT0, false, kT1, true, false>(acc, s, L);
+    else gemm64_half<kT0, false, kT1, true, false>(acc, s, L, m0);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -753,13 +838,18 @@ __global__ __launch_bounds__(256, 2) void intra_bf16_kernel(
   // d = m0 + 16 i + 4 qd), loaded here so phase 9 and the product hide them
   // (rows past the chunk's end repeat its last row; their qs is zero)
   bf16x4 qx[4][4];
+  {
+    // PAIR: a wave's rows r all lie in one chunk (n0 = 0: A, 64: B)
+    const bf* qsrc = PAIR && n0 ? rowsB(q, qk_gs, j) : qc;
+    const int rbase = PAIR ? 0 : n0, rlen = PAIR ? (n0 ? lbc : lac) : len;
 #pragma unroll
-  for (int jj = 0; jj < 4; ++jj) {
-    const uint32_t rr = (uint32_t)min(n0 + 16 * jj + (int)r16, len - 1);
+    for (int jj = 0; jj < 4; ++jj) {
+      const uint32_t rr = (uint32_t)min(rbase + 16 * jj + (int)r16, rlen - 1);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      qx[i][jj] = *reinterpret_cast<const bf16x4*>(
-          reinterpret_cast<const char*>(qc) + (rr * qk_gs + (uint32_t)(m0 + 16 * i) + 4u * qd) * 2u);
+      for (int i = 0; i < 4; ++i)
+        qx[i][jj] = *reinterpret_cast<const bf16x4*>(
+            reinterpret_cast<const char*>(qsrc) + (rr * qk_gs + (uint32_t)(m0 + 16 * i) + 4u * qd) * 2u);
+    }
   }
 
   // ---- 9. k rows times xk in slot 1 (both products with K take diag(xk) on
@@ -769,11 +859,13 @@ __global__ __launch_bounds__(256, 2) void intra_bf16_kernel(
   lds_barrier();
 
   // ---- 10. Qp = diag(qs) q - R (xk K):  acc[d][r] = sum_j (xk K)^T[d][j] R[r][j]
+  // (PAIR: j over the half of row r)
   Pieces vn;
   {
     f32x4 acc[4][4];
     zero(acc);
-    gemm64<kT1, true, kT0, false, false, NKT>(acc, s, L);
+    if (!PAIR) gemm64<kT1, true, kT0, false, false>(acc, s, L);
+    else gemm64_half<kT1, true, kT0, false, false>(acc, s, L, n0);
     // q is converted only here: without this the compiler hoists the
     // conversions of the first pieces into phase 9, whose scalings then
     // wait for the loads
@@ -791,8 +883,12 @@ __global__ __launch_bounds__(256, 2) void intra_bf16_kernel(
     }
     // v rows for phase 13 go out between the product and its stores (a
     // wave's memory counter retires in order)
-    vn.load(vc, v_gs, len);
-    store_block<Lay::Frag>(dst + 1 * 128 * 128, acc, m0, n0, 1.0f);
+    if (PAIR) vn.load_pair(vc, lac, rowsB(v, v_gs, h), lbc, v_gs);
+    else vn.load(vc, v_gs, len);
+    // PAIR: rows 64..127 are chunk B's rows 0..63
+    if (!PAIR) store_block<Lay::Frag>(dst + 1 * 128 * 128, acc, m0, n0, 1.0f);
+    else if (n0 ? hasB : hasA)
+      store_block<Lay::Frag>((n0 ? dstB() : dst) + 1 * 128 * 128, acc, m0, 0, 1.0f);
   }
   lds_barrier();
 
@@ -801,11 +897,25 @@ __global__ __launch_bounds__(256, 2) void intra_bf16_kernel(
   lds_barrier();
 
   // ---- 12. M' = -(xk K)^T Z:  acc[e][d] = sum_j (xk K)^T[e][j] Z^T[d][j];  Mt[d][e] = -acc
-  {
+  // (PAIR: one M' per chunk, j over its half)
+  if (!PAIR) {
     f32x4 acc[4][4];
     zero(acc);
-    gemm64<kT1, true, kT0, false, true, NKT>(acc, s, L);
+    gemm64<kT1, true, kT0, false>(acc, s, L);
     store_block<Lay::Frag>(dst + 0 * 128 * 128, acc, m0, n0, -1.0f);
+  } else {
+    {
+      f32x4 acc[4][4];
+      zero(acc);
+      gemm64<kT1, true, kT0, false, true, 0, 2>(acc, s, L);
+      if (hasA) store_block<Lay::Frag>(dst + 0 * 128 * 128, acc, m0, n0, -1.0f);
+    }
+    {
+      f32x4 acc[4][4];
+      zero(acc);
+      gemm64<kT1, true, kT0, false, true, 2, 4>(acc, s, L);
+      if (hasB) store_block<Lay::Frag>(dstB() + 0 * 128 * 128, acc, m0, n0, -1.0f);
+    }
   }
   lds_barrier();
 
@@ -814,11 +924,25 @@ __global__ __launch_bounds__(256, 2) void intra_bf16_kernel(
   lds_barrier();
 
   // ---- 14. Bm = (beta V)^T Z:  acc[d][e] = sum_j Z^T[d][j] (beta V)^T[e][j];  Bm[e][d]
-  {
+  // (PAIR: one Bm per chunk, j over its half)
+  if (!PAIR) {
     f32x4 acc[4][4];
     zero(acc);
-    gemm64<kT0, false, kT1, true, true, NKT>(acc, s, L);
+    gemm64<kT0, false, kT1, true>(acc, s, L);
     store_block<Lay::Bm>(dst + 2 * 128 * 128, acc, m0, n0, 1.0f);
+  } else {
+    {
+      f32x4 acc[4][4];
+      zero(acc);
+      gemm64<kT0, false, kT1, true, true, 0, 2>(acc, s, L);
+      if (hasA) store_block<Lay::Bm>(dst + 2 * 128 * 128, acc, m0, n0, 1.0f);
+    }
+    {
+      f32x4 acc[4][4];
+      zero(acc);
+      gemm64<kT0, false, kT1, true, true, 2, 4>(acc, s, L);
+      if (hasB) store_block<Lay::Bm>(dstB() + 2 * 128 * 128, acc, m0, n0, 1.0f);
+    }
   }
   lds_barrier();
 
@@ -827,11 +951,15 @@ __global__ __launch_bounds__(256, 2) void intra_bf16_kernel(
   lds_barrier();
 
   // ---- 16. Ou = R (beta V):  acc[e][r] = sum_j (beta V)^T[e][j] R[r][j];  Ou[r][e]
+  // (PAIR: j over the half of row r; rows 64..127 are chunk B's rows 0..63)
   {
     f32x4 acc[4][4];
     zero(acc);
-    gemm64<kT1, true, kT0, false, true, NKT>(acc, s, L);
-    store_block<Lay::Ou>(dst + 3 * 128 * 128, acc, m0, n0, 1.0f);
+    if (!PAIR) gemm64<kT1, true, kT0, false>(acc, s, L);
+    else gemm64_half<kT1, true, kT0, false>(acc, s, L, n0);
+    if (!PAIR) store_block<Lay::Ou>(dst + 3 * 128 * 128, acc, m0, n0, 1.0f);
+    else if (n0 ? hasB : hasA)
+      store_block<Lay::Ou>((n0 ? dstB() : dst) + 3 * 128 * 128, acc, m0, 0, 1.0f);
   }
 }
 
@@ -841,9 +969,12 @@ hipError_t launch_intra_bf16(const __bf16* q, const __bf16* k, const __bf16* v, 
                              const float* beta, Chunks chunks, int32_t Nqk, int32_t Nv,
                              int32_t slot0, int32_t nseg, float scale, int norm, __bf16* inter,
                              float* gam, hipStream_t stream, LaunchEvents ev) {
-  const unsigned groups = (unsigned)nseg * (unsigned)Nqk;
+  // 64-token chunks go two per workgroup
+  const bool pair = chunks.L <= 64;
+  const unsigned units = pair ? ((unsigned)nseg + 1u) / 2u : (unsigned)nseg;
+  const unsigned groups = units * (unsigned)Nqk;
   const unsigned blocks = (groups + 7u) / 8u * 8u * (unsigned)(Nv / Nqk);
-  if (chunks.L <= 64)
+  if (pair)
     hipExtLaunchKernelGGL(intra_bf16_kernel<true>, dim3(blocks), dim3(256), 0, stream, ev.start,
                           ev.stop, 0, q, k, v, g, beta, chunks, Nqk, Nv, slot0, nseg, scale, norm,
                           inter, gam);
