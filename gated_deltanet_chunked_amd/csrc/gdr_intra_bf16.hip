@@ -443,6 +443,9 @@ __device__ __forceinline__ void merge_level(Lds& s, int w, int l) {
   lds_barrier();
 }
 
+// BLOCKDIAG: the 64-row halves are independent (a pair of 64-token chunks):
+// the last merge would only form the zero block between them, and is left out.
+template <bool BLOCKDIAG = false>
 __device__ __forceinline__ void invert_unit_upper(Lds& s) {
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   // 16x16 diagonal blocks by back substitution, one column per thread (the
@@ -498,7 +501,7 @@ __device__ __forceinline__ void invert_unit_upper(Lds& s) {
   lds_barrier();
   merge_level<16>(s, w, l);
   merge_level<32>(s, w, l);
-  merge_level<64>(s, w, l);
+  if (!BLOCKDIAG) merge_level<64>(s, w, l);
 }
 
 // Global store of a 64x64 accumulator block, transposed, in one of the bf16
@@ -793,7 +796,7 @@ __global__ __launch_bounds__(256, 2) void intra_bf16_kernel(
   else kn.load(kc, qk_gs, len);
 
   // ---- 4. T^T = (I + N)^-1 in slot 0
-  invert_unit_upper(s);
+  invert_unit_upper<PAIR>(s);
 
   // ---- 5. P into slot 1 (rows r: P[r][i])
   put_t<kT1>(s, Pp, L);
