@@ -25,6 +25,8 @@
 //    on the row's low bits and the lane), so fragment reads and tile stores
 //    cost no vector ALU work, and the reads of the next k-step go out
 //    between the current step's matrix instructions.
+//  * 64-token chunks go two to a workgroup, as a block-diagonal 128-row unit
+//    (the PAIR instantiation of the kernel).
 #include "gdr_device.h"
 #include "gdr_kernels.h"
 
