@@ -86,3 +86,14 @@ def test_chunk64_timed_and_no_alloc_match():
                            sout, scale=SCALE, chunk=64)
     torch.cuda.synchronize()
     assert np.array_equal(to_f64(out), o) and np.array_equal(to_f64(sout), s)
+
+
+def test_chunk64_odd_segments_all_heads():
+    """T = 4160 (65 chunks of 64 tokens) at Nqk = 16, Nv = 32: the segments
+    hold 33 and 32 chunk slots, so the first segment ends with a pair whose
+    second chunk is absent, and the state crosses a segment boundary in the
+    middle of the sequence.  Every head against the oracle."""
+    inp = make_inputs([65 * 64], 16, 32, dtype="bf16", seed=77, state_std=0.01)
+    out, st = _chunk(inp, 64)
+    ro, rs = oracle_full(inp)
+    assert_close_per_seq_head(out, ro, st, rs, inp.cu_seqlens, TOL["bf16"], name="L=64 odd segments")
