@@ -352,3 +352,31 @@ def test_timed_call_with_fewer_slots_than_launches_times_the_span():
     torch.cuda.synchronize()
     assert rc == 0 and n.value == 0 and span.value > 0
     assert torch.equal(out, ref_o) and torch.equal(st, ref_s)
+
+
+# ------------------------------------------------------- many sequences
+
+
+@pytest.mark.parametrize("dtype,chunk", [("f32", 128), ("bf16", 128), ("bf16", 64)])
+def test_many_short_sequences(dtype, chunk):
+    """1,500 packed sequences, most of 0-39 tokens (empty and one-token ones
+    among them) and every 200th of 600 tokens: more sequences than the chunk
+    table's 1,024 threads (several per thread), more chunk slots than one
+    segment holds (the long sequences span segment boundaries and carry their
+    state), and, with 64-token chunks, pairs of slots from different
+    sequences in one workgroup of the intra-chunk kernel."""
+    rng = np.random.default_rng(120)
+    lengths = rng.integers(0, 40, size=1500)
+    lengths[::200] = 600
+    inp = make_inputs(lengths, 1, 2, dtype=dtype, seed=121, state_std=0.1)
+    import torch
+    t = device_tensors(inp)
+    out, st = gdr.chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], t["cu"], t["state_in"],
+                            scale=SCALE, chunk=chunk)
+    torch.cuda.synchronize()
+    ro, rs = oracle_full(inp)
+    assert_close_per_seq_head(to_f64(out), ro, to_f64(st), rs, inp.cu_seqlens, TOL[dtype],
+                              name=f"N=1500 {dtype} L={chunk}")
+    empty = np.flatnonzero(lengths == 0)
+    assert empty.size > 0
+    assert np.array_equal(to_f64(st)[empty], inp.state_in[empty].astype(np.float64))
