@@ -251,15 +251,14 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
     import gated_deltanet_chunked_amd as gdr
-    from gated_deltanet_chunked_amd.inputs import config_inputs, CONFIG_NAMES
+    from gated_deltanet_chunked_amd.inputs import WORKLOAD_SEEDS, WORKLOADS, workload_inputs
     gdr.load()   # raises if libgdr.so is missing: there is no fallback
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     scale = D ** -0.5
 
-    cfg = {"prefill": 1, "varlen": 2, "long": 3}[args.workload]
-    pre = config_inputs(cfg)
-    dec = config_inputs(4)
+    pre = workload_inputs(args.workload)
+    dec = workload_inputs("decode")
     leg = ChunkLeg(gdr, pre, dev, scale)
     T, N, Nqk, Nv = pre.T, pre.N, pre.Nqk, pre.Nv
 
@@ -348,7 +347,7 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded; distributions of the Qwen3-Next gate initialisation)",
-        "config": {"workload": CONFIG_NAMES[cfg] + " + " + CONFIG_NAMES[4],
+        "config": {"workload": WORKLOADS[args.workload] + " + " + WORKLOADS["decode"],
                    "tokens": T, "sequences": N, "Nqk": Nqk, "Nv": Nv, "D": D, "chunk": L,
                    "decode_sequences": dec.N},
         "chunk_fwd": chunk,
@@ -362,14 +361,14 @@ def main() -> int:
     # ---- beside the step: the prefill workload, and cold (Infinity Cache
     # flushed) figures of both chunk workloads
     flush = torch.zeros(1 << 27, dtype=torch.float32, device=dev)   # 512 MiB
-    if cfg != 1:
-        leg1 = ChunkLeg(gdr, config_inputs(1), dev, scale)
+    if args.workload != "prefill":
+        leg1 = ChunkLeg(gdr, workload_inputs("prefill"), dev, scale)
         res["chunk_fwd_prefill"] = time_chunk(leg1, args.steps, args.warmup)
     else:
         leg1 = leg
     cold = {"what": "512 MiB buffer written before every call; same calls otherwise"}
     cold[args.workload] = time_chunk(leg, args.steps, 1, flush)
-    if cfg != 1:
+    if args.workload != "prefill":
         cold["prefill"] = time_chunk(leg1, args.steps, 1, flush)
     res["cold"] = cold
     del flush, leg1
@@ -381,14 +380,14 @@ def main() -> int:
     del leg64
 
     if not args.chunk_only:
-        res.update(extras(gdr, dec, Dd, dout, pre, cfg, args, dev, scale))
+        res.update(extras(gdr, dec, Dd, dout, pre, WORKLOAD_SEEDS[args.workload], args, dev, scale))
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(pre, scale)
     print(json.dumps(res), flush=True)
     return 0
 
 
-def extras(gdr, dec, Dd, dout, pre, cfg, args, dev, scale):
+def extras(gdr, dec, Dd, dout, pre, seed, args, dev, scale):
     """The decode variants and the prefill prologue, measured after the timed
     steps and reported beside them (not part of the step)."""
     import torch
@@ -474,9 +473,9 @@ def extras(gdr, dec, Dd, dout, pre, cfg, args, dev, scale):
     # and fused into the decode step
     from gated_deltanet_chunked_amd.inputs import make_gate
     rows = T * Nv
-    nx = torch.randn((T, Nv, D), device=dev, generator=torch.Generator(device=dev).manual_seed(cfg))
+    nx = torch.randn((T, Nv, D), device=dev, generator=torch.Generator(device=dev).manual_seed(seed))
     nx = nx.to(torch.bfloat16)
-    z, w = make_gate((T, Nv, D), seed=cfg)
+    z, w = make_gate((T, Nv, D), seed=seed)
     nz = torch.from_numpy(z).to(dev, torch.bfloat16)
     nw = torch.from_numpy(w).to(dev, torch.bfloat16)
     ny = torch.empty_like(nx)
@@ -519,7 +518,7 @@ def extras(gdr, dec, Dd, dout, pre, cfg, args, dev, scale):
     # the conv/gate prologue of the chunked path (gdr_conv_prefill) on the
     # chunk workload's tokens: cached windows in, new windows out
     from gated_deltanet_chunked_amd.inputs import prefill_prologue_inputs
-    pp = prefill_prologue_inputs(np.diff(pre.cu_seqlens).tolist(), Nqk, Nv, seed=cfg)
+    pp = prefill_prologue_inputs(np.diff(pre.cu_seqlens).tolist(), Nqk, Nv, seed=seed)
     px = torch.from_numpy(pp.mixed_qkv).to(dev, torch.bfloat16)
     pcs = torch.from_numpy(pp.conv_state).to(dev, torch.bfloat16)
     pw = torch.from_numpy(pp.conv_w).to(dev, torch.bfloat16)

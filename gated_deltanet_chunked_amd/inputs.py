@@ -127,43 +127,35 @@ def make_gate(shape, *, dtype: str = "bf16", seed: int = 0, weight: bool = True)
     return z, w
 
 
-# The five workloads the throughput and parity targets are quoted on.
-CONFIG_NAMES = {
-    0: "tiny chunk fwd: B=1 T=512 Nqk=2 Nv=4 D=128 fp32, zero initial state",
-    1: "prefill: B=1 T=4096 Nqk=16 Nv=32 D=128 bf16",
-    2: "varlen packed prefill: 8 sequences, lengths U[1,8192], Nqk=16 Nv=32 bf16",
-    3: "long-context prefill: B=1 T=32768 Nqk=16 Nv=32 bf16",
-    4: "decode step: N=256 sequences x 1 token, Nqk=16 Nv=32 bf16, fp32 states",
+# The named full-size workloads the benchmark times and the parity tests run,
+# each with its own seed.
+WORKLOADS = {
+    "tiny": "tiny chunk fwd: B=1 T=512 Nqk=2 Nv=4 D=128 fp32, zero initial state",
+    "prefill": "prefill: B=1 T=4096 Nqk=16 Nv=32 D=128 bf16",
+    "varlen": "varlen packed prefill: 8 sequences, lengths U[1,8192], Nqk=16 Nv=32 bf16",
+    "long": "long-context prefill: B=1 T=32768 Nqk=16 Nv=32 bf16",
+    "decode": "decode step: N=256 sequences x 1 token, Nqk=16 Nv=32 bf16, fp32 states",
 }
+WORKLOAD_SEEDS = {"tiny": 0, "prefill": 1, "varlen": 2, "long": 3, "decode": 4}
 
 
-def config_inputs(c: int) -> GdrInputs:
-    """The seeded inputs of workload ``c`` (seed = c)."""
+def workload_inputs(name: str) -> GdrInputs:
+    """The seeded inputs of the named workload (see WORKLOADS)."""
+    if name not in WORKLOADS:
+        raise ValueError(f"no workload {name!r}")
+    c = WORKLOAD_SEEDS[name]
     rng = np.random.default_rng(c)
-    if c == 0:
-        return _draw(rng, [512], 2, 4, "f32", c, None, (0.0, 16.0), D, D, CONFIG_NAMES[c])
-    if c == 1:
-        return _draw(rng, [4096], 16, 32, "bf16", c, 0.01, (0.0, 16.0), D, D, CONFIG_NAMES[c])
-    if c == 2:
+    what = WORKLOADS[name]
+    if name == "tiny":
+        return _draw(rng, [512], 2, 4, "f32", c, None, (0.0, 16.0), D, D, what)
+    if name == "prefill":
+        return _draw(rng, [4096], 16, 32, "bf16", c, 0.01, (0.0, 16.0), D, D, what)
+    if name == "varlen":
         lengths = rng.integers(1, 8192, size=8, endpoint=True).tolist()
-        return _draw(rng, lengths, 16, 32, "bf16", c, 0.01, (0.0, 16.0), D, D, CONFIG_NAMES[c])
-    if c == 3:
-        return _draw(rng, [32768], 16, 32, "bf16", c, 0.01, (0.0, 16.0), D, D, CONFIG_NAMES[c])
-    if c == 4:
-        return _draw(rng, [1] * 256, 16, 32, "bf16", c, 0.01, (0.0, 16.0), D, D, CONFIG_NAMES[c])
-    raise ValueError(f"no workload {c}")
-
-
-def config_shape(c: int) -> dict:
-    """Sizes of workload ``c`` without drawing it (lengths of config 2 are drawn)."""
-    if c == 2:
-        rng = np.random.default_rng(c)
-        lengths = rng.integers(1, 8192, size=8, endpoint=True).tolist()
-        return dict(lengths=lengths, Nqk=16, Nv=32, dtype="bf16")
-    table = {0: ([512], 2, 4, "f32"), 1: ([4096], 16, 32, "bf16"), 3: ([32768], 16, 32, "bf16"),
-             4: ([1] * 256, 16, 32, "bf16")}
-    lengths, Nqk, Nv, dt = table[c]
-    return dict(lengths=lengths, Nqk=Nqk, Nv=Nv, dtype=dt)
+        return _draw(rng, lengths, 16, 32, "bf16", c, 0.01, (0.0, 16.0), D, D, what)
+    if name == "long":
+        return _draw(rng, [32768], 16, 32, "bf16", c, 0.01, (0.0, 16.0), D, D, what)
+    return _draw(rng, [1] * 256, 16, 32, "bf16", c, 0.01, (0.0, 16.0), D, D, what)
 
 
 def orthonormal_keys(n: int, dk: int, seed: int) -> np.ndarray:

@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 import gated_deltanet_chunked_amd as gdr
-from gated_deltanet_chunked_amd.inputs import config_inputs, make_inputs
+from gated_deltanet_chunked_amd.inputs import make_inputs, workload_inputs
 from tests.gpu_util import (SCALE, TOL, assert_close_per_seq_head, device_tensors, oracle_full,
                             rel_l2, to_f64)
 
@@ -56,13 +56,13 @@ def test_chunk64_slow_decay_long():
     assert_close_per_seq_head(out, ro, st, rs, inp.cu_seqlens, TOL["bf16"], name="L=64 slow decay")
 
 
-def test_chunk64_prefill_config_all_heads():
+def test_chunk64_prefill_workload_all_heads():
     """T=4096, Nqk=16, Nv=32, bf16 (64 chunks of 64 tokens per head): every
     head against the oracle, and against the 128-token call."""
-    inp = config_inputs(1)
+    inp = workload_inputs("prefill")
     o64, s64 = _chunk(inp, 64)
     ro, rs = oracle_full(inp)
-    assert_close_per_seq_head(o64, ro, s64, rs, inp.cu_seqlens, TOL["bf16"], name="L=64 config 1")
+    assert_close_per_seq_head(o64, ro, s64, rs, inp.cu_seqlens, TOL["bf16"], name="L=64 T=4096")
     o128, s128 = _chunk(inp, 128)
     e_o, e_s = rel_l2(o64, o128), rel_l2(s64, s128)
     print(f"L=64 vs L=128: out {e_o:.2e}, state {e_s:.2e}")

@@ -12,7 +12,7 @@ import pytest
 
 import gated_deltanet_chunked_amd as gdr
 import oracle
-from gated_deltanet_chunked_amd.inputs import config_inputs, make_gate, make_inputs
+from gated_deltanet_chunked_amd.inputs import make_gate, make_inputs, workload_inputs
 from tests.gpu_util import SCALE, TOL, device_tensors, oracle_full, rel_l2, to_f64
 
 pytestmark = pytest.mark.gpu
@@ -191,12 +191,12 @@ def _gated_step(inp, z, w, in_place=True):
 
 @pytest.mark.parametrize("in_place", [True, False])
 @pytest.mark.parametrize("weight", [True, False])
-def test_decode_gated_config(in_place, weight):
+def test_decode_gated_workload(in_place, weight):
     """The decode workload (256 sequences, Nqk=16, Nv=32, bf16) with the norm
     fused: against the oracle's gated step; the state is the plain step's,
     bit for bit."""
     import torch
-    inp = config_inputs(4)
+    inp = workload_inputs("decode")
     z, w = make_gate((inp.N, inp.Nv, 128), seed=43, weight=weight)
     y, s_out, t = _gated_step(inp, z, w, in_place)
     ref, rs = oracle.recurrent_step_gated(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.state_in, z, w,

@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 
 import gated_deltanet_chunked_amd as gdr
-from gated_deltanet_chunked_amd.inputs import config_inputs, make_inputs
+from gated_deltanet_chunked_amd.inputs import make_inputs, workload_inputs
 from tests.gpu_util import (SCALE, TOL, assert_close_per_seq_head, device_tensors, oracle_full,
                             rel_l2, to_f64)
 
@@ -48,9 +48,9 @@ def _assert_close(name, got, ref, tol):
 # ----------------------------------------------------------------- prefill
 
 
-def test_tiny_fp32_config():
+def test_tiny_fp32_workload():
     """B=1, T=512 (4 chunks), Nqk=2, Nv=4, fp32, zero initial state."""
-    inp = config_inputs(0)
+    inp = workload_inputs("tiny")
     out, st = _chunk(inp)
     ro, rs = oracle_full(inp)
     assert_close_per_seq_head(out, ro, st, rs, inp.cu_seqlens, TOL["f32"])
@@ -140,23 +140,23 @@ def test_empty_input():
     assert torch.count_nonzero(st).item() == 0
 
 
-def test_prefill_config_full():
+def test_prefill_workload_full():
     """T=4096, Nqk=16, Nv=32, bf16, initial state N(0, 0.01): every head compared."""
-    inp = config_inputs(1)
+    inp = workload_inputs("prefill")
     out, st = _chunk(inp)
     ro, rs = oracle_full(inp)
     assert_close_per_seq_head(out, ro, st, rs, inp.cu_seqlens, TOL["bf16"])
 
 
-@pytest.mark.parametrize("cfg", [2, 3])
-def test_full_size_all_heads(cfg):
+@pytest.mark.parametrize("name", ["varlen", "long"])
+def test_full_size_all_heads(name):
     """Varlen (8 sequences, lengths U[1, 8192]) and long-context (T=32768)
     workloads at full size, in the launch configuration the benchmark times,
     compared on every sequence and every value head."""
-    inp = config_inputs(cfg)
+    inp = workload_inputs(name)
     out, st = _chunk(inp)
     ro, rs = oracle_full(inp)
-    assert_close_per_seq_head(out, ro, st, rs, inp.cu_seqlens, TOL["bf16"], name=f"config {cfg}")
+    assert_close_per_seq_head(out, ro, st, rs, inp.cu_seqlens, TOL["bf16"], name=name)
 
 
 # ------------------------------------------------------------------ decode
@@ -176,9 +176,9 @@ def _step(inp, in_place=True):
 
 
 @pytest.mark.parametrize("in_place", [True, False])
-def test_decode_config(in_place):
+def test_decode_workload(in_place):
     """256 sequences x 1 token, Nqk=16, Nv=32, bf16, fp32 states N(0, 0.01)."""
-    inp = config_inputs(4)
+    inp = workload_inputs("decode")
     out, st = _step(inp, in_place)
     ro, rs = oracle_full(inp)
     assert_close_per_seq_head(out, ro, st, rs, inp.cu_seqlens, TOL["bf16"])
@@ -286,12 +286,12 @@ def _check_rounded_state(got, exact):
 
 
 @pytest.mark.parametrize("in_place", [True, False])
-def test_decode_bf16_state_config(in_place):
+def test_decode_bf16_state_workload(in_place):
     """The decode workload (256 sequences, Nqk=16, Nv=32, bf16) with the state
     stored in bf16 (the workload's states rounded once)."""
     import oracle
     import torch
-    inp = config_inputs(4)
+    inp = workload_inputs("decode")
     s0 = torch.from_numpy(inp.state_in).to("cuda:0").to(torch.bfloat16)
     s0_64 = to_f64(s0)
     out, st = _bf16_state_step(inp, s0, in_place)
