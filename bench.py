@@ -15,8 +15,8 @@ region: K whole steps through the untimed entry points, each chunk call
 between two events on the launch stream.  The same K steps then run through
 the timed entry points, whose events, recorded by the runtime at each
 kernel's start and end, give every kernel's own duration (the figure
-rocprofv3's kernel trace reports); those events add about 3 us at each kernel
-boundary, which is why the throughput is taken without them.  The rooflines
+rocprofv3's kernel trace reports); those events add a few microseconds at
+each kernel boundary, which is why the throughput is taken without them.  The rooflines
 come from the kernel durations: ``roofline`` is the chunk path's dominant
 kernel against the bf16 matrix-core peak, ``roofline_decode`` the decode step
 against HBM bandwidth.  ``ms_per_step`` is the host wall clock of a whole step
