@@ -15,7 +15,7 @@ import numpy as np
 import pytest
 
 import gated_deltanet_chunked_amd as gdr
-from gated_deltanet_chunked_amd.inputs import GdrInputs, make_inputs, orthonormal_keys
+from gated_deltanet_chunked_amd.inputs import GdrInputs, make_inputs, orthonormal_keys, round_to_bf16
 from tests.gpu_util import (SCALE, TOL, assert_close_per_seq_head, device_tensors, oracle_full,
                             rel_l2, to_f64)
 
@@ -380,3 +380,46 @@ def test_many_short_sequences(dtype, chunk):
     empty = np.flatnonzero(lengths == 0)
     assert empty.size > 0
     assert np.array_equal(to_f64(st)[empty], inp.state_in[empty].astype(np.float64))
+
+
+# ------------------------------------------------------- the q scale
+
+
+@pytest.mark.parametrize("path,dtype", [("chunk", "f32"), ("chunk", "bf16"), ("chunk64", "bf16"),
+                                        ("multi", "bf16"), ("step", "f32"), ("step", "bf16")])
+def test_scale_other_than_the_default(path, dtype):
+    """Every entry point takes q's scale as an argument (the Blog's D^-1/2 is
+    only the default): a scale of 0.37 against the oracle at the same scale,
+    with and without the L2 norms, so that a constant built into a kernel, or
+    the scale applied to k, fails."""
+    import oracle
+    import torch
+    sc = 0.37
+    lengths = [1] * 6 if path == "step" else ([200, 57, 1] if path != "multi" else [5, 1, 16])
+    for l2 in (True, False):
+        inp = make_inputs(lengths, 2, 4, dtype=dtype, seed=130, state_std=0.1)
+        if not l2:
+            # used as given: rows of norm U(0.5, 1) (so a norm applied anyway
+            # would show), rounded again for bf16 so both sides see the same
+            rng = np.random.default_rng(131)
+            for name in ("q", "k"):
+                x = getattr(inp, name)
+                x = x / np.linalg.norm(x, axis=-1, keepdims=True) * rng.uniform(0.5, 1.0, x.shape[:-1] + (1,))
+                x = x.astype(np.float32)
+                setattr(inp, name, round_to_bf16(x) if dtype == "bf16" else x)
+        t = device_tensors(inp)
+        if path == "step":
+            s = t["state_in"].clone()
+            out = gdr.recurrent_step(t["q"], t["k"], t["v"], t["g"], t["beta"], s, scale=sc, l2norm=l2)
+            st = s
+        elif path == "multi":
+            out, st = gdr.recurrent_multi(t["q"], t["k"], t["v"], t["g"], t["beta"], t["cu"],
+                                          t["state_in"], scale=sc, l2norm=l2)
+        else:
+            out, st = gdr.chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], t["cu"], t["state_in"],
+                                    scale=sc, l2norm=l2, chunk=64 if path == "chunk64" else 128)
+        torch.cuda.synchronize()
+        ro, rs = oracle.recurrent(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.state_in, inp.cu_seqlens,
+                                  sc, l2norm=l2)
+        assert_close_per_seq_head(to_f64(out), ro, to_f64(st), rs, inp.cu_seqlens, TOL[dtype],
+                                  name=f"{path} {dtype} scale {sc} l2norm={l2}")
