@@ -234,3 +234,32 @@ def test_decode_gated_empty():
                                  t["g"][:0].contiguous(), t["beta"][:0].contiguous(), st,
                                  e(0, 2, 128), None)
     assert y.shape == (0, 2, 128)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("eps", [0.01, 1.0])
+def test_eps_other_than_the_default(dtype, eps):
+    """eps is an argument of both norm entry points: values large enough to
+    matter for rows of magnitude 0.01-3, against the oracle at the same eps,
+    standalone and fused behind the decode step."""
+    import torch
+    x = _x((500, 128), dtype, seed=61)
+    z, w = make_gate((500, 128), dtype=dtype, seed=62)
+    y = gdr.gated_rmsnorm(_dev(x, dtype), _dev(z, dtype), _dev(w, dtype), eps=eps)
+    torch.cuda.synchronize()
+    ref = oracle.gated_rmsnorm(x, z, w, eps=eps)
+    _check(f"norm {dtype} eps={eps}", to_f64(y), ref, TOL[dtype])
+    # the default eps would give a different result here
+    assert rel_l2(oracle.gated_rmsnorm(x, z, w), ref) > 10 * TOL[dtype]
+
+    inp = make_inputs([1] * 7, 2, 4, dtype=dtype, seed=63, state_std=0.5)
+    zz, ww = make_gate((inp.N, inp.Nv, 128), dtype=dtype, seed=64)
+    t = device_tensors(inp)
+    s = t["state_in"].clone()
+    yy = gdr.recurrent_step_gated(t["q"], t["k"], t["v"], t["g"], t["beta"], s, _dev(zz, dtype),
+                                  _dev(ww, dtype), scale=SCALE, norm_eps=eps)
+    torch.cuda.synchronize()
+    ref2, rs = oracle.recurrent_step_gated(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.state_in, zz, ww,
+                                           SCALE, norm_eps=eps, out_bf16=(dtype == "bf16"))
+    _check(f"decode gated {dtype} eps={eps}", to_f64(yy), ref2, TOL[dtype])
+    assert rel_l2(to_f64(s), rs) <= TOL[dtype]
