@@ -423,3 +423,38 @@ def test_scale_other_than_the_default(path, dtype):
                                   sc, l2norm=l2)
         assert_close_per_seq_head(to_f64(out), ro, to_f64(st), rs, inp.cu_seqlens, TOL[dtype],
                                   name=f"{path} {dtype} scale {sc} l2norm={l2}")
+
+
+# ------------------------------------------------------- extreme decays
+
+
+@pytest.mark.parametrize("path,dtype", [("chunk", "f32"), ("chunk", "bf16"), ("chunk64", "bf16"),
+                                        ("multi", "bf16")])
+def test_hard_resets_and_underflowing_decays(path, dtype):
+    """Gates far outside the trained range, still finite and <= 0: every 37th
+    token has g = -1e4 (the state before it is forgotten exactly; within a
+    chunk the decay mask and the chunk factors underflow to zero), one
+    sequence has g = -200 throughout (e^-200 underflows in fp32, not in the
+    fp64 oracle: a difference far below the tolerance), and g = 0 elsewhere on
+    some heads (no decay at all)."""
+    import oracle
+    import torch
+    lengths = [300, 200, 129] if path != "multi" else [9, 16, 3]
+    inp = make_inputs(lengths, 2, 4, dtype=dtype, seed=140, state_std=0.5)
+    g = inp.g.copy()
+    g[::37, :] = -1e4
+    t0, t1 = int(inp.cu_seqlens[1]), int(inp.cu_seqlens[2])
+    g[t0:t1, :] = -200.0
+    g[:t0, 3] = 0.0
+    inp.g = g.astype(np.float32)
+    t = device_tensors(inp)
+    if path == "multi":
+        out, st = gdr.recurrent_multi(t["q"], t["k"], t["v"], t["g"], t["beta"], t["cu"],
+                                      t["state_in"], scale=SCALE)
+    else:
+        out, st = gdr.chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], t["cu"], t["state_in"],
+                                scale=SCALE, chunk=64 if path == "chunk64" else 128)
+    torch.cuda.synchronize()
+    ro, rs = oracle_full(inp)
+    assert_close_per_seq_head(to_f64(out), ro, to_f64(st), rs, inp.cu_seqlens, TOL[dtype],
+                              name=f"{path} {dtype} extreme gates")
