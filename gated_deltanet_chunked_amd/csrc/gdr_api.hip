@@ -59,11 +59,22 @@ struct EventPairs {
   }
 };
 
-// A single sequence needs no chunk table (Chunks derives its slots from
-// cu_seqlens directly), so its call is two launches per segment.
-int32_t launches_needed(const Workspace& w, int64_t N) {
-  const int64_t segs = (w.nslots + w.seg_slots - 1) / w.seg_slots;
-  return static_cast<int32_t>((N > 1 ? 1 : 0) + 2 * segs);
+// The launch in front of the segments: the chunk table for packed batches
+// (a single sequence needs none: Chunks derives its slots from cu_seqlens
+// directly), and the final states of empty sequences, which the state pass
+// never visits (only a packed batch, or a single sequence with T = 0, can
+// have one; in place there is nothing to copy).
+bool table_build(const ChunkArgs& a) { return a.N > 1; }
+bool table_copy(const ChunkArgs& a) {
+  return a.state_out && a.state_out != a.state_in && (a.N > 1 || a.T == 0);
+}
+
+// Launches of one call: the table launch (when it has work), then two per
+// segment.
+int32_t launches_needed(const ChunkArgs& a, const Workspace& w) {
+  // no slot at all (a single empty sequence): no segment
+  const int64_t segs = w.seg_slots > 0 ? (w.nslots + w.seg_slots - 1) / w.seg_slots : 0;
+  return static_cast<int32_t>((table_build(a) || table_copy(a) ? 1 : 0) + 2 * segs);
 }
 
 template <typename T>
@@ -73,6 +84,7 @@ gdr_status run_chunk(const ChunkArgs& a, hipStream_t st, Recorder& rec) {
   char* ws = static_cast<char*>(a.workspace);
   int4* table = reinterpret_cast<int4*>(ws + w.table);
   int32_t* choff = reinterpret_cast<int32_t*>(ws + w.choff);
+  int32_t* nonempty = reinterpret_cast<int32_t*>(ws + w.nonempty);
   float* gam = reinterpret_cast<float*>(ws + w.gam);
   T* inter = reinterpret_cast<T*>(ws + w.inter);
   float* carry = a.state_out ? a.state_out : reinterpret_cast<float*>(ws + w.carry);
@@ -86,12 +98,17 @@ gdr_status run_chunk(const ChunkArgs& a, hipStream_t st, Recorder& rec) {
 
   // Every launch is checked at once: hipGetLastError also clears the error,
   // so a failed launch followed by a good one would otherwise go unseen.
-  Chunks chunks{nullptr, nullptr, a.cu_seqlens, a.T, L};
-  if (a.N > 1) {
-    launch_table(a.cu_seqlens, a.N, a.T, L, nslots, table, choff, st, rec.next(GDR_STAGE_TABLE));
+  Chunks chunks{nullptr, nullptr, nullptr, a.cu_seqlens, a.T, L, a.N};
+  const bool build = table_build(a), copy = table_copy(a);
+  if (build || copy) {
+    launch_table(a.cu_seqlens, a.N, a.T, L, nslots, table, choff, nonempty, build, copy, a.Nv,
+                 a.state_in, a.state_out, st, rec.next(GDR_STAGE_TABLE));
     if (hipGetLastError() != hipSuccess) return GDR_ERR_HIP;
+  }
+  if (build) {
     chunks.table = table;
     chunks.choff = choff;
+    chunks.nonempty = nonempty;
   }
   for (int64_t s0 = 0; s0 < w.nslots; s0 += w.seg_slots) {
     const int32_t nseg = static_cast<int32_t>(w.nslots - s0 < w.seg_slots ? w.nslots - s0 : w.seg_slots);
@@ -99,8 +116,7 @@ gdr_status run_chunk(const ChunkArgs& a, hipStream_t st, Recorder& rec) {
                         a.scale, norm, inter, gam, st, rec.next(GDR_STAGE_INTRA)) != hipSuccess)
       return GDR_ERR_HIP;
     launch_inter<T>(inter, chunks, gam, a.state_in, carry, a.state_out, a.N, a.Nv,
-                    static_cast<int32_t>(s0), nseg, s0 == 0, out, discard, st,
-                    rec.next(GDR_STAGE_INTER));
+                    static_cast<int32_t>(s0), nseg, out, discard, st, rec.next(GDR_STAGE_INTER));
     if (hipGetLastError() != hipSuccess) return GDR_ERR_HIP;
   }
   return GDR_OK;
@@ -164,8 +180,7 @@ extern "C" gdr_status gdr_chunk_fwd_timed(const void* q, const void* k, const vo
   if (!kernel_ms || !kernel_kind || !n || max_kernels < 0) return GDR_ERR_INVALID_ARGUMENT;
   s = chunk_contract(a, static_cast<hipStream_t>(stream));
   if (s != GDR_OK) return s;
-  const int32_t need =
-      launches_needed(plan_workspace(T, N, Nqk, Nv, dtype, 0, chunk_len(flags)), N);
+  const int32_t need = launches_needed(a, plan_workspace(T, N, Nqk, Nv, dtype, 0, chunk_len(flags)));
   // more launches than the caller's arrays hold: the span alone is timed
   const bool span_only = need > max_kernels;
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -178,9 +193,16 @@ extern "C" gdr_status gdr_chunk_fwd_timed(const void* q, const void* k, const vo
   rec.span_only = span_only;
   rec.total = need;
   s = dispatch_chunk(a, st, rec);
+  if (s != GDR_OK) return s;
+  if (rec.n == 0) {
+    // nothing was launched (T = 0 and no state to copy)
+    *n = 0;
+    if (span_ms) *span_ms = 0.0f;
+    return GDR_OK;
+  }
   const hipEvent_t first = pairs.ev[0];
   const hipEvent_t last = span_only ? pairs.ev[1] : pairs.ev[2 * rec.n - 1];
-  if (s == GDR_OK && hipEventSynchronize(last) != hipSuccess) s = GDR_ERR_HIP;
+  if (hipEventSynchronize(last) != hipSuccess) s = GDR_ERR_HIP;
   if (s == GDR_OK) {
     const int32_t timed = span_only ? 0 : rec.n;
     for (int32_t i = 0; i < timed; ++i)

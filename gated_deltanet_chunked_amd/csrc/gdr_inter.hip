@@ -82,8 +82,7 @@ constexpr int kWarmAhead = 5;
 template <typename T>
 __global__ __launch_bounds__(256, 1) void inter_kernel(
     const T* __restrict__ inter, Chunks chunks, const float* __restrict__ gam, const float* state_in, float* carry, float* state_out,
-    int32_t N, int32_t Nv, int32_t slot0, int32_t nseg, int first_segment, T* __restrict__ out,
-    T* __restrict__ discard) {
+    int32_t Nv, int32_t slot0, int32_t nseg, T* __restrict__ out, T* __restrict__ discard) {
   constexpr int KSTEPS = ChunkOps<T>::KSTEPS;
   constexpr int DEPTH = Depth<T>::value;
   constexpr int NSET = DEPTH + 1;
@@ -94,20 +93,22 @@ __global__ __launch_bounds__(256, 1) void inter_kernel(
   __shared__ int2 sTab[kMaxSegSlots];
   __shared__ float sGam[kMaxSegSlots];
 
-  // Block -> (sequence b, head h, row block vb).  Blocks are dealt to the 8
-  // XCDs round-robin; the VB row blocks of one (b, h) read the same Mt and Qp,
-  // so when possible they land on the same XCD.
-  const int id = blockIdx.x;
-  const int pairs = N * Nv;
-  int bh, vb;
-  if ((pairs & 7) == 0) {
-    bh = (id & 7) + 8 * (id / (8 * VB));
-    vb = (id >> 3) % VB;
+  // blockIdx.x -> (head h, row block vb), blockIdx.y -> the sequence b of the
+  // y-th run of slots in the segment.  Blocks are dealt to the 8 XCDs
+  // round-robin in id order; the VB row blocks of one (b, h) read the same
+  // Mt and Qp, so when possible they land on the same XCD.
+  const int x = blockIdx.x;
+  int h, vb;
+  if ((Nv & 7) == 0) {
+    h = (x & 7) + 8 * (x / (8 * VB));
+    vb = (x >> 3) % VB;
   } else {
-    bh = id / VB;
-    vb = id % VB;
+    h = x / VB;
+    vb = x % VB;
   }
-  const int b = bh / Nv, h = bh % Nv;
+  int b;
+  if (!chunks.run_sequence(slot0, nseg, blockIdx.y, b)) return;
+  const int bh = b * Nv + h;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const bool state_wave = w < 2;
   const int rb = 64 * (w & 1);               // first row (d or r) of this wave's block
@@ -115,20 +116,6 @@ __global__ __launch_bounds__(256, 1) void inter_kernel(
   const size_t sb = (size_t)bh * kD * kD;    // this (b, h)'s state
   int c0, c1;
   chunks.seq_slots(b, c0, c1);
-
-  if (c0 == c1) {
-    // empty sequence: its final state is its initial state
-    if (first_segment && state_out && state_out != state_in) {
-      for (int idx = tid; idx < kBV * kD / 4; idx += 256) {
-        const int r = idx / (kD / 4), c = (idx % (kD / 4)) * 4;
-        const size_t off = sb + (size_t)(v0 + r) * kD + c;
-        float4 val = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (state_in) val = *reinterpret_cast<const float4*>(state_in + off);
-        *reinterpret_cast<float4*>(state_out + off) = val;
-      }
-    }
-    return;
-  }
   const int cb = max(c0, slot0), ce = min(c1, slot0 + nseg);
   if (cb >= ce) return;
   const float* src = (cb == c0) ? state_in : carry;
@@ -317,25 +304,24 @@ __global__ __launch_bounds__(256, 1) void inter_kernel(
 template <typename T>
 void launch_inter(const T* inter, Chunks chunks, const float* gam, const float* state_in,
                   float* carry, float* state_out, int32_t N, int32_t Nv, int32_t slot0,
-                  int32_t nseg, bool first_segment, T* out, T* discard, hipStream_t stream,
-                  LaunchEvents ev) {
+                  int32_t nseg, T* out, T* discard, hipStream_t stream, LaunchEvents ev) {
   if constexpr (sizeof(T) == 2) {
     // bf16 has its own kernel (gdr_inter_bf16.hip)
-    launch_inter_bf16(inter, chunks, gam, state_in, carry, state_out, N, Nv, slot0, nseg,
-                      first_segment, out, discard, stream, ev);
+    launch_inter_bf16(inter, chunks, gam, state_in, carry, state_out, N, Nv, slot0, nseg, out,
+                      discard, stream, ev);
   } else {
-    const unsigned blocks = (unsigned)N * (unsigned)Nv * (unsigned)(kD / kBV);
-    hipExtLaunchKernelGGL(inter_kernel<T>, dim3(blocks), dim3(256), 0, stream, ev.start, ev.stop,
-                          0, inter, chunks, gam, state_in, carry, state_out, N, Nv, slot0, nseg,
-                          first_segment ? 1 : 0, out, discard);
+    const unsigned runs = chunks.table ? (unsigned)(N < nseg ? N : nseg) : 1u;
+    hipExtLaunchKernelGGL(inter_kernel<T>, dim3((unsigned)Nv * (unsigned)(kD / kBV), runs),
+                          dim3(256), 0, stream, ev.start, ev.stop, 0, inter, chunks, gam, state_in,
+                          carry, state_out, Nv, slot0, nseg, out, discard);
   }
 }
 
 template void launch_inter<float>(const float*, Chunks, const float*, const float*, float*, float*,
-                                  int32_t, int32_t, int32_t, int32_t, bool, float*, float*,
-                                  hipStream_t, LaunchEvents);
+                                  int32_t, int32_t, int32_t, int32_t, float*, float*, hipStream_t,
+                                  LaunchEvents);
 template void launch_inter<__bf16>(const __bf16*, Chunks, const float*, const float*, float*,
-                                   float*, int32_t, int32_t, int32_t, int32_t, bool, __bf16*,
-                                   __bf16*, hipStream_t, LaunchEvents);
+                                   float*, int32_t, int32_t, int32_t, int32_t, __bf16*, __bf16*,
+                                   hipStream_t, LaunchEvents);
 
 }  // namespace gdr

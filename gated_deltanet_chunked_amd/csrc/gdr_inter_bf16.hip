@@ -72,44 +72,34 @@ __device__ __forceinline__ void dma16(const char* src_wave, char* dst_wave, int 
 
 __global__ __launch_bounds__(512, 1) void inter_bf16_kernel(
     const bf* __restrict__ inter, Chunks chunks, const float* __restrict__ gam,
-    const float* state_in, float* carry, float* state_out, int32_t N, int32_t Nv, int32_t slot0,
-    int32_t nseg, int first_segment, bf* __restrict__ out, bf* __restrict__ discard) {
+    const float* state_in, float* carry, float* state_out, int32_t Nv, int32_t slot0,
+    int32_t nseg, bf* __restrict__ out, bf* __restrict__ discard) {
   constexpr int VB = 128 / kBV;
   __shared__ InterLds s;
 
-  const int id = blockIdx.x;
-  const int pairs = N * Nv;
-  int bh, vb;
-  if ((pairs & 7) == 0) {
+  // blockIdx.x -> (value head h, row block vb), blockIdx.y -> the sequence b
+  // of the y-th run of slots in the segment
+  const int x = blockIdx.x;
+  int h, vb;
+  if ((Nv & 7) == 0) {
     // the VB row blocks of one (b, h) read the same Mt and Qp: deal them to
-    // the same XCD (workgroups go to the 8 XCDs round-robin)
-    bh = (id & 7) + 8 * (id / (8 * VB));
-    vb = (id >> 3) % VB;
+    // the same XCD (workgroups go to the 8 XCDs round-robin in id order, and
+    // a row of the grid is Nv VB workgroups, a multiple of 8)
+    h = (x & 7) + 8 * (x / (8 * VB));
+    vb = (x >> 3) % VB;
   } else {
-    bh = id / VB;
-    vb = id % VB;
+    h = x / VB;
+    vb = x % VB;
   }
-  const int b = bh / Nv, h = bh % Nv;
+  int b;
+  if (!chunks.run_sequence(slot0, nseg, blockIdx.y, b)) return;
+  const int bh = b * Nv + h;
   const int tid = threadIdx.x, l = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int v0 = kBV * vb;
   const size_t sb = (size_t)bh * 128 * 128;
   int c0, c1;
   chunks.seq_slots(b, c0, c1);
-
-  if (c0 == c1) {
-    // empty sequence: its final state is its initial state
-    if (first_segment && state_out && state_out != state_in) {
-      for (int idx = tid; idx < kBV * 128 / 4; idx += 512) {
-        const int r = idx / 32, c = (idx % 32) * 4;
-        const size_t off = sb + (size_t)(v0 + r) * 128 + c;
-        float4 val = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (state_in) val = *reinterpret_cast<const float4*>(state_in + off);
-        *reinterpret_cast<float4*>(state_out + off) = val;
-      }
-    }
-    return;
-  }
   const int cb = max(c0, slot0), ce = min(c1, slot0 + nseg);
   if (cb >= ce) return;
   const float* src = (cb == c0) ? state_in : carry;
@@ -314,12 +304,12 @@ __global__ __launch_bounds__(512, 1) void inter_bf16_kernel(
 
 void launch_inter_bf16(const __bf16* inter, Chunks chunks, const float* gam, const float* state_in,
                        float* carry, float* state_out, int32_t N, int32_t Nv, int32_t slot0,
-                       int32_t nseg, bool first_segment, __bf16* out, __bf16* discard,
+                       int32_t nseg, __bf16* out, __bf16* discard,
                        hipStream_t stream, LaunchEvents ev) {
-  const unsigned blocks = (unsigned)N * (unsigned)Nv * (unsigned)(128 / kBV);
-  hipExtLaunchKernelGGL(inter_bf16_kernel, dim3(blocks), dim3(512), 0, stream, ev.start, ev.stop, 0,
-                        inter, chunks, gam, state_in, carry, state_out, N, Nv, slot0, nseg,
-                        first_segment ? 1 : 0, out, discard);
+  const unsigned runs = chunks.table ? (unsigned)(N < nseg ? N : nseg) : 1u;
+  hipExtLaunchKernelGGL(inter_bf16_kernel, dim3((unsigned)Nv * (unsigned)(128 / kBV), runs),
+                        dim3(512), 0, stream, ev.start, ev.stop, 0, inter, chunks, gam, state_in,
+                        carry, state_out, Nv, slot0, nseg, out, discard);
 }
 
 }  // namespace gdr

@@ -27,8 +27,10 @@ constexpr int kMaxSegSlots = 512;
 
 // Largest number of value heads.  It keeps the 128 rows of a chunk of v (row
 // stride Nv * 128 elements of at most 4 bytes) within 2 GiB, so the kernels
-// address a chunk's rows with 32-bit byte offsets from a per-chunk base.
-constexpr int32_t kMaxNv = 32768;
+// address a chunk's rows with 32-bit byte offsets from a per-chunk base, and
+// every launch's grid within 2^32 work-items (the intra-chunk kernel runs up
+// to 512 slots x Nv workgroups of 256 threads per segment).
+constexpr int32_t kMaxNv = 16384;
 
 // Chunk slots processed per segment: the intra-chunk products of one segment
 // are written to the workspace and consumed by the state pass of the same
@@ -54,6 +56,7 @@ constexpr int64_t kMatElems = 128 * 128;
 struct Workspace {
   int64_t table;      // int32 [nslots][4]: {sequence, first token, length, 0}; sequence -1 = unused
   int64_t choff;      // int32 [N + 1]: first slot of each sequence
+  int64_t nonempty;   // int32 [N]: the non-empty sequences in order (-1 past the last)
   int64_t gam;        // float [nslots][Nv]: exp(sum of g over the chunk)
   int64_t inter;      // [seg_slots][Nv][4][128][128] of the matrix-core operand type
   int64_t carry;      // float [N][Nv][128][128]: state between segments

@@ -17,16 +17,19 @@ struct LaunchEvents {
 
 // Chunk slots of the packed sequences.  Chunks restart at every sequence
 // start (Qwen3-Next blog post, section 5(1)c).  With a chunk table (built
-// from cu_seqlens by table_kernel) slot s is {sequence, first token, length};
-// for a single sequence (table == nullptr) slot s covers tokens
-// [lo + 128 s, min(lo + 128 (s + 1), hi)), lo and hi being cu_seqlens[0..1]
+// from cu_seqlens by table_kernel) slot s is {sequence, first token, length,
+// rank of the sequence among the non-empty ones}, and nonempty[r] is the
+// sequence of rank r; for a single sequence (table == nullptr) slot s covers
+// tokens [lo + L s, min(lo + L (s + 1), hi)), lo and hi being cu_seqlens[0..1]
 // clamped into [0, T]: the entries the table kernel would write.
 struct Chunks {
   const int4* table;
   const int32_t* choff;
+  const int32_t* nonempty;
   const int32_t* cu;
   int32_t T;
   int32_t L;   // chunk length: 128, or 64
+  int32_t N;   // sequences
   __device__ __forceinline__ void one_range(int& lo, int& hi) const {
     lo = min(max(cu[0], 0), T);
     hi = min(max(cu[1], lo), T);
@@ -45,6 +48,22 @@ struct Chunks {
     len = min(L, hi - start);
     return start < hi;
   }
+  // The sequence b of the r-th run of one sequence's slots among slots
+  // [s0, s0 + n) (a segment); false when the segment holds fewer runs.  The
+  // runs of a segment are sequences of consecutive ranks, at most n of them,
+  // so a launch over a segment needs min(N, n) of them whatever N is.
+  __device__ __forceinline__ bool run_sequence(int s0, int n, int r, int& b) const {
+    if (!table) {
+      b = 0;
+      return r == 0;
+    }
+    const int4 e = table[s0];
+    if (e.x < 0) return false;   // the segment lies past the used slots
+    const int rank = e.w + r;
+    if (rank >= N) return false;
+    b = nonempty[rank];
+    return b >= 0 && choff[b] < s0 + n;
+  }
   // slots [c0, c1) of sequence b
   __device__ __forceinline__ void seq_slots(int b, int& c0, int& c1) const {
     if (table) {
@@ -59,8 +78,15 @@ struct Chunks {
   }
 };
 
+// One launch in front of the chunkwise passes, with up to two parts: the
+// chunk table (build: table, choff, nonempty; for N > 1), and the final
+// states of the empty sequences (copy: state_out[b] = state_in[b], or zeros
+// without state_in), which the state pass, running over chunk slots only,
+// never visits.
 void launch_table(const int32_t* cu, int32_t N, int32_t T, int32_t L, int32_t nslots, int4* table,
-                  int32_t* choff, hipStream_t stream, LaunchEvents ev = {});
+                  int32_t* choff, int32_t* nonempty, bool build, bool copy, int32_t Nv,
+                  const float* state_in, float* state_out, hipStream_t stream,
+                  LaunchEvents ev = {});
 
 // Intra-chunk products for chunk slots [slot0, slot0 + nseg) of every value head;
 // also writes exp(total gate of the chunk) to gam[slot][head].
@@ -76,18 +102,20 @@ hipError_t launch_intra_bf16(const __bf16* q, const __bf16* k, const __bf16* v, 
                              int32_t slot0, int32_t nseg, float scale, int norm, __bf16* inter,
                              float* gam, hipStream_t stream, LaunchEvents ev = {});
 
-// Chunk-serial state pass over chunk slots [slot0, slot0 + nseg).  `discard` is
-// 256 bytes of scratch that absorbs the stores of rows past a chunk's end.
+// Chunk-serial state pass over chunk slots [slot0, slot0 + nseg), for the
+// sequences with slots there (grid: value heads x row blocks, then the
+// segment's runs of slots, at most min(N, nseg)).  `discard` is 256 bytes of
+// scratch that absorbs the stores of rows past a chunk's end.
 template <typename Tin>
 void launch_inter(const Tin* inter, Chunks chunks, const float* gam,
                   const float* state_in, float* carry, float* state_out, int32_t N, int32_t Nv,
-                  int32_t slot0, int32_t nseg, bool first_segment, Tin* out, Tin* discard,
+                  int32_t slot0, int32_t nseg, Tin* out, Tin* discard,
                   hipStream_t stream, LaunchEvents ev = {});
 
 // The bf16 kernel behind launch_inter<__bf16> (gdr_inter_bf16.hip).
 void launch_inter_bf16(const __bf16* inter, Chunks chunks, const float* gam, const float* state_in,
                        float* carry, float* state_out, int32_t N, int32_t Nv, int32_t slot0,
-                       int32_t nseg, bool first_segment, __bf16* out, __bf16* discard,
+                       int32_t nseg, __bf16* out, __bf16* discard,
                        hipStream_t stream, LaunchEvents ev = {});
 
 // One decode step; the state is stored as St (float, or __bf16 for a bf16

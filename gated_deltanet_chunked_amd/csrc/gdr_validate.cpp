@@ -39,7 +39,7 @@ Workspace plan_workspace(int64_t T, int64_t N, int64_t Nqk, int64_t Nv, gdr_dtyp
   const int64_t per_slot = Nv * kInterMats * kMatElems * es;
   w.nslots = max_slots(T, N, L);
   // everything but the segment's matrices
-  const int64_t fixed = align256(w.nslots * 4 * 4) + align256((N + 1) * 4) +
+  const int64_t fixed = align256(w.nslots * 4 * 4) + align256((N + 1) * 4) + align256(N * 4) +
                         align256(w.nslots * Nv * 4) + align256(N * Nv * kMatElems * 4) + 256;
   if (budget > 0) {
     // the largest segment that fits the budget, then the slots split evenly
@@ -49,7 +49,8 @@ Workspace plan_workspace(int64_t T, int64_t N, int64_t Nqk, int64_t Nv, gdr_dtyp
       w.total = -1;   // does not fit
       return w;
     }
-    const int64_t nsegs = (w.nslots + cap - 1) / cap;
+    // at least one segment, also for no slot at all (then of no slot)
+    const int64_t nsegs = w.nslots > cap ? (w.nslots + cap - 1) / cap : 1;
     w.seg_slots = (w.nslots + nsegs - 1) / nsegs;
   } else {
     w.seg_slots = segment_slots(w.nslots, Nv, es);
@@ -57,6 +58,7 @@ Workspace plan_workspace(int64_t T, int64_t N, int64_t Nqk, int64_t Nv, gdr_dtyp
   int64_t off = 0;
   w.table = off; off = align256(off + w.nslots * 4 * 4);
   w.choff = off; off = align256(off + (N + 1) * 4);
+  w.nonempty = off; off = align256(off + N * 4);
   w.gam = off; off = align256(off + w.nslots * Nv * 4);
   w.inter = off;
   off = align256(off + w.seg_slots * per_slot);
@@ -73,8 +75,8 @@ gdr_status validate_chunk(const ChunkArgs& a) {
   // every element offset must fit comfortably in 63 bits; the kernels also
   // index tokens with 32-bit integers
   if (static_cast<int64_t>(a.T) * a.Nv > (int64_t(1) << 40)) return GDR_ERR_INVALID_ARGUMENT;
-  if (a.no_workspace && static_cast<int64_t>(a.N) * a.Nv > (int64_t(1) << 31) / 4)
-    return GDR_ERR_INVALID_ARGUMENT;   // one workgroup per (sequence, head)
+  if (a.no_workspace && static_cast<int64_t>(a.N) * a.Nv >= (int64_t(1) << 24))
+    return GDR_ERR_INVALID_ARGUMENT;   // one workgroup of 256 threads per (sequence, head)
   if (!a.cu_seqlens || (!a.workspace && !a.no_workspace)) return GDR_ERR_INVALID_ARGUMENT;
   if (a.T > 0 && (!a.q || !a.k || !a.v || !a.g || !a.beta || !a.out)) return GDR_ERR_INVALID_ARGUMENT;
   const void* ptrs[] = {a.q, a.k, a.v, a.g, a.beta, a.state_in, a.cu_seqlens, a.out, a.state_out};
@@ -118,7 +120,8 @@ gdr_status validate_step(const StepArgs& a) {
   gdr_status s = common_sizes(a.Nqk, a.Nv, a.D, a.dtype, a.flags);
   if (s != GDR_OK) return s;
   if (a.N < 0) return GDR_ERR_INVALID_ARGUMENT;
-  if (static_cast<int64_t>(a.N) * a.Nv > (int64_t(1) << 31) / 4) return GDR_ERR_INVALID_ARGUMENT;
+  // one workgroup of 256 threads per (sequence, head): the grid stays below 2^32 work-items
+  if (static_cast<int64_t>(a.N) * a.Nv >= (int64_t(1) << 24)) return GDR_ERR_INVALID_ARGUMENT;
   if (a.N == 0) return GDR_OK;
   if (!a.q || !a.k || !a.v || !a.g || !a.beta || !a.state_in || !a.state_out || !a.out)
     return GDR_ERR_INVALID_ARGUMENT;
@@ -172,7 +175,8 @@ gdr_status validate_conv_step(const ConvStepArgs& a) {
   if (s != GDR_OK) return s;
   if (a.conv_k != 4) return GDR_ERR_UNSUPPORTED;
   if (a.N < 0) return GDR_ERR_INVALID_ARGUMENT;
-  if (static_cast<int64_t>(a.N) * a.Nv > (int64_t(1) << 31) / 4) return GDR_ERR_INVALID_ARGUMENT;
+  // one workgroup of 256 threads per (sequence, head): the grid stays below 2^32 work-items
+  if (static_cast<int64_t>(a.N) * a.Nv >= (int64_t(1) << 24)) return GDR_ERR_INVALID_ARGUMENT;
   if (a.N == 0) return GDR_OK;
   const void* req[] = {a.x, a.cs_in, a.cs_out, a.w, a.a, a.b, a.A_log, a.dt_bias, a.state_in,
                        a.state_out, a.out};

@@ -36,8 +36,9 @@
  *     global state, so calls on different streams may run concurrently as long
  *     as their buffers do not overlap.
  *   - D (= Dk = Dv) must be 128; Nv must be a multiple of Nqk (operator page,
- *     parameter constraints) and at most 32768 (GDR_ERR_UNSUPPORTED beyond,
- *     so that a chunk's rows span less than 2 GiB of any input).
+ *     parameter constraints) and at most 16384 (GDR_ERR_UNSUPPORTED beyond,
+ *     so that a chunk's rows span less than 2 GiB of any input and every
+ *     launch stays within 2^32 work-items).
  *   - `dtype` is the storage type of q, k, v and out.  g, beta and the states
  *     are always float32.  Arithmetic accumulates in float32; bf16 inputs are
  *     multiplied on bf16 matrix cores, f32 inputs on f32 matrix cores.
@@ -68,7 +69,7 @@ typedef enum { GDR_F32 = 0, GDR_BF16 = 1 } gdr_dtype;
 typedef enum {
     GDR_OK = 0,
     GDR_ERR_INVALID_ARGUMENT = -1,   /* bad size, null pointer, misalignment, ... */
-    GDR_ERR_UNSUPPORTED = -2,        /* D != 128, Nv > 32768, unknown dtype or flag */
+    GDR_ERR_UNSUPPORTED = -2,        /* D != 128, Nv > 16384, unknown dtype or flag */
     GDR_ERR_WORKSPACE_TOO_SMALL = -3,
     GDR_ERR_HIP = -4,                /* a HIP runtime call or launch failed */
     GDR_ERR_CONTRACT = -5            /* debug checks on: a device value breaks the contract */
@@ -141,7 +142,10 @@ gdr_status gdr_chunk_fwd(const void* q, const void* k, const void* v,
  * state_out  [N, Nv, D, D] float32 (required); may equal state_in for an
  *            in-place update
  * out        [N, Nv, D]   dtype
- * Requires N >= 0 (N = 0 does nothing).
+ * Requires N >= 0 (N = 0 does nothing) and N * Nv < 2^24 (one workgroup per
+ * (sequence, head); GDR_ERR_INVALID_ARGUMENT beyond), which holds for every
+ * batch whose states fit in memory.  The same bound applies to the decode
+ * variants below.
  */
 gdr_status gdr_recurrent_step(const void* q, const void* k, const void* v,
                               const float* g, const float* beta,
@@ -194,7 +198,7 @@ size_t gdr_chunk_fwd_no_alloc_scratch_bytes(void);
  * written.  The number of launches is 2 * ceil(slots / segment), plus 1 (the
  * chunk table) when N > 1: a handful for the configurations of the pages.
  */
-#define GDR_STAGE_TABLE 0   /* chunk table from cu_seqlens */
+#define GDR_STAGE_TABLE 0   /* chunk table from cu_seqlens, final states of empty sequences */
 #define GDR_STAGE_INTRA 1   /* norms, gate cumsum, intra-chunk products; parallel over chunks */
 #define GDR_STAGE_INTER 2   /* chunk-serial state pass and outputs */
 gdr_status gdr_chunk_fwd_timed(const void* q, const void* k, const void* v,
@@ -258,7 +262,7 @@ gdr_status gdr_recurrent_step_bf16_state(const void* q, const void* k, const voi
  * longest sequence, so long sequences belong to gdr_chunk_fwd.
  * kernel_ms: NULL, or where to write the kernel's GPU time (the call then
  * blocks until the kernel ends).  Errors as for gdr_chunk_fwd, plus
- * GDR_ERR_INVALID_ARGUMENT when N * Nv > 2^29.
+ * GDR_ERR_INVALID_ARGUMENT when N * Nv >= 2^24.
  */
 gdr_status gdr_recurrent_multi(const void* q, const void* k, const void* v,
                                const float* g, const float* beta,

@@ -59,7 +59,8 @@ def test_workspace_size():
     assert lib.gdr_chunk_fwd_workspace_size(512, 0, 2, 4, 128, 0) == 0  # N < 1
     assert lib.gdr_chunk_fwd_workspace_size(-1, 1, 2, 4, 128, 0) == 0
     assert lib.gdr_chunk_fwd_workspace_size(512, 1, 2, 4, 128, 5) == 0  # dtype
-    assert lib.gdr_chunk_fwd_workspace_size(512, 1, 1, 65536, 128, 0) == 0  # Nv > 32768
+    assert lib.gdr_chunk_fwd_workspace_size(512, 1, 1, 16385, 128, 0) == 0  # Nv > 16384
+    assert lib.gdr_chunk_fwd_workspace_size(512, 1, 1, 16384, 128, 0) > 0
     # bounded by the segment buffer: grows slowly with T
     assert ws(1 << 20, 1, 16, 32, gdr.GDR_BF16) < 2 * ws(1 << 16, 1, 16, 32, gdr.GDR_BF16) + (1 << 30)
 
@@ -98,7 +99,7 @@ def call_chunk(fb, **over):
     (dict(D=64), UNSUPPORTED),
     (dict(dtype=7), UNSUPPORTED),
     (dict(flags=4), UNSUPPORTED),
-    (dict(Nqk=1, Nv=65536), UNSUPPORTED),   # more than 32768 value heads
+    (dict(Nqk=1, Nv=16385), UNSUPPORTED),   # more than 16384 value heads
     (dict(Nqk=3), INVALID),            # Nv % Nqk != 0
     (dict(N=0), INVALID),
     (dict(T=-1), INVALID),
@@ -149,6 +150,7 @@ def call_step(fb, **over):
     (dict(state_out=None), INVALID),
     (dict(out=None), INVALID),
     (dict(k=1 << 40 | 4), INVALID),
+    (dict(N=1 << 21, Nqk=8, Nv=8), INVALID),   # 2^24 workgroups: beyond a grid's 2^32 work-items
 ], ids=lambda x: str(x))
 def test_recurrent_step_rejects(over, expect):
     fb = FakeBuffers(T=2, N=2)
@@ -442,3 +444,32 @@ def test_chunk64_flag_and_workspace():
     with pytest.raises(ValueError):
         gdr._chunk_flags(True, 32)
     assert gdr._chunk_flags(True, 64) == 3 and gdr._chunk_flags(False, 128) == 0
+
+
+def test_single_empty_sequence_plans_without_dividing_by_zero():
+    """N = 1, T = 0 has no chunk slot: planning the workspace (the
+    no-allocation entry point plans against its fixed array) and counting the
+    timed call's launches must not divide by a segment of zero slots.  Here,
+    without a GPU, each call gets past validation and planning and then
+    fails at its first HIP call, or does nothing."""
+    import ctypes
+    lib = gdr.load()
+    fb = FakeBuffers(T=0, N=1, Nqk=1, Nv=2)
+    HIP_ERR = -4
+    rc = lib.gdr_chunk_fwd_no_alloc(None, None, None, None, None, fb.addr["state_in"], fb.addr["cu"],
+                                    1, 0, 1, 2, 128, gdr.GDR_BF16, 0.1, gdr.GDR_FLAG_QK_L2NORM,
+                                    None, fb.addr["state_out"], None)
+    assert rc in (OK, HIP_ERR)
+    kms = (ctypes.c_float * 4)()
+    kind = (ctypes.c_int32 * 4)()
+    n = ctypes.c_int32(-1)
+    span = ctypes.c_float(-1.0)
+    for state_out in (fb.addr["state_out"], fb.addr["state_in"], None):
+        rc = lib.gdr_chunk_fwd_timed(None, None, None, None, None, fb.addr["state_in"], fb.addr["cu"],
+                                     1, 0, 1, 2, 128, gdr.GDR_BF16, 0.1, gdr.GDR_FLAG_QK_L2NORM,
+                                     None, state_out, fb.addr["ws"], fb.sizes["ws"], None, kms, kind,
+                                     4, ctypes.byref(n), ctypes.byref(span))
+        assert rc in (OK, HIP_ERR)
+        if state_out != fb.addr["state_out"]:
+            # nothing to launch: no HIP call at all
+            assert rc == OK and n.value == 0 and span.value == 0.0

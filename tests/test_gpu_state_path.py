@@ -458,3 +458,67 @@ def test_hard_resets_and_underflowing_decays(path, dtype):
     ro, rs = oracle_full(inp)
     assert_close_per_seq_head(to_f64(out), ro, to_f64(st), rs, inp.cu_seqlens, TOL[dtype],
                               name=f"{path} {dtype} extreme gates")
+
+
+# ------------------------------------------- empty calls, huge packed batches
+
+
+def test_single_empty_sequence_keeps_its_state():
+    """N = 1, T = 0: no chunk slot at all, so no intra-chunk or state-pass
+    launch; the final state is still the initial state (zeros without one),
+    in place nothing is touched, and the timed call reports no kernel."""
+    import ctypes
+    import torch
+    dev = "cuda:0"
+    q = torch.empty((0, 1, 128), dtype=torch.bfloat16, device=dev)
+    v = torch.empty((0, 2, 128), dtype=torch.bfloat16, device=dev)
+    g = torch.empty((0, 2), dtype=torch.float32, device=dev)
+    cu = torch.zeros(2, dtype=torch.int32, device=dev)
+    s0 = torch.randn((1, 2, 128, 128), device=dev)
+    for chunk in (128, 64):
+        st = torch.full_like(s0, 7.0)
+        out, st = gdr.chunk_fwd(q, q, v, g, g, cu, s0, state_out=st, scale=SCALE, chunk=chunk)
+        torch.cuda.synchronize()
+        assert out.shape == (0, 2, 128) and torch.equal(st, s0)
+        st = torch.full_like(s0, 7.0)
+        _, st = gdr.chunk_fwd(q, q, v, g, g, cu, None, state_out=st, scale=SCALE, chunk=chunk)
+        torch.cuda.synchronize()
+        assert torch.count_nonzero(st).item() == 0
+    s = s0.clone()
+    tim = []
+    _, st = gdr.chunk_fwd(q, q, v, g, g, cu, s, state_out=s, scale=SCALE, timings=tim)
+    torch.cuda.synchronize()
+    assert torch.equal(s, s0) and tim == [("span", 0.0)]
+    tim = []
+    out, st = gdr.chunk_fwd(q, q, v, g, g, cu, s0, scale=SCALE, timings=tim)
+    torch.cuda.synchronize()
+    assert torch.equal(st, s0) and [n for n, _ in tim] == ["table", "span"]
+
+
+@pytest.mark.parametrize("dtype,chunk", [("bf16", 128), ("bf16", 64), ("f32", 128)])
+def test_many_sequences_mostly_empty(dtype, chunk):
+    """6,000 packed sequences, 70% of them empty and the rest 1-40 tokens
+    (every 500th 700 tokens): the state pass launches over each segment's runs
+    of slots (at most one per slot), not over all 6,000 sequences, so a
+    segment's sequence ids span far more than its slots; the empty sequences
+    get their initial states from the table launch."""
+    import time
+    import torch
+    rng = np.random.default_rng(160)
+    N = 6000
+    lengths = np.where(rng.random(N) < 0.7, 0, rng.integers(1, 41, size=N))
+    lengths[::500] = 700
+    inp = make_inputs(lengths, 1, 2, dtype=dtype, seed=161, state_std=0.1)
+    t = device_tensors(inp)
+    args = (t["q"], t["k"], t["v"], t["g"], t["beta"], t["cu"], t["state_in"])
+    gdr.chunk_fwd(*args, scale=SCALE, chunk=chunk)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    out, st = gdr.chunk_fwd(*args, scale=SCALE, chunk=chunk)
+    torch.cuda.synchronize()
+    print(f"N={N} T={inp.T} {dtype} L={chunk}: {1e3 * (time.perf_counter() - t0):.2f} ms", flush=True)
+    ro, rs = oracle_full(inp)
+    assert_close_per_seq_head(to_f64(out), ro, to_f64(st), rs, inp.cu_seqlens, TOL[dtype],
+                              name=f"N={N} mostly empty {dtype} L={chunk}")
+    empty = np.flatnonzero(lengths == 0)
+    assert np.array_equal(to_f64(st)[empty], inp.state_in[empty].astype(np.float64))
