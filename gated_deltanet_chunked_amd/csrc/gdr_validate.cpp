@@ -217,6 +217,8 @@ gdr_status validate_conv_prefill(const ConvPrefillCheck& a) {
   if (s != GDR_OK) return s;
   if (a.conv_k != 4) return GDR_ERR_UNSUPPORTED;
   if (a.N < 1 || a.T < 0) return GDR_ERR_INVALID_ARGUMENT;
+  // the window update runs one row of 256-thread workgroups per sequence
+  if (a.N >= (int32_t(1) << 24)) return GDR_ERR_INVALID_ARGUMENT;
   const int64_t C = (2 * static_cast<int64_t>(a.Nqk) + a.Nv) * 128;
   if (static_cast<int64_t>(a.T) * C > (int64_t(1) << 40)) return GDR_ERR_INVALID_ARGUMENT;
   if (!a.w || !a.A_log || !a.dt_bias || !a.cu) return GDR_ERR_INVALID_ARGUMENT;

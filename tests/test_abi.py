@@ -325,6 +325,7 @@ def test_conv_prefill_validates_before_launching():
     assert call(D=64) == UNSUPPORTED
     assert call(Nqk=3) == INVALID
     assert call(N=0) == INVALID
+    assert call(N=1 << 24) == INVALID                              # beyond a grid's 2^32 work-items
     assert call(T=-1) == INVALID
     for name in ("x", "w", "a", "b", "A_log", "dt_bias", "cu", "q", "k", "v", "g", "beta"):
         assert call(**{name: None}) == INVALID, name
